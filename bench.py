@@ -1,0 +1,322 @@
+"""Benchmark of the AWQ W4A16 hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+
+  producer  for layer L = step % layers of a Llama-3-8B-shaped stack:
+            awq_calib_stats on the layer's 4 distinct inputs (512 calibration
+            tokens each), awq_search_scale (20-point alpha grid, g = 128) and
+            awq_pack_int4 for its 7 linears, written back into the stack;
+  decode    the whole 32-layer stack (7 linears per layer, 224 calls of
+            awq_linear_w4a16, replayed as one HIP graph each) at M = 1, 8 and
+            32 tokens with g = 128, and at M = 1 and 32 with g = 64;
+  prefill   the 7 linears of layer L at M = 2048 tokens (GEMM).
+
+Inputs are resident in HBM before the timed region.  The reported value is
+the M = 1 decode: algorithmic bytes of the 224 weight streams (packed
+nibbles + fp16 scales + packed zeros + activations in/out) divided by the time
+of the graph replays, measured with HIP events on the stream the kernels run
+on.  The stack is 3.6 GB, far beyond the 256 MB Infinity Cache, so every
+weight byte comes from HBM.
+
+    python bench.py [--steps K] [--warmup W] [--layers 32] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+METRIC = "W4A16 GEMV achieved HBM GB/s (% of peak) at M=1; GEMM TFLOP/s at M=2048"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(m, n, k, g):
+    """Algorithmic bytes of one W4A16 linear call: packed weights, fp16 scales,
+    packed zero points, the fp16 activation and inv_s read once, the fp16 output
+    written once."""
+    return n * k // 2 + 2 * n * (k // g) + 4 * n * (-(-k // (8 * g))) + 2 * m * k + 2 * k + 2 * m * n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic as S
+    import weight_only_int4_awq_amd as P
+
+    P.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    L = args.layers
+    shapes = S.LLAMA3_8B_LINEARS
+    inputs = ("attn_in", "o", "mlp_in", "down_in")
+    kin = {"attn_in": 4096, "o": 4096, "mlp_in": 4096, "down_in": 14336}
+    m_cal = 512
+    n_grid = 20
+
+    # ------------------------------------------------------------ set-up (untimed)
+    t_setup = time.time()
+    W = []      # [layer][linear] fp16 weights
+    XC = []     # [layer][input] fp16 calibration tokens
+    for layer in range(L):
+        W.append([S.torch_weights(n, k, 0.02, S.seed_of(5, layer, S.SLOTS[nm], 0), dev)
+                  for nm, n, k in shapes])
+        xc = {}
+        for inp in inputs:
+            slot = S.SLOTS.get(inp, S.SLOTS.get("o"))
+            ch = S.outlier_channels(kin[inp], 0.01, S.seed_of(5, layer, slot, 3))
+            xc[inp] = S.torch_activations(m_cal, kin[inp], S.seed_of(5, layer, slot, 1), ch, 20.0, dev)
+        XC.append(xc)
+    log(f"generated {L} layers of weights in {time.time() - t_setup:.1f}s")
+
+    def produce(layer, g, dst, m_tokens, ws):
+        """calib -> search -> pack for one layer; packed tensors written into dst[layer]."""
+        stats = {inp: P.awq_calib_stats(XC[layer][inp][:m_tokens].contiguous() if m_tokens < m_cal
+                                        else XC[layer][inp]) for inp in inputs}
+        for li, (nm, n, k) in enumerate(shapes):
+            inp = S.INPUT_OF[nm]
+            x = XC[layer][inp] if m_tokens == m_cal else XC[layer][inp][:m_tokens].contiguous()
+            so = dst[layer][li + len(shapes)]          # persistent (best, s16, inv_s16, losses)
+            P.awq_search_scale(W[layer][li], x, stats[inp], g=g, n_grid=n_grid,
+                               workspace=ws[li], out=so)
+            qw, sc, qz, bad = dst[layer][li]
+            P.awq_pack_int4(W[layer][li], so[1], g=g, out=(qw, sc, qz, bad))
+
+    def alloc_stack(g):
+        st = []
+        for layer in range(L):
+            row = []
+            for nm, n, k in shapes:
+                row.append((torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                            torch.empty((n, k // g), dtype=torch.float16, device=dev),
+                            torch.empty((n, -(-k // (8 * g))), dtype=torch.int32, device=dev),
+                            torch.empty(1, dtype=torch.int32, device=dev)))
+            for nm, n, k in shapes:
+                row.append((torch.empty(1, dtype=torch.int32, device=dev),
+                            torch.empty(k, dtype=torch.float16, device=dev),
+                            torch.empty(k, dtype=torch.float16, device=dev),
+                            torch.empty(n_grid, dtype=torch.float64, device=dev)))
+            st.append(row)
+        return st
+
+    def alloc_ws(g, m_tokens):
+        return [torch.empty(P.awq_search_workspace_size(n, k, m_tokens, g, n_grid), dtype=torch.uint8,
+                            device=dev) for nm, n, k in shapes]
+
+    stacks = {128: alloc_stack(128), 64: alloc_stack(64)}
+    ws_setup = {g: alloc_ws(g, 128) for g in (128, 64)}
+    ws_step = alloc_ws(128, m_cal)
+    t0 = time.time()
+    for g in (128, 64):
+        for layer in range(L):
+            produce(layer, g, stacks[g], 128, ws_setup[g])   # whole-stack search over 128 tokens
+    torch.cuda.synchronize()
+    log(f"searched + packed the {L}-layer stack at g=128 and g=64 in {time.time() - t0:.1f}s")
+
+    # decode inputs: one token batch per distinct input per layer
+    XR = {}
+    for m in (1, 8, 32):
+        XR[m] = []
+        for layer in range(L):
+            d = {}
+            for inp in inputs:
+                slot = S.SLOTS.get(inp, S.SLOTS.get("o"))
+                ch = S.outlier_channels(kin[inp], 0.01, S.seed_of(5, layer, slot, 3))
+                d[inp] = S.torch_activations(m, kin[inp], S.seed_of(5, layer, slot, 2) + 7 * m, ch, 20.0, dev)
+            XR[m].append(d)
+    YR = {m: [[torch.empty((m, n), dtype=torch.float16, device=dev) for nm, n, k in shapes]
+              for _ in range(L)] for m in (1, 8, 32)}
+
+    def decode(g, m):
+        st = stacks[g]
+        for layer in range(L):
+            for li, (nm, n, k) in enumerate(shapes):
+                qw, sc, qz, _ = st[layer][li]
+                P.awq_linear_w4a16(XR[m][layer][S.INPUT_OF[nm]], qw, sc, qz,
+                                   st[layer][li + len(shapes)][2], g=g, out=YR[m][layer][li])
+
+    decode_cases = [(128, 1), (128, 8), (128, 32), (64, 1), (64, 32)]
+    for g, m in decode_cases:        # eager run first: allocates the library scratch
+        decode(g, m)
+    torch.cuda.synchronize()
+    graphs = {}
+    for g, m in decode_cases:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            decode(g, m)
+        graphs[(g, m)] = gr
+    torch.cuda.synchronize()
+    log("captured the decode graphs")
+
+    # prefill inputs
+    XP = {}
+    for inp in inputs:
+        slot = S.SLOTS.get(inp, S.SLOTS.get("o"))
+        ch = S.outlier_channels(kin[inp], 0.01, S.seed_of(3, 0, slot, 3))
+        XP[inp] = S.torch_activations(2048, kin[inp], S.seed_of(3, 0, slot, 2), ch, 20.0, dev)
+    YP = [torch.empty((2048, n), dtype=torch.float16, device=dev) for nm, n, k in shapes]
+
+    def prefill(layer):
+        st = stacks[128]
+        for li, (nm, n, k) in enumerate(shapes):
+            qw, sc, qz, _ = st[layer][li]
+            P.awq_linear_w4a16(XP[S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2],
+                               g=128, out=YP[li])
+
+    phases = ["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["prefill"]
+    acc = {p: 0.0 for p in phases}
+
+    def step(i, timed):
+        layer = i % L
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        ev[0].record(stream)
+        produce(layer, 128, stacks[128], m_cal, ws_step)
+        ev[1].record(stream)
+        for pi, (g, m) in enumerate(decode_cases):
+            graphs[(g, m)].replay()
+            ev[2 + pi].record(stream)
+        prefill(layer)
+        ev[-1].record(stream)
+        if timed:
+            return ev
+        return None
+
+    for i in range(args.warmup):
+        step(i, False)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    torch.cuda.synchronize()
+    events = []
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        events.append(step(args.warmup + i, True))
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    for ev in events:
+        for pi, p in enumerate(phases):
+            acc[p] += ev[pi].elapsed_time(ev[pi + 1]) * 1e-3     # seconds
+    log(f"timed {args.steps} steps in {t_total:.3f}s")
+
+    K = args.steps
+    nlin = L * len(shapes)
+    bytes_by = {}
+    for g, m in decode_cases:
+        bytes_by[(g, m)] = L * sum(gemv_bytes(m, n, k, g) for nm, n, k in shapes)
+    rows = {}
+    for g, m in decode_cases:
+        t = acc[f"decode_g{g}_m{m}"] / K
+        rows[f"decode_g{g}_m{m}"] = {"us_per_stack": t * 1e6, "us_per_linear": t * 1e6 / nlin,
+                                     "GBps": bytes_by[(g, m)] / t / 1e9,
+                                     "frac_hbm_peak": bytes_by[(g, m)] / t / 1e9 / HBM_PEAK_GBS}
+    prefill_flops = sum(2 * 2048 * n * k for nm, n, k in shapes)
+    t_pf = acc["prefill"] / K
+    rows["prefill_m2048"] = {"us_per_layer": t_pf * 1e6, "TFLOPs": prefill_flops / t_pf / 1e12,
+                             "frac_mfma_peak": prefill_flops / t_pf / 1e12 / F16_MFMA_PEAK_TFLOPS}
+    search_flops = n_grid * sum(2 * n * k * m_cal for nm, n, k in shapes)
+    t_pr = acc["producer"] / K
+    rows["producer_m512"] = {"us_per_layer": t_pr * 1e6,
+                             "search_TFLOPs_algorithmic": search_flops / t_pr / 1e12}
+
+    value = rows["decode_g128_m1"]["GBps"]
+    t1 = acc["decode_g128_m1"] / K
+    avg_launch = t1 / nlin
+    bytes_per_launch = bytes_by[(128, 1)] / nlin
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_total / K * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% x20 outlier channels)",
+        "config": {"workload": "llama3-8b-shaped linear stack: producer (calib 512 tok, 20-pt alpha "
+                               "search, int4 g128 pack) on one layer + 32-layer decode at M=1/8/32 "
+                               "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048",
+                   "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32],
+                   "m_prefill": 2048, "m_calib": m_cal, "n_grid": n_grid, "group_size": [128, 64]},
+        "gemm_tflops_m2048": round(rows["prefill_m2048"]["TFLOPs"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(bytes_per_launch / avg_launch / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(bytes_per_launch / avg_launch / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "W4A16 decode GEMV (M=1, g=128)",
+                     "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch * 1e6},
+        "roofline_gemm": {"bound": "mfma", "achieved": round(rows["prefill_m2048"]["TFLOPs"], 2),
+                          "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(rows["prefill_m2048"]["frac_mfma_peak"], 4)},
+        "rows": rows,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(budget_s):
+    """The CPU oracle on a bounded sample of the same workload: the float64
+    reference W4A16 linear at M = 1 over Llama-3-8B-shaped linears (unpack,
+    dequantize, matrix-vector product), repeated until about budget_s seconds
+    of CPU time; reported in the metric's unit (algorithmic GB/s)."""
+    import synthetic as S
+    from oracle import awq_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    done_bytes, t_used, calls, names = 0, 0.0, 0, []
+    try:
+        prepared = []
+        for nm, n, k in S.LLAMA3_8B_LINEARS:
+            w = S.weights(n, k, 0.02, S.seed_of(2, 0, S.SLOTS[nm], 0))
+            qw, sc, qz, _ = O.pack_int4(w, None, 128)
+            x = S.activations(1, k, S.seed_of(2, 0, S.SLOTS[nm], 2))
+            prepared.append((nm, n, k, qw, sc, qz, x))
+            del w
+        while t_used < budget_s:
+            for nm, n, k, qw, sc, qz, x in prepared:
+                t0 = time.perf_counter()
+                O.linear_ref(x, qw, sc, qz, None, k, 128)
+                t_used += time.perf_counter() - t0
+                done_bytes += gemv_bytes(1, n, k, 128)
+                calls += 1
+                names.append(nm)
+                if t_used >= budget_s:
+                    break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{calls} float64 oracle W4A16 linears at M=1 (g=128) over the 7 Llama-3-8B-shaped "
+                      f"layer linears, {t_used:.1f}s of single-thread CPU time; "
+                      f"host has {len(os.sched_getaffinity(0))} cores"}
+
+
+if __name__ == "__main__":
+    main()

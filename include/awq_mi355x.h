@@ -1,0 +1,180 @@
+/*
+ * awq_mi355x.h -- C ABI of the AWQ W4A16 group-quantized linear layer on
+ * MI355X (gfx950).
+ *
+ * The method (activation-aware weight quantization, AWQ) as the source pages
+ * describe it:
+ *   - jsqmd.com "从Java转行大模型应用，大模型量化实现，AWQ 与 GPTQ 算法",
+ *     section 二.1 (2) weight importance via the per-channel mean |activation|,
+ *     section 二.1 (3) channel scaling: salient input channels of W are
+ *     multiplied by s, the activation is divided by s, and s minimises the
+ *     output error of the quantized layer; section 五.3 asks for a clip
+ *     against scale overflow;
+ *   - CSDN "LLM-AWQ学术影响力…", section "量化流程优化": a scale search whose
+ *     result is dumped, then real 4-bit, group-128 quantization into packed
+ *     weights;
+ *   - bjdmk.com.cn "大模型量化技术极速优化…", section "量化参数配置": 4-bit
+ *     weights, group size 128, zero point on, GEMV mode for batch 1 and GEMM
+ *     mode for long inputs;
+ *   - zeeklog.com "LLM-AWQ多模态基准…": W4A16 = 4-bit weights, 16-bit
+ *     activations.
+ * Where the pages leave a step open, the reading used is stated at the entry
+ * point that implements it.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP device memory) owned by the
+ *     caller.  fp16 tensors are passed as uint16_t bit patterns.  Matrices are
+ *     row-major with K (input features) contiguous: W is [N out][K in], X is
+ *     [M tokens][K].
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous and ordered on that stream; nothing is synchronised.
+ *   - Argument errors are detected on the host before any launch and nothing
+ *     is written; the status code says which check failed and
+ *     awq_last_error() returns a message (thread-local).
+ *   - Launch failures return AWQ_ERR_HIP.
+ *   - Results are bitwise deterministic run to run: every reduction has a
+ *     fixed order.
+ *   - Outputs must not alias inputs.
+ *   - Non-finite data cannot be seen on the host without a synchronisation;
+ *     it is reported through device-side values as stated per entry point.
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  AWQ_ERR_SHAPE = 2,       /* a size or group size is out of range                */
+  AWQ_ERR_ALIGN = 3,       /* a pointer is not aligned as required                 */
+  AWQ_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required           */
+  AWQ_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed           */
+  AWQ_ERR_UNSUPPORTED = 7  /* not supported on this device                         */
+} awq_status;
+
+/* Version of this ABI and of the packed layout ("layout v1" below). */
+int32_t awq_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* awq_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * awq_calib_stats -- per-input-channel mean absolute activation.
+ * Passage: jsqmd.com page, section 二.1 (2): the importance of input channel j
+ * comes from E[|X_j|], the mean absolute activation over calibration data
+ * (the pseudocode of section 二.2 takes mean(|activation|) over tokens).
+ *
+ *   x        [m][k] fp16 calibration tokens, 16-byte aligned.
+ *   mean_abs [k] float64 out: a_j = (sum_t |x_tj|) / m.  The sum is exact
+ *            (|fp16| * 2^24 is an integer; the kernel sums integers), and
+ *            a_j is the exact mean rounded once.
+ *   Limits: 1 <= m <= 8192, 1 <= k, k % 8 == 0.
+ *   Non-finite x: an inf gives a_j = inf, a NaN gives a_j = NaN.
+ * ------------------------------------------------------------------------- */
+awq_status awq_calib_stats(const uint16_t* x, int64_t m, int64_t k,
+                           double* mean_abs, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_search_scale -- grid search of the per-channel scale s = a^alpha.
+ * Passage: jsqmd.com page, section 二.1 (3): scale salient input channels of W
+ * by s, divide the activation by s, and pick s to minimise the output error
+ * of the quantized layer.  Readings (the pages give no parametrisation):
+ *   alpha_i = i / n_grid, i = 0 .. n_grid-1;
+ *   s_ik    = fp16_rn(max(a_k^alpha_i, 2^-14))  (lower clamp = the clip the
+ *             page asks for; a NaN power stays NaN);
+ *   W'      = fp16_rn(W * s_i) per element;
+ *   per (row, group of g along K): D = fp16_rn(max(max W' - min W', 2^-16)/15),
+ *             z = clamp(RNE(-min W' / D), 0, 15),
+ *             q = clamp(RNE(W' / D) + z, 0, 15)   (RNE = round half to even);
+ *   loss    L_i = sum_{t,n} (sum_k ((q - z) D / s_ik - W_nk) X_tk)^2;
+ *   best    = first index of the minimum over finite L_i (-1 if none).
+ * The kernels evaluate L_i with fp32 MFMA accumulation of an fp16 hi+lo split
+ * of the weight error, and reduce squares in float64 (relative error of L_i
+ * about 1e-7; the index is exact whenever the best-vs-second gap is larger).
+ *
+ *   w        [n][k] fp16 weights;  x [m][k] fp16 calibration tokens
+ *            (both 16-byte aligned);  mean_abs [k] float64 (awq_calib_stats).
+ *   best_idx [1] int32 out;  s16 [k] fp16 out = s at the best alpha;
+ *   inv_s16  [k] fp16 out = fp16_rn(1 / s16) (float64 quotient);
+ *   losses   [n_grid] float64 out (may be NULL);
+ *   When no loss is finite: best_idx = -1 and s16 = inv_s16 = 1.0.
+ *   workspace/ws_bytes: device scratch of at least
+ *            awq_search_workspace_size(n, k, m, g, n_grid) bytes, 256-byte
+ *            aligned; contents on entry are ignored.
+ *   Limits: g in {32, 64, 128}; k % g == 0; 1 <= n; 1 <= m <= 8192;
+ *           1 <= n_grid <= 64.
+ * ------------------------------------------------------------------------- */
+size_t awq_search_workspace_size(int64_t n, int64_t k, int64_t m, int32_t g,
+                                 int32_t n_grid);
+awq_status awq_search_scale(const uint16_t* w, const uint16_t* x,
+                            const double* mean_abs, int64_t n, int64_t k,
+                            int64_t m, int32_t g, int32_t n_grid,
+                            int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
+                            double* losses, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_pack_int4 -- real quantization and nibble packing (layout v1).
+ * Passage: CSDN page, section "量化流程优化" (real 4-bit, group-128
+ * quantization of the scaled weights into a packed dump) and bjdmk.com.cn
+ * page, section "量化参数配置" (4 bit, group 128, zero point on).  The
+ * arithmetic is the per-group rule of awq_search_scale at s = s16.
+ *
+ *   w        [n][k] fp16, 16-byte aligned.
+ *   s16      [k] fp16 channel scale, or NULL for s = 1 (plain RTN).
+ *   qweight  [n][k/8] uint32 out: bits 4*(k%8)..+3 of word k/8 hold q_nk.
+ *   scales   [n][k/g] fp16 out: D_nj.
+ *   qzeros   [n][ceil(k/(8g))] uint32 out: bits 4*(j%8)..+3 of word j/8 hold
+ *            z_nj; unused nibbles of the last word are 0.
+ *   nonfinite_groups: optional device int32 out (may be NULL): number of
+ *            groups whose W' holds inf or NaN (fp16 overflow of W * s or a
+ *            non-finite W).  Such a group gets q = 0, z = 0 and scale =
+ *            fp16 NaN (0x7E00).
+ *   Limits: g in {32, 64, 128}; k % g == 0; n >= 1; k >= g; qweight 16-byte
+ *           aligned.
+ * ------------------------------------------------------------------------- */
+awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n,
+                         int64_t k, int32_t g, uint32_t* qweight,
+                         uint16_t* scales, uint32_t* qzeros,
+                         int32_t* nonfinite_groups, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_linear_w4a16 -- y = x_tilde W_deq^T with 4-bit weights and fp16
+ * activations.
+ * Passage: bjdmk.com.cn page, section "量化参数配置" / "技术选型决策树"
+ * (GEMV mode for batch-1 decode, GEMM mode for long inputs); zeeklog.com page
+ * (W4A16 kernels); jsqmd.com page, section 二.1 (3) (the activation is
+ * divided by s at inference, here x_tilde = x * inv_s16).
+ *
+ *   y[t][n] = fp16_rn( sum_k x_tilde_tk (q_nk - z_nj) D_nj ),  j = k / g,
+ *   x_tilde = x * inv_s16 (per channel) or x when inv_s16 is NULL.
+ *   Accumulation is fp32; against the float64 value the result is within
+ *   5e-3 * max(|y_ref|, rms of the row of y_ref) per output.
+ *   x        [m][k] fp16, 16-byte aligned;  inv_s16 [k] fp16 or NULL;
+ *   qweight/scales/qzeros in layout v1 (awq_pack_int4);  y [m][n] fp16 out.
+ *   m = 1..8 runs the decode kernel (GEMV mode); m = 9..32 the same kernel
+ *   over token chunks; m > 32 the prefill GEMM.  Both dequantize in-kernel.
+ *   The library keeps one device scratch buffer per device for the staged
+ *   activations (grown on demand with hipMalloc, never freed); calls that
+ *   overlap on one device from different host threads must be serialised
+ *   by the caller.
+ *   Limits: g in {32, 64, 128}; k % g == 0; k % 64 == 0; m >= 1; n >= 1;
+ *           x and qweight 16-byte aligned.  |x_tilde| must stay within the
+ *           fp16 range (larger values give a non-finite y).
+ * ------------------------------------------------------------------------- */
+awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight,
+                            const uint16_t* scales, const uint32_t* qzeros,
+                            const uint16_t* inv_s16, int64_t m, int64_t n,
+                            int64_t k, int32_t g, uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

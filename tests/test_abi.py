@@ -1,0 +1,152 @@
+"""The C ABI library loads and exports every symbol the header declares, and its
+host-side argument checks reject bad calls before any launch (CPU only: every
+call here fails validation, so nothing reaches the GPU)."""
+from __future__ import annotations
+
+import ctypes as C
+import pathlib
+import re
+import subprocess
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "awq_mi355x.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from weight_only_int4_awq_amd import _lib
+    if not _lib.LIB_PATH.exists():
+        from weight_only_int4_awq_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    body = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(awq_\w+)\s*\(", body, flags=re.M)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for want in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
+                 "awq_pack_int4", "awq_linear_w4a16", "awq_last_error", "awq_abi_version"):
+        assert want in names, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from weight_only_int4_awq_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+        assert name in _lib.SIGNATURES, name
+    assert lib.awq_abi_version() == 1
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = 0x10002
+
+
+def _status(lib, fn, *args):
+    st = getattr(lib, fn)(*args)
+    msg = lib.awq_last_error().decode()
+    return st, msg
+
+
+def test_calib_stats_argument_errors(lib):
+    assert _status(lib, "awq_calib_stats", None, 4, 64, FAKE, None)[0] == 1
+    assert _status(lib, "awq_calib_stats", FAKE, 0, 64, FAKE, None)[0] == 2
+    assert _status(lib, "awq_calib_stats", FAKE, 8193, 64, FAKE, None)[0] == 2
+    assert _status(lib, "awq_calib_stats", FAKE, 4, 60, FAKE, None)[0] == 2
+    st, msg = _status(lib, "awq_calib_stats", MISALIGNED, 4, 64, FAKE, None)
+    assert st == 3 and "aligned" in msg
+
+
+def test_search_argument_errors(lib):
+    ws = lib.awq_search_workspace_size(64, 256, 16, 128, 20)
+    assert ws > 0
+    assert lib.awq_search_workspace_size(64, 256, 16, 96, 20) == 0
+    assert lib.awq_search_workspace_size(64, 256, 16, 128, 65) == 0
+    base = [FAKE, FAKE, FAKE, 64, 256, 16, 128, 20, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["w", "x", "a", "n", "k", "m", "g", "ng", "best", "s", "inv", "loss", "ws", "wsb", "st"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_search_scale", *a)[0]
+
+    assert call(w=None) == 1
+    assert call(best=None) == 1
+    assert call(g=96) == 2
+    assert call(k=200) == 2
+    assert call(m=0) == 2
+    assert call(m=9000) == 2
+    assert call(ng=0) == 2
+    assert call(ng=65) == 2
+    assert call(n=0) == 2
+    assert call(w=MISALIGNED) == 3
+    assert call(wsb=ws - 1) == 4
+    assert call(ws=None) == 4
+    assert call(ws=FAKE + 16) == 3
+
+
+def test_pack_argument_errors(lib):
+    base = [FAKE, None, 16, 256, 128, FAKE, FAKE, FAKE, None, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["w", "s", "n", "k", "g", "qw", "sc", "qz", "bad", "st"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_pack_int4", *a)[0]
+
+    assert call(w=None) == 1
+    assert call(qz=None) == 1
+    assert call(g=16) == 2
+    assert call(k=192) == 2
+    assert call(k=64) == 2
+    assert call(n=0) == 2
+    assert call(qw=MISALIGNED) == 3
+    assert call(s=MISALIGNED) == 3
+
+
+def test_linear_argument_errors(lib):
+    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, FAKE, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "y", "st"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_linear_w4a16", *a)[0]
+
+    assert call(x=None) == 1
+    assert call(y=None) == 1
+    assert call(g=48) == 2
+    assert call(k=96, g=32) == 2
+    assert call(m=0) == 2
+    assert call(n=0) == 2
+    assert call(x=MISALIGNED) == 3
+    assert call(qw=FAKE + 4) == 3
+
+
+def test_python_binding_has_the_c_names():
+    import weight_only_int4_awq_amd as P
+    for name in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
+                 "awq_pack_int4", "awq_linear_w4a16"):
+        assert callable(getattr(P, name))
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = ROOT / "weight_only_int4_awq_amd"
+    for f in pkg.rglob("*"):
+        if f.suffix in (".py", ".hip", ".h", ".cpp"):
+            text = f.read_text()
+            assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), f
+            assert "awq_oracle" not in text, f

@@ -1,0 +1,305 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle on the same
+seeded inputs.  Bit-exact for the statistic, the packed nibbles, zero points,
+fp16 scales, s16, inv_s16 and the chosen alpha; the linear outputs within the
+floored relative tolerance 5e-3 against float64.
+
+Small shapes span several tiles and a ragged tail; full Llama-shaped sizes are
+checked on sampled rows / columns the oracle computes one by one."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import awq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def P():
+    import weight_only_int4_awq_amd as P
+    P.load()
+    assert torch.cuda.is_available()
+    return P
+
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host16(t):
+    return t.cpu().numpy().astype(np.float16)
+
+
+def host_u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+# ----------------------------------------------------------------- calib stats
+
+
+@pytest.mark.parametrize("m,k", [(1, 8), (37, 264), (128, 4096), (512, 14336), (8192, 64)])
+def test_calib_stats_bit_exact(P, m, k):
+    x = S.activations(m, k, 1000 + m, S.outlier_channels(k, 0.01, 7), 20.0)
+    got = P.awq_calib_stats(dev(x)).cpu().numpy()
+    want = O.calib_stats(x)
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+
+
+def test_calib_stats_nonfinite(P):
+    x = S.activations(16, 64, 5)
+    x[3, 5] = np.float16(np.inf)
+    x[4, 9] = np.float16(-np.inf)
+    x[2, 9] = np.float16(np.nan)
+    got = P.awq_calib_stats(dev(x)).cpu().numpy()
+    want = O.calib_stats(x)
+    assert np.isinf(got[5]) and np.isnan(got[9]) and np.isnan(want[9])
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin], want[fin])
+
+
+# ----------------------------------------------------------------- pack
+
+
+def _check_pack(P, w, s16, g):
+    qw, sc, qz, bad = P.awq_pack_int4(dev(w), None if s16 is None else dev(s16), g=g)
+    torch.cuda.synchronize()
+    oqw, osc, oqz, obad = O.pack_int4(w, s16, g)
+    assert np.array_equal(host_u32(qw), oqw)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), osc.view(np.uint16))
+    assert np.array_equal(host_u32(qz), oqz)
+    assert int(bad.item()) == obad
+
+
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("n,k", [(1, 128), (33, 384), (7, 2048 + 384), (300, 4096)])
+def test_pack_bit_exact(P, g, n, k):
+    if k % g:
+        pytest.skip("k must be a multiple of g")
+    w = S.weights(n, k, 0.02, 77 + n + k)
+    _check_pack(P, w, None, g)
+    x = S.activations(64, k, 78, S.outlier_channels(k, 0.01, 79), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(x), 0.45)
+    _check_pack(P, w, s16, g)
+
+
+def test_pack_ties_and_edge_groups(P):
+    g = 32
+    d = 2.0 ** -7
+    w = S.weights(4, 4 * g, 0.02, 91)
+    # exact half-step values in a group of range 15 d: every rounding tie
+    w[0, :g] = np.float16(0)
+    w[0, 0], w[0, 1] = np.float16(-7 * d), np.float16(8 * d)
+    for i, h in enumerate((0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 6.5, 7.5, -6.5)):
+        w[0, 2 + i] = np.float16(h * d)
+    w[1, :g] = np.float16(0.3)                      # constant group (range floor)
+    w[1, g:2 * g] = np.abs(w[1, g:2 * g]) + np.float16(1.0)   # no zero in range
+    w[2, :g] = (w[2, :g].astype(np.float64) * 1e-3).astype(np.float16)   # subnormal-ish
+    w[3, :g] = (w[3, :g].astype(np.float64) * 2000).astype(np.float16)   # large values
+    _check_pack(P, w, None, g)
+
+
+def test_pack_nonfinite_groups(P):
+    g = 64
+    w = S.weights(3, 256, 0.02, 95)
+    w[1, 70] = np.float16(np.nan)
+    w[2, 200] = np.float16(np.inf)
+    s16 = np.ones(256, np.float16)
+    s16[10] = np.float16(60000.0)
+    w[0, 10] = np.float16(3.0)
+    _check_pack(P, w, s16, g)
+
+
+@pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
+def test_pack_full_size_sampled_rows(P, name, n, k):
+    w, x_cal, _, _ = S.config_layer(2, name, n, k, 128, 0, 0.02, 0.01, 20.0)
+    s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
+    qw, sc, qz, bad = P.awq_pack_int4(dev(w), dev(s16), g=128)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.Generator(np.random.PCG64(n + k)).choice(n, 256, replace=False))
+    oqw, osc, oqz, obad = O.pack_int4(w[rows], s16, 128)
+    assert np.array_equal(host_u32(qw)[rows], oqw)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16)[rows], osc.view(np.uint16))
+    assert np.array_equal(host_u32(qz)[rows], oqz)
+    assert int(bad.item()) == 0
+
+
+# ----------------------------------------------------------------- search
+
+
+def _check_search(P, w, x, g, n_grid, expect_best=None):
+    a_dev = P.awq_calib_stats(dev(x))
+    best, s16, inv, losses = P.awq_search_scale(dev(w), dev(x), a_dev, g=g, n_grid=n_grid)
+    torch.cuda.synchronize()
+    a = O.calib_stats(x)
+    ob, os16, oinv, olosses = O.search_scale(w, x, a, g=g, n_grid=n_grid)
+    gl = losses.cpu().numpy()
+    fin = np.isfinite(olosses)
+    assert np.array_equal(np.isfinite(gl), fin)
+    # The kernel's loss carries the fp32 accumulation error of E = dW X^T plus the
+    # 2^-22 residue of the fp16 hi+lo split of dW.  Both are bounded per output by
+    # gamma * sum_k |dW X| with gamma far below 1e-5, so with
+    # S = sum_{t,n} (sum_k |dW_nk X_tk|)^2:  |L_gpu - L| <= 2 gamma sqrt(L S) + gamma^2 S.
+    gamma = 1e-5
+    xa = np.abs(x.astype(np.float64))
+    for i in np.flatnonzero(fin):
+        s_i = O.scale_candidate(a, i / n_grid)
+        dw = O.fake_quantize(w, s_i, g)[5] / s_i.astype(np.float64)[None, :] - w.astype(np.float64)
+        sabs = float(np.sum((np.abs(dw) @ xa.T) ** 2))
+        bound = 2 * gamma * np.sqrt(olosses[i] * sabs) + gamma * gamma * sabs
+        assert abs(gl[i] - olosses[i]) <= bound, (i, gl[i], olosses[i], bound)
+    srt = np.sort(olosses[fin])
+    gap = (srt[1] - srt[0]) / srt[0] if len(srt) > 1 and srt[0] > 0 else np.inf
+    assert int(best.item()) == ob, (int(best.item()), ob, gap)
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16), os16.view(np.uint16))
+    assert np.array_equal(inv.cpu().numpy().view(np.uint16), oinv.view(np.uint16))
+    if expect_best is not None:
+        assert ob == expect_best
+    return ob, gap
+
+
+@pytest.mark.parametrize("n,k,m,g", [(40, 256, 20, 64), (70, 384, 130, 128), (33, 96, 5, 32),
+                                      (64, 512, 600, 128), (1, 128, 1, 128)])
+def test_search_small(P, n, k, m, g):
+    w = S.weights(n, k, 0.02, 300 + n)
+    x = S.activations(m, k, 301 + m, S.outlier_channels(k, 0.02, 302), 20.0)
+    _check_search(P, w, x, g, 20)
+
+
+def test_search_tie_break_constant_activations(P):
+    w = S.weights(48, 256, 0.02, 311)
+    x = np.where(np.random.Generator(np.random.PCG64(312)).random((16, 256)) < 0.5, -1.0,
+                 1.0).astype(np.float16)
+    _check_search(P, w, x, 128, 20, expect_best=0)
+
+
+def test_search_nonfinite_alpha(P):
+    # a huge activation column makes large alphas overflow W * s: those get an infinite loss
+    w = S.weights(32, 128, 0.5, 321)
+    x = S.activations(8, 128, 322)
+    x[:, 3] = np.float16(60000.0)
+    w[0, 3] = np.float16(2.0)      # 2 * 60000^0.95 overflows fp16
+    ob, gap = _check_search(P, w, x, 128, 20)
+    a = O.calib_stats(x)
+    assert not np.isfinite(O.search_loss(w, x, O.scale_candidate(a, 0.95), 128))
+
+
+@pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
+def test_search_full_k_sampled_rows(P, name, n, k):
+    # full K and the calibration set of the Llama-3-8B prefill workload (512 tokens) on 96
+    # sampled rows: the loss is a sum over rows, so this is the same search restricted to them
+    w, x_cal, _, _ = S.config_layer(3, name, n, k, 512, 0, 0.02, 0.01, 20.0)
+    rows = np.sort(np.random.Generator(np.random.PCG64(n)).choice(n, 96, replace=False))
+    _check_search(P, np.ascontiguousarray(w[rows]), x_cal, 128, 20)
+
+
+def test_search_rows_additive_full_size(P):
+    # the full 4096 x 4096 search (128 tokens) equals the sum of its row-block searches
+    w, x_cal, _, _ = S.config_layer(1, "q", 4096, 4096, 128, 0, 0.02, 0.01, 20.0)
+    wd, xd = dev(w), dev(x_cal)
+    a = P.awq_calib_stats(xd)
+    best, s16, inv, losses = P.awq_search_scale(wd, xd, a)
+    parts = [P.awq_search_scale(wd[i:i + 1024].contiguous(), xd, a)[3] for i in range(0, 4096, 1024)]
+    torch.cuda.synchronize()
+    tot = sum(p.cpu().numpy() for p in parts)
+    full = losses.cpu().numpy()
+    assert np.max(np.abs(tot - full) / full) < 1e-12
+    # and the 128 sampled rows agree with the oracle
+    rows = np.arange(0, 4096, 32)
+    _check_search(P, np.ascontiguousarray(w[rows]), x_cal, 128, 20)
+
+
+def test_search_deterministic(P):
+    w = S.weights(256, 1024, 0.02, 331)
+    x = S.activations(200, 1024, 332, S.outlier_channels(1024, 0.01, 333), 20.0)
+    wd, xd = dev(w), dev(x)
+    a = P.awq_calib_stats(xd)
+    r1 = P.awq_search_scale(wd, xd, a)
+    r2 = P.awq_search_scale(wd, xd, a)
+    torch.cuda.synchronize()
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
+# ----------------------------------------------------------------- linear
+
+
+def _check_linear(P, w, x, s16, g, cols=None):
+    inv = None if s16 is None else O.fp16_rn(1.0 / s16.astype(np.float64))
+    qw, sc, qz, _ = P.awq_pack_int4(dev(w), None if s16 is None else dev(s16), g=g)
+    y = P.awq_linear_w4a16(dev(x), qw, sc, qz, None if inv is None else dev(inv), g=g)
+    torch.cuda.synchronize()
+    k = w.shape[1]
+    hq, hs, hz = host_u32(qw), sc.cpu().numpy(), host_u32(qz)
+    yh = host16(y)
+    if cols is None:
+        yr = O.linear_ref(x, hq, hs, hz, inv, k, g)
+        ok, worst, raw = O.check_linear(yh, yr)
+    else:
+        yr = O.linear_ref_rows(x, hq, hs, hz, inv, k, g, cols)
+        ok, worst, raw = O.check_linear(yh[:, cols], yr)
+    assert ok, (worst, raw)
+    return worst, raw
+
+
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 9, 16, 31, 32, 33, 100, 257])
+@pytest.mark.parametrize("g", [32, 64, 128])
+def test_linear_small(P, m, g):
+    n, k = 50, 640
+    w = S.weights(n, k, 0.02, 400 + m)
+    x = S.activations(m, k, 401 + m, S.outlier_channels(k, 0.01, 402), 20.0)
+    xc = S.activations(64, k, 403, S.outlier_channels(k, 0.01, 402), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.4)
+    _check_linear(P, w, x, s16, g)
+    _check_linear(P, w, x, None, g)
+
+
+@pytest.mark.parametrize("n,k", [(16, 64), (257, 1152), (129, 4096)])
+def test_linear_ragged(P, n, k):
+    for m in (1, 8, 40, 300):
+        w = S.weights(n, k, 0.02, 410 + n)
+        x = S.activations(m, k, 411 + m)
+        _check_linear(P, w, x, None, 64)
+
+
+@pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
+@pytest.mark.parametrize("m", [1, 8])
+def test_linear_decode_full_size(P, name, n, k, m):
+    w, x_cal, x_run, _ = S.config_layer(2, name, n, k, 128, m, 0.02, 0.01, 20.0)
+    s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
+    _check_linear(P, w, x_run, s16, 128)
+
+
+@pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
+def test_linear_prefill_full_size_sampled(P, name, n, k):
+    w, x_cal, x_run, _ = S.config_layer(3, name, n, k, 512, 2048, 0.02, 0.01, 20.0)
+    s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
+    cols = np.sort(np.random.Generator(np.random.PCG64(n + 1)).choice(n, 96, replace=False))
+    _check_linear(P, w, x_run, s16, 128, cols=cols)
+
+
+@pytest.mark.parametrize("name,n,k", S.LLAMA3_70B_LINEARS)
+def test_linear_70b_shapes_sampled(P, name, n, k):
+    w = S.weights(n, k, 0.015, S.seed_of(4, 0, S.SLOTS[name], 0))
+    ch = S.outlier_channels(k, 0.005, S.seed_of(4, 0, S.SLOTS[name], 3))
+    cols = np.sort(np.random.Generator(np.random.PCG64(n + 2)).choice(n, 256, replace=False))
+    for m in (1, 16):
+        x = S.activations(m, k, S.seed_of(4, 0, S.SLOTS[name], 2), ch, 30.0)
+        _check_linear(P, w, x, None, 128, cols=cols)
+
+
+def test_linear_deterministic(P):
+    w = S.weights(512, 2048, 0.02, 431)
+    qw, sc, qz, _ = P.awq_pack_int4(dev(w), None, g=128)
+    for m in (1, 8, 32, 300):
+        x = dev(S.activations(m, 2048, 432 + m))
+        y1 = P.awq_linear_w4a16(x, qw, sc, qz, None, g=128)
+        y2 = P.awq_linear_w4a16(x, qw, sc, qz, None, g=128)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)

@@ -1,0 +1,164 @@
+"""MI355X-native AWQ W4A16 hot path: Python binding of libawq_mi355x.so.
+
+The functions below carry the names of the C entry points and only marshal
+arguments: they check devices, dtypes, shapes and contiguity, allocate outputs
+with torch (device memory plumbing) and pass raw device pointers plus
+``torch.cuda.current_stream()`` to the library.  Every step of the path runs in
+the library's HIP kernels; there is no fallback.
+
+    awq_calib_stats(x)                          -> mean_abs  float64 [k]
+    awq_search_scale(w, x, mean_abs, g, n_grid) -> (best_idx int32 [1], s16, inv_s16, losses)
+    awq_pack_int4(w, s16, g)                    -> (qweight, scales, qzeros, nonfinite int32 [1])
+    awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16, g) -> y fp16 [m, n]
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import AWQError  # noqa: F401
+
+__all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_pack_int4",
+           "awq_linear_w4a16", "AWQError", "load"]
+
+
+def load():
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _out_tensor(t, dtype, shape, name):
+    _dev_tensor(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _dev_tensor(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+    return t
+
+
+def awq_calib_stats(x, out=None):
+    """Per-channel mean |x| over tokens: x fp16 [m, k] -> float64 [k]."""
+    torch = _torch()
+    _dev_tensor(x, torch.float16, "x", 2)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty(k, dtype=torch.float64, device=x.device)
+    _out_tensor(out, torch.float64, (k,), "out")
+    _lib.check("awq_calib_stats", _lib.load().awq_calib_stats(_ptr(x), m, k, _ptr(out), _stream()))
+    return out
+
+
+def awq_search_workspace_size(n, k, m, g=128, n_grid=20):
+    return int(_lib.load().awq_search_workspace_size(n, k, m, g, n_grid))
+
+
+def awq_search_scale(w, x, mean_abs, g=128, n_grid=20, workspace=None, out=None):
+    """Grid search of s = mean_abs ** alpha.  Returns (best_idx int32 [1], s16 fp16 [k],
+    inv_s16 fp16 [k], losses float64 [n_grid]) as device tensors (written into
+    ``out`` when given)."""
+    torch = _torch()
+    _dev_tensor(w, torch.float16, "w", 2)
+    _dev_tensor(x, torch.float16, "x", 2)
+    _dev_tensor(mean_abs, torch.float64, "mean_abs", 1)
+    n, k = w.shape
+    m = x.shape[0]
+    if x.shape[1] != k or mean_abs.shape[0] != k:
+        raise ValueError("w, x and mean_abs disagree on k")
+    need = awq_search_workspace_size(n, k, m, g, n_grid)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    dev = w.device
+    if out is None:
+        best = torch.empty(1, dtype=torch.int32, device=dev)
+        s16 = torch.empty(k, dtype=torch.float16, device=dev)
+        inv = torch.empty(k, dtype=torch.float16, device=dev)
+        losses = torch.empty(n_grid, dtype=torch.float64, device=dev)
+    else:
+        best, s16, inv, losses = out
+    _out_tensor(best, torch.int32, (1,), "best_idx")
+    _out_tensor(s16, torch.float16, (k,), "s16")
+    _out_tensor(inv, torch.float16, (k,), "inv_s16")
+    _out_tensor(losses, torch.float64, (n_grid,), "losses")
+    _dev_tensor(workspace, torch.uint8, "workspace")
+    st = _lib.load().awq_search_scale(_ptr(w), _ptr(x), _ptr(mean_abs), n, k, m, g, n_grid,
+                                      _ptr(best), _ptr(s16), _ptr(inv), _ptr(losses),
+                                      _ptr(workspace), workspace.numel(), _stream())
+    _lib.check("awq_search_scale", st)
+    return best, s16, inv, losses
+
+
+def awq_pack_int4(w, s16=None, g=128, out=None):
+    """Quantize and pack w (fp16 [n, k]) at channel scale s16 (fp16 [k] or None).
+    Returns (qweight int32 [n, k/8], scales fp16 [n, k/g], qzeros int32
+    [n, ceil(k/(8g))], nonfinite int32 [1]); the packed words are uint32 bit
+    patterns held in int32 tensors."""
+    torch = _torch()
+    _dev_tensor(w, torch.float16, "w", 2)
+    n, k = w.shape
+    if s16 is not None:
+        _dev_tensor(s16, torch.float16, "s16", 1)
+        if s16.shape[0] != k:
+            raise ValueError("s16 must have k entries")
+    dev = w.device
+    if out is None:
+        qw = torch.empty((n, k // 8), dtype=torch.int32, device=dev)
+        sc = torch.empty((n, k // g), dtype=torch.float16, device=dev)
+        qz = torch.empty((n, -(-k // (8 * g))), dtype=torch.int32, device=dev)
+        bad = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        qw, sc, qz, bad = out
+    _out_tensor(qw, torch.int32, (n, k // 8), "qweight")
+    _out_tensor(sc, torch.float16, (n, k // g), "scales")
+    _out_tensor(qz, torch.int32, (n, -(-k // (8 * g))), "qzeros")
+    if bad is not None:
+        _out_tensor(bad, torch.int32, (1,), "nonfinite")
+    st = _lib.load().awq_pack_int4(_ptr(w), _ptr(s16), n, k, g, _ptr(qw), _ptr(sc), _ptr(qz),
+                                   _ptr(bad), _stream())
+    _lib.check("awq_pack_int4", st)
+    return qw, sc, qz, bad
+
+
+def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
+    """y = (x * inv_s16) @ dequant(W)^T in fp16: x fp16 [m, k] -> y fp16 [m, n]."""
+    torch = _torch()
+    _dev_tensor(x, torch.float16, "x", 2)
+    _dev_tensor(qweight, torch.int32, "qweight", 2)
+    _dev_tensor(scales, torch.float16, "scales", 2)
+    _dev_tensor(qzeros, torch.int32, "qzeros", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k or scales.shape != (n, k // g) or qzeros.shape != (n, -(-k // (8 * g))):
+        raise ValueError("packed tensors do not match x and g")
+    if inv_s16 is not None:
+        _dev_tensor(inv_s16, torch.float16, "inv_s16", 1)
+        if inv_s16.shape[0] != k:
+            raise ValueError("inv_s16 must have k entries")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _out_tensor(y, torch.float16, (m, n), "y")
+    st = _lib.load().awq_linear_w4a16(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
+                                      _ptr(inv_s16), m, n, k, g, _ptr(y), _stream())
+    _lib.check("awq_linear_w4a16", st)
+    return y

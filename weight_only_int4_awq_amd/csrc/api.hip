@@ -1,0 +1,149 @@
+// C ABI entry points: argument validation on the host, then launches on the
+// caller's stream.  No entry point synchronises.
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/awq_mi355x.h"
+#include "awq_common.h"
+#include "awq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+awq_status fail(awq_status s, const char* fmt, long long a = 0, long long b = 0) {
+  snprintf(g_err, sizeof(g_err), fmt, a, b);
+  return s;
+}
+
+awq_status hip_fail(hipError_t e, const char* where) {
+  snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
+  return AWQ_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool group_ok(int32_t g) { return g == 32 || g == 64 || g == 128; }
+
+// One grow-only device scratch buffer per device for the staged activations
+// of the decode kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+size_t g_scratch_bytes[kMaxDevices] = {};
+
+awq_status get_scratch(size_t bytes, void** out) {
+  *out = nullptr;
+  if (bytes == 0) return AWQ_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(AWQ_ERR_UNSUPPORTED, "device index %lld out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_bytes[dev] < bytes) {
+    size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+    void* p = nullptr;
+    e = hipMalloc(&p, want);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(linear scratch)");
+    // the previous buffer may still be in use by queued kernels: keep it
+    // alive (grown buffers are rare and small)
+    g_scratch[dev] = p;
+    g_scratch_bytes[dev] = want;
+  }
+  *out = g_scratch[dev];
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t awq_abi_version(void) { return 1; }
+
+const char* awq_last_error(void) { return g_err; }
+
+awq_status awq_calib_stats(const uint16_t* x, int64_t m, int64_t k, double* mean_abs,
+                           void* stream) {
+  g_err[0] = 0;
+  if (!x || !mean_abs) return fail(AWQ_ERR_NULL, "awq_calib_stats: null pointer");
+  if (m < 1 || m > 8192) return fail(AWQ_ERR_SHAPE, "awq_calib_stats: m=%lld outside 1..8192", m);
+  if (k < 8 || k % 8 != 0) return fail(AWQ_ERR_SHAPE, "awq_calib_stats: k=%lld must be a positive multiple of 8", k);
+  if (!aligned(x, 16) || !aligned(mean_abs, 8)) return fail(AWQ_ERR_ALIGN, "awq_calib_stats: x must be 16-byte aligned");
+  hipError_t e = awq::launch_calib_stats(x, m, k, mean_abs, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_calib_stats launch");
+  return AWQ_OK;
+}
+
+size_t awq_search_workspace_size(int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid) {
+  if (n < 1 || k < 1 || m < 1 || n_grid < 1 || n_grid > 64 || !group_ok(g)) return 0;
+  return awq::search_layout(n, k, m, g, n_grid).total;
+}
+
+awq_status awq_search_scale(const uint16_t* w, const uint16_t* x, const double* mean_abs,
+                            int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid,
+                            int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
+                            double* losses, void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!w || !x || !mean_abs || !best_idx || !s16 || !inv_s16)
+    return fail(AWQ_ERR_NULL, "awq_search_scale: null pointer");
+  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_search_scale: g=%lld not in {32,64,128}", g);
+  if (k < g || k % g != 0) return fail(AWQ_ERR_SHAPE, "awq_search_scale: k=%lld not a positive multiple of g=%lld", k, g);
+  if (n < 1) return fail(AWQ_ERR_SHAPE, "awq_search_scale: n=%lld < 1", n);
+  if (m < 1 || m > 8192) return fail(AWQ_ERR_SHAPE, "awq_search_scale: m=%lld outside 1..8192", m);
+  if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_SHAPE, "awq_search_scale: n_grid=%lld outside 1..64", n_grid);
+  if (!aligned(w, 16) || !aligned(x, 16)) return fail(AWQ_ERR_ALIGN, "awq_search_scale: w and x must be 16-byte aligned");
+  if (!aligned(mean_abs, 8) || !aligned(s16, 2) || !aligned(inv_s16, 2) || (losses && !aligned(losses, 8)))
+    return fail(AWQ_ERR_ALIGN, "awq_search_scale: misaligned output");
+  const size_t need = awq::search_layout(n, k, m, g, n_grid).total;
+  if (!workspace || ws_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "awq_search_scale: workspace of %lld bytes < %lld needed", (long long)ws_bytes, (long long)need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_ALIGN, "awq_search_scale: workspace must be 256-byte aligned");
+  hipError_t e = awq::launch_search(w, x, mean_abs, n, k, m, g, n_grid, best_idx, s16, inv_s16,
+                                    losses, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_search_scale launch");
+  return AWQ_OK;
+}
+
+awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k, int32_t g,
+                         uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
+                         int32_t* nonfinite_groups, void* stream) {
+  g_err[0] = 0;
+  if (!w || !qweight || !scales || !qzeros) return fail(AWQ_ERR_NULL, "awq_pack_int4: null pointer");
+  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_pack_int4: g=%lld not in {32,64,128}", g);
+  if (k < g || k % g != 0) return fail(AWQ_ERR_SHAPE, "awq_pack_int4: k=%lld not a positive multiple of g=%lld", k, g);
+  if (n < 1 || n > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_pack_int4: n=%lld out of range", n);
+  if (!aligned(w, 16) || !aligned(qweight, 16) || (s16 && !aligned(s16, 16)))
+    return fail(AWQ_ERR_ALIGN, "awq_pack_int4: w, s16 and qweight must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(qzeros, 4) || (nonfinite_groups && !aligned(nonfinite_groups, 4)))
+    return fail(AWQ_ERR_ALIGN, "awq_pack_int4: misaligned output");
+  hipError_t e = awq::launch_pack(w, s16, n, k, g, qweight, scales, qzeros, nonfinite_groups,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_pack_int4 launch");
+  return AWQ_OK;
+}
+
+awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
+                            int64_t k, int32_t g, uint16_t* y, void* stream) {
+  g_err[0] = 0;
+  if (!x || !qweight || !scales || !qzeros || !y) return fail(AWQ_ERR_NULL, "awq_linear_w4a16: null pointer");
+  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: g=%lld not in {32,64,128}", g);
+  if (k < 64 || k % g != 0 || k % 64 != 0)
+    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: k=%lld must be a multiple of g=%lld and of 64", k, g);
+  if (m < 1 || m > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: m=%lld out of range", m);
+  if (n < 1 || n > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: n=%lld out of range", n);
+  if (!aligned(x, 16) || !aligned(qweight, 16))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_w4a16: x and qweight must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2) || (inv_s16 && !aligned(inv_s16, 2)))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_w4a16: misaligned pointer");
+  void* scratch = nullptr;
+  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g), &scratch);
+  if (st != AWQ_OK) return st;
+  hipError_t e = awq::launch_linear(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, scratch,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16 launch");
+  return AWQ_OK;
+}
+
+}  // extern "C"

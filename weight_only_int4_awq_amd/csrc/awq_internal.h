@@ -1,0 +1,41 @@
+// Internal launch functions behind the C ABI (host side).  Arguments are
+// already validated by the entry points in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+hipError_t launch_calib_stats(const uint16_t* x, int64_t m, int64_t k, double* out,
+                              hipStream_t stream);
+
+// Search workspace layout (bytes, 256-aligned sections):
+//   s16  [n_grid][k]        fp16 candidate scales
+//   rs   [n_grid][k]        fp32 reciprocals of the candidates
+//   part [n_grid][n_blocks] float64 per-row-block partial losses
+struct SearchLayout {
+  size_t off_s16, off_rs, off_part, total;
+  int64_t n_blocks;
+};
+SearchLayout search_layout(int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid);
+
+hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mean_abs,
+                         int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid,
+                         int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
+                         double* losses, void* workspace, hipStream_t stream);
+
+hipError_t launch_pack(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
+                       int32_t g, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
+                       int32_t* nonfinite, hipStream_t stream);
+
+// Scratch bytes the linear needs for the staged activations.
+size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g);
+
+hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                         const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
+                         int64_t n, int64_t k, int32_t g, uint16_t* y, void* scratch,
+                         hipStream_t stream);
+
+}  // namespace awq

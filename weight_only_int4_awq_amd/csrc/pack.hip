@@ -1,0 +1,124 @@
+// Real quantization and nibble packing (layout v1) of scaled weights.
+// Passage: CSDN page "LLM-AWQ学术影响力…", section "量化流程优化" (real 4-bit,
+// group-128 quantization into a packed dump) and bjdmk.com.cn page, section
+// "量化参数配置" (4 bit, group 128, zero point on).
+//
+// Launch: grid (n, ceil(k/2048)); one work-group of 256 threads per row chunk
+// of 2048 input channels; thread t owns qweight word t of the chunk (8
+// consecutive channels, one 16-byte load of W and of s).  A group of g
+// channels spans g/8 adjacent lanes (4, 8 or 16), reduced with xor shuffles.
+// The chunk holds a whole number of zero-point words (8g divides 2048), which
+// are assembled from LDS after a barrier.
+#include "awq_common.h"
+#include "awq_internal.h"
+
+namespace awq {
+
+template <int G>
+__global__ __launch_bounds__(256) void pack_int4_kernel(
+    const uint16_t* __restrict__ w, const uint16_t* __restrict__ s16, int64_t n, int64_t k,
+    uint32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
+    uint32_t* __restrict__ qzeros, int32_t* __restrict__ nonfinite) {
+  constexpr int L = G / 8;                 // lanes per group
+  constexpr int GROUPS_PER_CHUNK = 2048 / G;
+  __shared__ uint32_t zbuf[GROUPS_PER_CHUNK];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t wi = (int64_t)blockIdx.y * 256 + tid;       // word index in the row
+  const int64_t k0 = wi * 8;
+  const bool valid = k0 < k;
+
+  float v[8];
+  float mx = -__builtin_inff(), mn = __builtin_inff();
+  int bad = 0;
+  if (valid) {
+    uint4 wv = *reinterpret_cast<const uint4*>(w + row * k + k0);
+    uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    uint32_t ss[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+    if (s16 != nullptr) {
+      uint4 sv = *reinterpret_cast<const uint4*>(s16 + k0);
+      ss[0] = sv.x; ss[1] = sv.y; ss[2] = sv.z; ss[3] = sv.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t wb = (uint16_t)(ww[i >> 1] >> ((i & 1) * 16));
+      uint16_t sb = (uint16_t)(ss[i >> 1] >> ((i & 1) * 16));
+      // fp16 * fp16 is exact in fp32; one RNE rounding back to fp16
+      uint16_t pb = f2h_rn(h2f(wb) * h2f(sb));
+      bad |= f16_nonfinite(pb) ? 1 : 0;
+      v[i] = h2f(pb);
+      mx = __builtin_fmaxf(mx, v[i]);
+      mn = __builtin_fminf(mn, v[i]);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < L; off <<= 1) {
+    mx = __builtin_fmaxf(mx, shfl_xor_f(mx, off));
+    mn = __builtin_fminf(mn, shfl_xor_f(mn, off));
+    bad |= __shfl_xor(bad, off, 64);
+  }
+  const int64_t j = k0 / G;                  // group index in the row
+  const int64_t ng = k / G;
+  const int jl = tid / L;                    // group index in the chunk
+  if (valid) {
+    uint32_t word = 0;
+    uint32_t zq = 0;
+    uint16_t dbits = kF16NaN;
+    if (!bad) {
+      GroupQ gq = group_q(mx, mn);
+      dbits = gq.d_bits;
+      zq = (uint32_t)gq.z;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t q = (uint32_t)(code_minus_zero(v[i], gq) + gq.z);
+        word |= (q & 0xFu) << (4 * i);
+      }
+    }
+    qweight[row * (k / 8) + wi] = word;
+    if ((tid % L) == 0) {
+      scales[row * ng + j] = dbits;
+      zbuf[jl] = zq;
+      if (bad && nonfinite != nullptr) atomicAdd(nonfinite, 1);
+    }
+  }
+  __syncthreads();
+  // zero-point words of this chunk
+  const int64_t j0 = (int64_t)blockIdx.y * GROUPS_PER_CHUNK;
+  const int64_t groups_here = (ng - j0) < GROUPS_PER_CHUNK ? (ng - j0) : GROUPS_PER_CHUNK;
+  const int64_t zwords = (groups_here + 7) / 8;
+  const int64_t nzw = (ng + 7) / 8;
+  if (tid < zwords) {
+    uint32_t word = 0;
+    for (int i = 0; i < 8; ++i) {
+      int64_t jj = (int64_t)tid * 8 + i;
+      if (jj < groups_here) word |= (zbuf[jj] & 0xFu) << (4 * i);
+    }
+    qzeros[row * nzw + j0 / 8 + tid] = word;
+  }
+}
+
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+hipError_t launch_pack(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
+                       int32_t g, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
+                       int32_t* nonfinite, hipStream_t stream) {
+  if (nonfinite != nullptr) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, stream, nonfinite);
+  dim3 grid((unsigned)n, (unsigned)((k + 2047) / 2048));
+  switch (g) {
+    case 32:
+      hipLaunchKernelGGL(pack_int4_kernel<32>, grid, dim3(256), 0, stream, w, s16, n, k, qweight,
+                         scales, qzeros, nonfinite);
+      break;
+    case 64:
+      hipLaunchKernelGGL(pack_int4_kernel<64>, grid, dim3(256), 0, stream, w, s16, n, k, qweight,
+                         scales, qzeros, nonfinite);
+      break;
+    default:
+      hipLaunchKernelGGL(pack_int4_kernel<128>, grid, dim3(256), 0, stream, w, s16, n, k, qweight,
+                         scales, qzeros, nonfinite);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace awq
