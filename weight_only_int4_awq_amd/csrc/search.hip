@@ -5,15 +5,18 @@
 // Three kernels, all on the caller's stream:
 //  1. search_prep: s_ik = fp16_rn(max(a_k^alpha_i, 2^-14)) and 1/s_ik (fp32)
 //     for every grid point and channel (float64 pow, single fp16 rounding).
-//  2. search_loss: one work-group per (32-row block, alpha).  For every group
+//  2. search_blockscale: a power-of-two factor per 32-row block that keeps the
+//     fp16 split of the weight error in the normal range (see below).
+//  3. search_loss: one work-group per (32-row block, alpha).  For every group
 //     of g channels it fake-quantizes the 32 x g block of W' = fp16(W s_i)
 //     (exact per-element codes, see awq_common.h), forms the weight error
-//     dW = (q - z) D / s - W in fp32, splits it into fp16 hi + lo, stages both
+//     dW = ((q - z) D - W s) / s in fp32 (no cancellation: both terms of the
+//     difference are exact), splits it into fp16 hi + lo, stages both
 //     in LDS in the MFMA A-operand layout and multiplies them with the
 //     calibration tokens (B operand, straight from global memory) into fp32
 //     accumulators E = dW X^T.  After the last group it squares E in float64
 //     and writes the block's partial loss.
-//  3. search_select: sums the partials of each alpha in block order (fixed),
+//  4. search_select: sums the partials of each alpha in block order (fixed),
 //     takes the first minimum over finite losses and writes s16 and
 //     inv_s16 = fp16_rn(1/s16) (float64 quotient).
 #include <math.h>
@@ -36,6 +39,7 @@ SearchLayout search_layout(int64_t n, int64_t k, int64_t m, int32_t g, int32_t n
   L.off_s16 = off;  off = align256(off + (size_t)n_grid * (size_t)k * 2);
   L.off_rs = off;   off = align256(off + (size_t)n_grid * (size_t)k * 4);
   L.off_part = off; off = align256(off + (size_t)n_grid * (size_t)L.n_blocks * 8);
+  L.off_cblk = off; off = align256(off + (size_t)L.n_blocks * 4);
   L.total = off;
   return L;
 }
@@ -60,11 +64,56 @@ __global__ __launch_bounds__(256) void search_prep_kernel(const double* __restri
   rs[(int64_t)i * k + col] = 1.0f / h2f(sb);
 }
 
+// Per 32-row block: a power-of-two factor c for the weight error dW.  Every
+// |dW_nk| is at most about 1.03 |W_nk| (an element on quantization level 0 has
+// dW = -W; on any other level |W'| >= D/2, so |deq - W'| <= 0.51 D <= 1.02 |W'|).
+// With max|W| < 2^e the factor c = 2^(14 - e) keeps c |dW| below 17000, inside
+// fp16, while lifting small errors far above the fp16 subnormal range, so the
+// fp16 hi + lo split of c dW keeps about 22 significant bits.
+__global__ __launch_bounds__(256) void search_blockscale_kernel(const uint16_t* __restrict__ w,
+                                                                int64_t n, int64_t k,
+                                                                float* __restrict__ cblk) {
+  __shared__ uint32_t red[4];
+  const int64_t rb = blockIdx.x;
+  const int64_t r0 = rb * kSearchRows;
+  const int64_t rows = (n - r0) < kSearchRows ? (n - r0) : kSearchRows;
+  const int64_t words = rows * k / 8;          // 8 halves per 16-byte load
+  const uint4* base = reinterpret_cast<const uint4*>(w + r0 * k);
+  uint32_t mx = 0;
+  for (int64_t i = threadIdx.x; i < words; i += 256) {
+    uint4 v = base[i];
+    uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      uint32_t b = (ww[h >> 1] >> ((h & 1) * 16)) & 0x7FFFu;
+      if (b < 0x7C00u && b > mx) mx = b;         // |fp16| bits order like the values
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(mx, off, 64);
+    mx = o > mx ? o : mx;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = red[0];
+    for (int i = 1; i < 4; ++i) m = red[i] > m ? red[i] : m;
+    float c = 1.0f;
+    if (m != 0) {
+      int e;
+      (void)__builtin_frexpf(h2f((uint16_t)m), &e);   // max|W| < 2^e
+      c = __builtin_ldexpf(1.0f, 14 - e);
+    }
+    cblk[rb] = c;
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void search_loss_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ x, int64_t n, int64_t k,
     int64_t m, int32_t n_grid, int64_t n_blocks, const uint16_t* __restrict__ s16_all,
-    const float* __restrict__ rs_all, double* __restrict__ part) {
+    const float* __restrict__ rs_all, const float* __restrict__ cblk, double* __restrict__ part) {
   constexpr int EPT = G / 8;          // elements of one row-group per thread
   constexpr int KSTEPS = G / 16;      // MFMA k-steps per group
   __shared__ __attribute__((aligned(16))) uint16_t a_hi[KSTEPS * 32 * 16];
@@ -91,6 +140,7 @@ __global__ __launch_bounds__(256) void search_loss_kernel(
   const int sub = tid & 7;            // which EPT-slice of the group
   const int64_t row = rb * kSearchRows + r;
   const bool row_ok = row < n;
+  const float cscale = cblk[rb];
 
   double loss = 0.0;
   for (int64_t t0 = 0; t0 < m; t0 += kSearchTokPass) {
@@ -103,7 +153,7 @@ __global__ __launch_bounds__(256) void search_loss_kernel(
     for (int64_t j = 0; j < k / G; ++j) {
       // ---- stage 1: fake-quantize this thread's EPT elements, stage dW in LDS
       const int64_t kb = j * G + sub * EPT;
-      float wv[EPT], wp[EPT], rsv[EPT];
+      float wsx[EPT], wp[EPT], rsv[EPT];
       float mx = -__builtin_inff(), mn = __builtin_inff();
       int bad = 0;
       if (row_ok) {
@@ -119,9 +169,10 @@ __global__ __launch_bounds__(256) void search_loss_kernel(
           for (int i = 0; i < 4; ++i) {
             uint16_t wb = (uint16_t)(ww[i >> 1] >> ((i & 1) * 16));
             uint16_t sb = (uint16_t)(ss[i >> 1] >> ((i & 1) * 16));
-            uint16_t pb = f2h_rn(h2f(wb) * h2f(sb));
+            const float prod = h2f(wb) * h2f(sb);      // W s, exact in fp32
+            uint16_t pb = f2h_rn(prod);
             bad |= f16_nonfinite(pb) ? 1 : 0;
-            wv[e + i] = h2f(wb);
+            wsx[e + i] = prod;
             wp[e + i] = h2f(pb);
             rsv[e + i] = rq[i];
             mx = __builtin_fmaxf(mx, wp[e + i]);
@@ -140,8 +191,10 @@ __global__ __launch_bounds__(256) void search_loss_kernel(
         GroupQ gq = group_q(mx, mn);
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
+          // dW = (deq - W s) / s: deq and W s are exact, so the small difference is
+          // rounded once, then scaled by the block factor c (a power of two)
           float deq = code_minus_zero(wp[e], gq) * gq.d;          // exact
-          float dw = bad ? __builtin_nanf("") : __builtin_fmaf(deq, rsv[e], -wv[e]);
+          float dw = bad ? __builtin_nanf("") : (deq - wsx[e]) * (rsv[e] * cscale);
           uint16_t h = f2h_rn(dw);
           hi[e] = h;
           lo[e] = f2h_rn(dw - h2f(h));
@@ -199,7 +252,8 @@ __global__ __launch_bounds__(256) void search_loss_kernel(
     loss += ((red[0] + red[1]) + red[2]) + red[3];
     __syncthreads();
   }
-  if (tid == 0) part[(int64_t)ai * n_blocks + rb] = loss;
+  const double inv_c = 1.0 / (double)cscale;       // exact: c is a power of two
+  if (tid == 0) part[(int64_t)ai * n_blocks + rb] = loss * inv_c * inv_c;
 }
 
 __global__ __launch_bounds__(256) void search_select_kernel(
@@ -245,22 +299,25 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
   uint16_t* s16_all = reinterpret_cast<uint16_t*>(ws + L.off_s16);
   float* rs_all = reinterpret_cast<float*>(ws + L.off_rs);
   double* part = reinterpret_cast<double*>(ws + L.off_part);
+  float* cblk = reinterpret_cast<float*>(ws + L.off_cblk);
 
   hipLaunchKernelGGL(search_prep_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)n_grid),
                      dim3(256), 0, stream, mean_abs, k, n_grid, s16_all, rs_all);
+  hipLaunchKernelGGL(search_blockscale_kernel, dim3((unsigned)L.n_blocks), dim3(256), 0, stream, w,
+                     n, k, cblk);
   const unsigned nwg = (unsigned)(L.n_blocks * n_grid);
   switch (g) {
     case 32:
       hipLaunchKernelGGL(search_loss_kernel<32>, dim3(nwg), dim3(256), 0, stream, w, x, n, k, m,
-                         n_grid, L.n_blocks, s16_all, rs_all, part);
+                         n_grid, L.n_blocks, s16_all, rs_all, cblk, part);
       break;
     case 64:
       hipLaunchKernelGGL(search_loss_kernel<64>, dim3(nwg), dim3(256), 0, stream, w, x, n, k, m,
-                         n_grid, L.n_blocks, s16_all, rs_all, part);
+                         n_grid, L.n_blocks, s16_all, rs_all, cblk, part);
       break;
     default:
       hipLaunchKernelGGL(search_loss_kernel<128>, dim3(nwg), dim3(256), 0, stream, w, x, n, k, m,
-                         n_grid, L.n_blocks, s16_all, rs_all, part);
+                         n_grid, L.n_blocks, s16_all, rs_all, cblk, part);
       break;
   }
   hipLaunchKernelGGL(search_select_kernel, dim3(1), dim3(256), 0, stream, part, L.n_blocks,
