@@ -137,6 +137,8 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const ui
     return fail(AWQ_ERR_ALIGN, "awq_linear_w4a16: x and qweight must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2) || (inv_s16 && !aligned(inv_s16, 2)))
     return fail(AWQ_ERR_ALIGN, "awq_linear_w4a16: misaligned pointer");
+  if ((unsigned long long)n * (unsigned long long)k / 2 >= (1ull << 32))
+    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: packed weights of n=%lld x k=%lld exceed 4 GiB", n, k);
   void* scratch = nullptr;
   awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g), &scratch);
   if (st != AWQ_OK) return st;

@@ -5,7 +5,8 @@
 // section 二.1 (3): the activation is divided by s at inference
 // (x_tilde = x * inv_s16).
 //
-// Decode path (m <= 32): two kernels.
+// Decode path, m = 1: linear_gemv (one kernel, activations staged in LDS; see
+// below).  Decode path, 2 <= m <= 32: two kernels.
 //  * linear_prep stages x_tilde once per call as the MFMA A operand: every
 //    token contributes an fp16 hi row and an fp16 lo row (x_tilde = hi + lo,
 //    so the staged activation carries ~22 bits), 8 tokens per 16-row chunk,
@@ -37,7 +38,7 @@ constexpr int kSkinnyWaves = 8;        // waves per work-group
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g) {
-  if (m > 32) return 0;
+  if (m > 32 || m == 1) return 0;
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / g;
   size_t a = (size_t)tc * (size_t)k * 16 * 2;          // [tc][ng][4][16][g/4] halves
@@ -101,14 +102,38 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
   if (c == 0) tu[pair * 16 + r] = make_float2((float)tsum, (float)usum);
 }
 
+// Constants of the nibble unpack, made opaque to constant folding (the empty
+// asm statements emit nothing).  gfx9 VOP3 encodings take no literal
+// constants, so with literal masks the compiler splits (w & mask) | magic into
+// v_and + v_or; with the masks in SGPRs and the magic numbers in VGPRs it
+// selects a single v_and_or_b32 per fp16 pair.
+struct UnpackConsts {
+  uint32_t m_lo, m_hi, mag1024, mag64;
+};
+__device__ __forceinline__ UnpackConsts unpack_consts() {
+  UnpackConsts u;
+  u.m_lo = 0x000F000Fu;
+  u.m_hi = 0x00F000F0u;
+  u.mag1024 = 0x64006400u;
+  u.mag64 = 0x54005400u;
+  asm volatile("" : "+s"(u.m_lo));
+  asm volatile("" : "+s"(u.m_hi));
+  asm volatile("" : "+v"(u.mag1024));
+  asm volatile("" : "+v"(u.mag64));
+  return u;
+}
+
 // Unpack one qweight word into four fp16 pairs in slot order:
 // (1024+q0, 1024+q4), (64+q1, 64+q5), (1024+q2, 1024+q6), (64+q3, 64+q7).
-__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4]) {
-  out[0] = (w & 0x000F000Fu) | 0x64006400u;
-  out[1] = (w & 0x00F000F0u) | 0x54005400u;
+// Masking a nibble into the mantissa of 1024.0 (bits 0-3) or 64.0 (bits 4-7)
+// gives offset + q exactly, with no conversion instruction: 5 instructions
+// per 8 weights.
+__device__ __forceinline__ void unpack_word(uint32_t w, uint32_t out[4], const UnpackConsts& k) {
+  out[0] = (w & k.m_lo) | k.mag1024;
+  out[1] = (w & k.m_hi) | k.mag64;
   const uint32_t w8 = w >> 8;
-  out[2] = (w8 & 0x000F000Fu) | 0x64006400u;
-  out[3] = (w8 & 0x00F000F0u) | 0x54005400u;
+  out[2] = (w8 & k.m_lo) | k.mag1024;
+  out[3] = (w8 & k.m_hi) | k.mag64;
 }
 
 template <int G, int TC>
@@ -132,6 +157,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
   floatx4_t ytot[TC];
 #pragma unroll
   for (int i = 0; i < TC; ++i) ytot[i] = floatx4_t{};
+  const UnpackConsts uc = unpack_consts();
 
   for (int64_t j = wave; j < ng; j += kSkinnyWaves) {
     uint32_t wq[WPL];
@@ -157,7 +183,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
       uint32_t u[4];
-      unpack_word(wq[i], u);
+      unpack_word(wq[i], u, uc);
       bop[i] = __builtin_bit_cast(half8_t, make_uint4(u[0], u[1], u[2], u[3]));
     }
 #pragma unroll
@@ -203,6 +229,214 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- decode GEMV (m = 1)
+// Persistent work-groups of 8 waves.  A work-group stages x_tilde once in LDS
+// as the two live rows of the MFMA A operand (row 0 = fp16 hi, row 8 = fp16
+// lo; the other 14 rows read a zero block) together with the per-group offset
+// sums T and U, then walks its 16-column blocks (block b, b + grid, ...).
+// Every wave owns a fixed contiguous range of groups along K; it walks the
+// flattened sequence (block, group) with a double-buffered prefetch that
+// runs across block boundaries, so a wave always has kGemvPF groups of packed
+// weights in flight while it computes.  At the end of a block the waves meet
+// at one barrier; a designated wave sums the 8 partial rows in a fixed order
+// and stores 16 outputs while the others continue with the next block.
+#ifndef AWQ_GEMV_PF
+#define AWQ_GEMV_PF 4
+#endif
+#ifndef AWQ_GEMV_WG_PER_CU
+#define AWQ_GEMV_WG_PER_CU 2
+#endif
+constexpr int kGemvWaves = 8;
+constexpr int kGemvPF = AWQ_GEMV_PF;
+constexpr int kGemvCUs = 256;
+
+size_t gemv_lds_bytes(int64_t k, int32_t g) {
+  return (size_t)k * 4 + (size_t)(k / g) * 16 + (size_t)(g / 4) * 2 + 2 * kGemvWaves * 16 * 4;
+}
+
+template <int WPL>
+__device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t (&w)[WPL]) {
+  if constexpr (WPL == 4) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (WPL == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *p;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_gemv_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
+    const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, int64_t n, int64_t k, uint16_t* __restrict__ y) {
+  constexpr int WPL = G / 32;            // qweight words per lane per group
+  constexpr int HPL = G / 4;             // staged halves per (group, lane group, row)
+  constexpr int LPG = G / 8;             // words per group
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t ng = k / G;
+  uint16_t* xa = reinterpret_cast<uint16_t*>(smem);                 // [ng][4][2][HPL]
+  float4* tu = reinterpret_cast<float4*>(smem + (size_t)k * 4);     // [ng] (T_hi, U_hi, T_lo, U_lo)
+  uint16_t* zblk = reinterpret_cast<uint16_t*>(smem + (size_t)k * 4 + (size_t)ng * 16);  // HPL zeros
+  float* red = reinterpret_cast<float*>(smem + (size_t)k * 4 + (size_t)ng * 16 + HPL * 2);  // [2][8][16]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave: keep it (and every group index
+  // and group base address derived from it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int64_t nblk = (n + 15) / 16;
+  const int64_t my_blocks = (nblk - blockIdx.x + gridDim.x - 1) / gridDim.x;   // >= 1
+  const int64_t jb = ng * wave / kGemvWaves, je = ng * (wave + 1) / kGemvWaves;
+  const int64_t cnt = je - jb;                        // groups of this wave per block
+  const int64_t total = my_blocks * cnt;              // (block, group) items of this wave
+  const int64_t nzw = (ng + 7) / 8, kw_row = k / 8;
+
+  // Prefetch slots hold raw loaded bits only (converting at issue time would
+  // make the wave wait there: memory counters retire in order), and every
+  // load is unconditional (clamped item and column), so no branch separates
+  // a load from its use and the waits stay precise.
+  uint32_t wq[2 * kGemvPF][WPL];
+  uint16_t dsc[2 * kGemvPF];
+  uint32_t zwd[2 * kGemvPF];
+  const char* qbase = reinterpret_cast<const char*>(qweight);
+  const char* sbase = reinterpret_cast<const char*>(scales);
+  const char* zbase = reinterpret_cast<const char*>(qzeros);
+  auto item_block = [&](int64_t t) -> int64_t { return blockIdx.x + (t / cnt) * (int64_t)gridDim.x; };
+  auto issue = [&](int slot, int64_t t) {
+    t = t < total ? t : total - 1;
+    const int64_t blk = item_block(t);
+    const int64_t j = jb + t % cnt;
+    int64_t col = blk * 16 + r;
+    col = col < n ? col : n - 1;
+    // 32-bit per-lane byte offsets (the packed tensors of one call are below 4 GiB)
+    const uint32_t qoff = (uint32_t)((col * kw_row + WPL * c) * 4);
+    const uint32_t soff = (uint32_t)(col * ng * 2);
+    const uint32_t zoff = (uint32_t)(col * nzw * 4);
+    load_words<WPL>(reinterpret_cast<const uint32_t*>(qbase + j * (LPG * 4) + qoff), wq[slot]);
+    dsc[slot] = *reinterpret_cast<const uint16_t*>(sbase + j * 2 + soff);
+    zwd[slot] = *reinterpret_cast<const uint32_t*>(zbase + (j >> 3) * 4 + zoff);
+  };
+  const bool active = cnt > 0;                        // wave-uniform
+  if (active) {
+#pragma unroll
+    for (int p = 0; p < kGemvPF; ++p) issue(p, p);
+  }
+
+  // ---- stage x_tilde (hi, lo) and the offset sums in LDS
+  if (tid < HPL / 2) reinterpret_cast<uint32_t*>(zblk)[tid] = 0u;
+  const bool has_inv = inv_s != nullptr;
+  for (int64_t wi = tid; wi < k / 8; wi += kGemvWaves * 64) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + wi * 8);
+    uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    if (has_inv) sv = *reinterpret_cast<const uint4*>(inv_s + wi * 8);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    uint16_t hi[8], lo[8];
+    float th = 0.f, uh = 0.f, tl = 0.f, ul = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xt = h2f((uint16_t)(xw[e >> 1] >> ((e & 1) * 16))) *
+                       h2f((uint16_t)(sw[e >> 1] >> ((e & 1) * 16)));     // exact
+      hi[e] = f2h_rn(xt);
+      lo[e] = f2h_rn(xt - h2f(hi[e]));
+      const float off = (e & 1) ? 64.0f : 1024.0f;
+      th += off * h2f(hi[e]);
+      uh += h2f(hi[e]);
+      tl += off * h2f(lo[e]);
+      ul += h2f(lo[e]);
+    }
+    const int64_t j = wi / LPG;
+    const int wg = (int)(wi % LPG);
+    const int cc = wg / WPL, i = wg % WPL;
+    uint16_t* dh = xa + ((j * 4 + cc) * 2 + 0) * HPL + i * 8;
+    uint16_t* dl = xa + ((j * 4 + cc) * 2 + 1) * HPL + i * 8;
+    // slot order (k0, k4, k1, k5, k2, k6, k3, k7) matches unpack_word
+    uint4 vh, vl;
+    vh.x = hi[0] | ((uint32_t)hi[4] << 16); vh.y = hi[1] | ((uint32_t)hi[5] << 16);
+    vh.z = hi[2] | ((uint32_t)hi[6] << 16); vh.w = hi[3] | ((uint32_t)hi[7] << 16);
+    vl.x = lo[0] | ((uint32_t)lo[4] << 16); vl.y = lo[1] | ((uint32_t)lo[5] << 16);
+    vl.z = lo[2] | ((uint32_t)lo[6] << 16); vl.w = lo[3] | ((uint32_t)lo[7] << 16);
+    *reinterpret_cast<uint4*>(dh) = vh;
+    *reinterpret_cast<uint4*>(dl) = vl;
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) {
+      th += shfl_xor_f(th, off); uh += shfl_xor_f(uh, off);
+      tl += shfl_xor_f(tl, off); ul += shfl_xor_f(ul, off);
+    }
+    if (wg == 0) tu[j] = make_float4(th, uh, tl, ul);
+  }
+  __syncthreads();
+
+  // rows 0 (hi) and 8 (lo) of the A operand are live; the others read zeros
+  const int part = r >> 3;
+  const bool arow = (r == 0) || (r == 8);
+  const uint32_t a_lane = arow ? (uint32_t)(((c * 2 + part) * HPL) * 2) : 0u;
+  const char* a_base = arow ? reinterpret_cast<const char*>(xa) : reinterpret_cast<const char*>(zblk);
+  const uint32_t a_step = arow ? (uint32_t)(4 * 2 * HPL * 2) : 0u;      // bytes per group
+  const char* tu_lane = reinterpret_cast<const char*>(tu) + ((c >= 2) ? 8 : 0);
+  const int reducer = kGemvWaves - 1;                 // always owns at least one group
+  const UnpackConsts uc = unpack_consts();
+  float yacc = 0.0f;
+  int64_t blocks_done = 0;
+
+  // end of a column block: combine hi + lo rows, meet the other waves, reduce
+  auto finish_block = [&](int64_t blk) {
+    const float other = __shfl_xor(yacc, 32, 64);
+    float* rb = red + (blocks_done & 1) * (kGemvWaves * 16);
+    if (lane < 16) rb[wave * 16 + lane] = yacc + other;
+    yacc = 0.0f;
+    __syncthreads();
+    if (wave == reducer && lane < 16) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kGemvWaves; ++wv) sum += rb[wv * 16 + lane];
+      const int64_t col = blk * 16 + lane;
+      if (col < n) y[col] = f2h_rn(sum);
+    }
+    ++blocks_done;
+  };
+  auto consume = [&](int p, int64_t t) {
+    if (t < total) {                                   // wave-uniform
+      const int64_t j = jb + t % cnt;
+      const char* asrc = a_base + a_lane + (uint32_t)j * a_step;
+      half8_t aop[WPL];
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) aop[i] = *reinterpret_cast<const half8_t*>(asrc + 16 * i);
+      const float2 tv = *reinterpret_cast<const float2*>(tu_lane + (uint32_t)j * 16);
+      floatx4_t cacc = floatx4_t{};
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        uint32_t u[4];
+        unpack_word(wq[p][i], u, uc);
+        const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(u[0], u[1], u[2], u[3]));
+        cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[i], bop, cacc, 0, 0, 0);
+      }
+      // lanes with c >= 2 hold the lo row and read (T_lo, U_lo)
+      const float zf = (float)((zwd[p] >> (4 * (j & 7))) & 0xFu);
+      yacc = __builtin_fmaf(h2f(dsc[p]), __builtin_fmaf(-zf, tv.y, cacc[0] - tv.x), yacc);
+      if (j == je - 1) finish_block(item_block(t));
+    }
+  };
+  if (active) {
+    for (int64_t s0 = 0; s0 < total; s0 += 2 * kGemvPF) {
+#pragma unroll
+      for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p, s0 + kGemvPF + p);
+#pragma unroll
+      for (int p = 0; p < kGemvPF; ++p) consume(p, s0 + p);
+#pragma unroll
+      for (int p = 0; p < kGemvPF; ++p) issue(p, s0 + 2 * kGemvPF + p);
+#pragma unroll
+      for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p, s0 + kGemvPF + p);
+    }
+  } else {
+    // a wave without groups (k < 8 groups) still takes part in every block's barrier
+    for (int64_t bi = 0; bi < my_blocks; ++bi) finish_block(blockIdx.x + bi * (int64_t)gridDim.x);
   }
 }
 
@@ -319,6 +553,22 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
     dim3 grid((unsigned)((n + kGemmBN - 1) / kGemmBN), (unsigned)((m + kGemmBM - 1) / kGemmBM));
     hipLaunchKernelGGL(linear_gemm_kernel<G>, grid, dim3(256), 0, stream, x, qweight, scales,
                        qzeros, inv_s16, m, n, k, y);
+    return hipGetLastError();
+  }
+  if (m == 1) {
+    const size_t lds = gemv_lds_bytes(k, G);
+    const void* fn = reinterpret_cast<const void*>(&linear_gemv_kernel<G>);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t nblk = (n + 15) / 16;
+    const int64_t slots = (int64_t)kGemvCUs * AWQ_GEMV_WG_PER_CU;
+    // as many work-groups as fit at once, each with an equal share of blocks
+    const int64_t per = (nblk + slots - 1) / slots;
+    const int64_t grid = (nblk + per - 1) / per;
+    hipLaunchKernelGGL((linear_gemv_kernel<G>), dim3((unsigned)grid), dim3(kGemvWaves * 64), lds,
+                       stream, x, inv_s16, qweight, scales, qzeros, n, k, y);
     return hipGetLastError();
   }
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
