@@ -303,3 +303,12 @@ def test_linear_deterministic(P):
         y2 = P.awq_linear_w4a16(x, qw, sc, qz, None, g=128)
         torch.cuda.synchronize()
         assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("n,k,g", [(40, 16384, 32), (24, 28672, 64), (33, 8192, 32)])
+def test_linear_decode_wide_k(P, n, k, g):
+    # long K with small groups: the decode kernel's LDS plan does not fit and the
+    # staged two-kernel path runs at m = 1; other shapes exercise the boundaries
+    w = S.weights(n, k, 0.02, 440 + n)
+    x = S.activations(1, k, 441 + n, S.outlier_channels(k, 0.01, 442), 20.0)
+    _check_linear(P, w, x, None, g)

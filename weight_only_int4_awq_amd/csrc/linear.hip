@@ -38,7 +38,7 @@ constexpr int kSkinnyWaves = 8;        // waves per work-group
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g) {
-  if (m > 32 || m == 1) return 0;
+  if (m > 32) return 0;
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / g;
   size_t a = (size_t)tc * (size_t)k * 16 * 2;          // [tc][ng][4][16][g/4] halves
@@ -238,11 +238,14 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
 // lo; the other 14 rows read a zero block) together with the per-group offset
 // sums T and U, then walks its 16-column blocks (block b, b + grid, ...).
 // Every wave owns a fixed contiguous range of groups along K; it walks the
-// flattened sequence (block, group) with a double-buffered prefetch that
-// runs across block boundaries, so a wave always has kGemvPF groups of packed
-// weights in flight while it computes.  At the end of a block the waves meet
-// at one barrier; a designated wave sums the 8 partial rows in a fixed order
-// and stores 16 outputs while the others continue with the next block.
+// flattened sequence (block, group) with a double-buffered prefetch of packed
+// weights that runs across block boundaries.  The per-group scales and zero
+// points of a block are staged in LDS one block ahead with 16-byte loads (one
+// per 8 groups of a column), as packed words (fp16 scale | zero << 16) laid
+// out [group][column]: scattered 2- and 4-byte loads of them would cost as
+// many memory requests as the weights themselves.  At the end of a block the
+// waves meet at one barrier; a designated wave sums the 8 partial rows in a
+// fixed order and stores 16 outputs while the others go on.
 #ifndef AWQ_GEMV_PF
 #define AWQ_GEMV_PF 4
 #endif
@@ -253,8 +256,11 @@ constexpr int kGemvWaves = 8;
 constexpr int kGemvPF = AWQ_GEMV_PF;
 constexpr int kGemvCUs = 256;
 
+// LDS: x_tilde [ng][4][2][g/4] halves, T/U [ng] float4, zero block, scale|zero
+// words [2][ng][16], reduction rows [2][8][16] floats.
 size_t gemv_lds_bytes(int64_t k, int32_t g) {
-  return (size_t)k * 4 + (size_t)(k / g) * 16 + (size_t)(g / 4) * 2 + 2 * kGemvWaves * 16 * 4;
+  const size_t ng = (size_t)(k / g);
+  return (size_t)k * 4 + ng * 16 + (size_t)(g / 4) * 2 + 2 * ng * 16 * 4 + 2 * kGemvWaves * 16 * 4;
 }
 
 template <int WPL>
@@ -279,62 +285,105 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
   constexpr int HPL = G / 4;             // staged halves per (group, lane group, row)
   constexpr int LPG = G / 8;             // words per group
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int64_t ng = k / G;
-  uint16_t* xa = reinterpret_cast<uint16_t*>(smem);                 // [ng][4][2][HPL]
-  float4* tu = reinterpret_cast<float4*>(smem + (size_t)k * 4);     // [ng] (T_hi, U_hi, T_lo, U_lo)
-  uint16_t* zblk = reinterpret_cast<uint16_t*>(smem + (size_t)k * 4 + (size_t)ng * 16);  // HPL zeros
-  float* red = reinterpret_cast<float*>(smem + (size_t)k * 4 + (size_t)ng * 16 + HPL * 2);  // [2][8][16]
+  const int ng = (int)(k / G);
+  unsigned char* sp = smem;
+  uint16_t* xa = reinterpret_cast<uint16_t*>(sp);          sp += (size_t)k * 4;     // [ng][4][2][HPL]
+  float4* tu = reinterpret_cast<float4*>(sp);              sp += (size_t)ng * 16;   // (T_hi, U_hi, T_lo, U_lo)
+  uint16_t* zblk = reinterpret_cast<uint16_t*>(sp);        sp += HPL * 2;           // zeros
+  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);         sp += (size_t)2 * ng * 16 * 4;  // [2][ng][16]
+  float* red = reinterpret_cast<float*>(sp);                                         // [2][8][16]
 
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave: keep it (and every group index
   // and group base address derived from it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane >> 4, r = lane & 15;
-  const int64_t nblk = (n + 15) / 16;
-  const int64_t my_blocks = (nblk - blockIdx.x + gridDim.x - 1) / gridDim.x;   // >= 1
-  const int64_t jb = ng * wave / kGemvWaves, je = ng * (wave + 1) / kGemvWaves;
-  const int64_t cnt = je - jb;                        // groups of this wave per block
-  const int64_t total = my_blocks * cnt;              // (block, group) items of this wave
-  const int64_t nzw = (ng + 7) / 8, kw_row = k / 8;
+  const int nblk = (int)((n + 15) / 16);
+  const int grid = (int)gridDim.x;
+  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // >= 1
+  const int jb = ng * wave / kGemvWaves, je = ng * (wave + 1) / kGemvWaves;
+  const int cnt = je - jb;                            // groups of this wave per block
+  const int total = my_blocks * cnt;                  // (block, group) items of this wave
+  const int nzw = (ng + 7) / 8, kw_row = (int)(k / 8);
+
+  // ---- scale / zero staging: thread t < 16 * nzw owns (column t / nzw, octet t % nzw)
+  const bool sz_thread = tid < 16 * nzw;
+  const int sz_row = sz_thread ? tid / nzw : 0;
+  const int sz_oct = sz_thread ? tid % nzw : 0;
+  const bool sz_vec = (ng % 8) == 0;                  // 16-byte aligned octets
+  auto sz_load = [&](int blk, uint4& ss, uint32_t& zz) {   // registers <- global, block blk
+    blk = blk < nblk ? blk : nblk - 1;
+    int col = blk * 16 + sz_row;
+    col = col < (int)n ? col : (int)n - 1;
+    if (sz_thread) {
+      const uint16_t* srow = scales + (int64_t)col * ng + sz_oct * 8;
+      if (sz_vec) {
+        ss = *reinterpret_cast<const uint4*>(srow);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = (sz_oct * 8 + i < ng) ? srow[i] : (uint16_t)0;
+        ss = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                        h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+      }
+      zz = qzeros[(int64_t)col * nzw + sz_oct];
+    }
+  };
+  uint4 sz_s = make_uint4(0, 0, 0, 0);                // block staged at the next block end
+  uint32_t sz_z = 0;
+  auto sz_store_regs = [&](int buf, const uint4& ss, uint32_t zz) {   // LDS <- registers
+    if (sz_thread) {
+      const uint32_t sw[4] = {ss.x, ss.y, ss.z, ss.w};
+      const uint32_t sz_zv = zz;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = sz_oct * 8 + i;
+        if (j < ng)
+          szw[((size_t)buf * ng + j) * 16 + sz_row] =
+              ((sw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu) | (((sz_zv >> (4 * i)) & 0xFu) << 16);
+      }
+    }
+  };
 
   // Prefetch slots hold raw loaded bits only (converting at issue time would
   // make the wave wait there: memory counters retire in order), and every
-  // load is unconditional (clamped item and column), so no branch separates
-  // a load from its use and the waits stay precise.
+  // load is unconditional (the cursor stops on the last item, the column is
+  // clamped), so no branch separates a load from its use and the waits stay
+  // precise.  The (block, group) cursors advance incrementally in scalar
+  // registers: no division per item.
   uint32_t wq[2 * kGemvPF][WPL];
-  uint16_t dsc[2 * kGemvPF];
-  uint32_t zwd[2 * kGemvPF];
   const char* qbase = reinterpret_cast<const char*>(qweight);
-  const char* sbase = reinterpret_cast<const char*>(scales);
-  const char* zbase = reinterpret_cast<const char*>(qzeros);
-  auto item_block = [&](int64_t t) -> int64_t { return blockIdx.x + (t / cnt) * (int64_t)gridDim.x; };
-  auto issue = [&](int slot, int64_t t) {
-    t = t < total ? t : total - 1;
-    const int64_t blk = item_block(t);
-    const int64_t j = jb + t % cnt;
-    int64_t col = blk * 16 + r;
-    col = col < n ? col : n - 1;
-    // 32-bit per-lane byte offsets (the packed tensors of one call are below 4 GiB)
-    const uint32_t qoff = (uint32_t)((col * kw_row + WPL * c) * 4);
-    const uint32_t soff = (uint32_t)(col * ng * 2);
-    const uint32_t zoff = (uint32_t)(col * nzw * 4);
-    load_words<WPL>(reinterpret_cast<const uint32_t*>(qbase + j * (LPG * 4) + qoff), wq[slot]);
-    dsc[slot] = *reinterpret_cast<const uint16_t*>(sbase + j * 2 + soff);
-    zwd[slot] = *reinterpret_cast<const uint32_t*>(zbase + (j >> 3) * 4 + zoff);
+  int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;    // issue cursor
+  auto issue = [&](int slot) {
+    int col = i_blk * 16 + r;
+    col = col < (int)n ? col : (int)n - 1;
+    // 32-bit per-lane byte offset (the packed tensors of one call are below 4 GiB)
+    const uint32_t qoff = ((uint32_t)col * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
+    load_words<WPL>(reinterpret_cast<const uint32_t*>(qbase + (int64_t)i_j * (LPG * 4) + qoff), wq[slot]);
+    if (i_left > 1) {
+      --i_left;
+      if (++i_j == je) { i_j = jb; i_blk += grid; }
+    }
   };
   const bool active = cnt > 0;                        // wave-uniform
   if (active) {
 #pragma unroll
-    for (int p = 0; p < kGemvPF; ++p) issue(p, p);
+    for (int p = 0; p < kGemvPF; ++p) issue(p);
   }
+  // every prologue load is issued before anything waits on one (memory
+  // counters retire in order): weights, the scales of blocks 0 and 1, then x
+  uint4 sz_s0 = make_uint4(0, 0, 0, 0);
+  uint32_t sz_z0 = 0;
+  sz_load((int)blockIdx.x, sz_s0, sz_z0);             // block 0 of this work-group
+  sz_load((int)blockIdx.x + grid, sz_s, sz_z);        // block 1, stored at the first block end
 
   // ---- stage x_tilde (hi, lo) and the offset sums in LDS
   if (tid < HPL / 2) reinterpret_cast<uint32_t*>(zblk)[tid] = 0u;
   const bool has_inv = inv_s != nullptr;
-  for (int64_t wi = tid; wi < k / 8; wi += kGemvWaves * 64) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + wi * 8);
+  for (int wi = tid; wi < kw_row; wi += kGemvWaves * 64) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + (int64_t)wi * 8);
     uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-    if (has_inv) sv = *reinterpret_cast<const uint4*>(inv_s + wi * 8);
+    if (has_inv) sv = *reinterpret_cast<const uint4*>(inv_s + (int64_t)wi * 8);
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
     const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
     uint16_t hi[8], lo[8];
@@ -351,8 +400,8 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
       tl += off * h2f(lo[e]);
       ul += h2f(lo[e]);
     }
-    const int64_t j = wi / LPG;
-    const int wg = (int)(wi % LPG);
+    const int j = wi / LPG;
+    const int wg = wi % LPG;
     const int cc = wg / WPL, i = wg % WPL;
     uint16_t* dh = xa + ((j * 4 + cc) * 2 + 0) * HPL + i * 8;
     uint16_t* dl = xa + ((j * 4 + cc) * 2 + 1) * HPL + i * 8;
@@ -371,6 +420,7 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
     }
     if (wg == 0) tu[j] = make_float4(th, uh, tl, ul);
   }
+  sz_store_regs(0, sz_s0, sz_z0);
   __syncthreads();
 
   // rows 0 (hi) and 8 (lo) of the A operand are live; the others read zeros
@@ -383,10 +433,12 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
   const int reducer = kGemvWaves - 1;                 // always owns at least one group
   const UnpackConsts uc = unpack_consts();
   float yacc = 0.0f;
-  int64_t blocks_done = 0;
+  int blocks_done = 0;
 
-  // end of a column block: combine hi + lo rows, meet the other waves, reduce
-  auto finish_block = [&](int64_t blk) {
+  // end of a column block: stage the scales of the block after next, combine
+  // hi + lo rows, meet the other waves, reduce
+  auto finish_block = [&](int blk) {
+    sz_store_regs((blocks_done + 1) & 1, sz_s, sz_z);
     const float other = __shfl_xor(yacc, 32, 64);
     float* rb = red + (blocks_done & 1) * (kGemvWaves * 16);
     if (lane < 16) rb[wave * 16 + lane] = yacc + other;
@@ -396,19 +448,22 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
       float sum = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < kGemvWaves; ++wv) sum += rb[wv * 16 + lane];
-      const int64_t col = blk * 16 + lane;
+      const int64_t col = (int64_t)blk * 16 + lane;
       if (col < n) y[col] = f2h_rn(sum);
     }
     ++blocks_done;
+    sz_load(blk + 2 * grid, sz_s, sz_z);
   };
-  auto consume = [&](int p, int64_t t) {
-    if (t < total) {                                   // wave-uniform
-      const int64_t j = jb + t % cnt;
+  int c_blk = (int)blockIdx.x, c_j = jb, c_left = total;    // consume cursor
+  auto consume = [&](int p) {
+    if (c_left > 0) {                                 // wave-uniform
+      const int j = c_j;
       const char* asrc = a_base + a_lane + (uint32_t)j * a_step;
       half8_t aop[WPL];
 #pragma unroll
       for (int i = 0; i < WPL; ++i) aop[i] = *reinterpret_cast<const half8_t*>(asrc + 16 * i);
       const float2 tv = *reinterpret_cast<const float2*>(tu_lane + (uint32_t)j * 16);
+      const uint32_t szv = szw[((blocks_done & 1) * ng + j) * 16 + r];
       floatx4_t cacc = floatx4_t{};
 #pragma unroll
       for (int i = 0; i < WPL; ++i) {
@@ -418,25 +473,30 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
         cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[i], bop, cacc, 0, 0, 0);
       }
       // lanes with c >= 2 hold the lo row and read (T_lo, U_lo)
-      const float zf = (float)((zwd[p] >> (4 * (j & 7))) & 0xFu);
-      yacc = __builtin_fmaf(h2f(dsc[p]), __builtin_fmaf(-zf, tv.y, cacc[0] - tv.x), yacc);
-      if (j == je - 1) finish_block(item_block(t));
+      const float zf = (float)(szv >> 16);
+      yacc = __builtin_fmaf(h2f((uint16_t)szv), __builtin_fmaf(-zf, tv.y, cacc[0] - tv.x), yacc);
+      --c_left;
+      if (++c_j == je) {
+        finish_block(c_blk);
+        c_j = jb;
+        c_blk += grid;
+      }
     }
   };
   if (active) {
-    for (int64_t s0 = 0; s0 < total; s0 += 2 * kGemvPF) {
+    for (int s0 = 0; s0 < total; s0 += 2 * kGemvPF) {
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p, s0 + kGemvPF + p);
+      for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p);
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) consume(p, s0 + p);
+      for (int p = 0; p < kGemvPF; ++p) consume(p);
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) issue(p, s0 + 2 * kGemvPF + p);
+      for (int p = 0; p < kGemvPF; ++p) issue(p);
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p, s0 + kGemvPF + p);
+      for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p);
     }
   } else {
-    // a wave without groups (k < 8 groups) still takes part in every block's barrier
-    for (int64_t bi = 0; bi < my_blocks; ++bi) finish_block(blockIdx.x + bi * (int64_t)gridDim.x);
+    // a wave without groups (fewer than 8 groups in k) still meets every block's barrier
+    for (int bi = 0; bi < my_blocks; ++bi) finish_block((int)blockIdx.x + bi * grid);
   }
 }
 
@@ -555,7 +615,11 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
                        qzeros, inv_s16, m, n, k, y);
     return hipGetLastError();
   }
-  if (m == 1) {
+  // the fused decode kernel needs its LDS plan to fit (160 KiB) and one
+  // scale/zero octet per thread (16 columns x ceil(ng/8) octets <= 512);
+  // other shapes take the staged two-kernel path below
+  const int64_t ng_all = k / G;
+  if (m == 1 && gemv_lds_bytes(k, G) <= 160 * 1024 && 16 * ((ng_all + 7) / 8) <= kGemvWaves * 64) {
     const size_t lds = gemv_lds_bytes(k, G);
     const void* fn = reinterpret_cast<const void*>(&linear_gemv_kernel<G>);
     if (lds > 65536) {
@@ -563,10 +627,13 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
       if (e != hipSuccess) return e;
     }
     const int64_t nblk = (n + 15) / 16;
-    const int64_t slots = (int64_t)kGemvCUs * AWQ_GEMV_WG_PER_CU;
-    // as many work-groups as fit at once, each with an equal share of blocks
-    const int64_t per = (nblk + slots - 1) / slots;
-    const int64_t grid = (nblk + per - 1) / per;
+    // work-groups resident at once: bounded by the launch bound and by LDS
+    int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)lds;
+    per_cu = per_cu < AWQ_GEMV_WG_PER_CU ? per_cu : AWQ_GEMV_WG_PER_CU;
+    per_cu = per_cu > 0 ? per_cu : 1;
+    const int64_t slots = (int64_t)kGemvCUs * per_cu;
+    // as many work-groups as fit at once; blocks go round-robin
+    const int64_t grid = nblk < slots ? nblk : slots;
     hipLaunchKernelGGL((linear_gemv_kernel<G>), dim3((unsigned)grid), dim3(kGemvWaves * 64), lds,
                        stream, x, inv_s16, qweight, scales, qzeros, n, k, y);
     return hipGetLastError();
