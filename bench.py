@@ -46,6 +46,27 @@ def gemv_bytes(m, n, k, g):
     return n * k // 2 + 2 * n * (k // g) + 4 * n * (-(-k // (8 * g))) + 2 * m * k + 2 * k + 2 * m * n
 
 
+def measured_traffic(root):
+    """HBM bytes per decode-GEMV launch from the committed counter summary, if it
+    was taken on the current kernel source (else None)."""
+    import hashlib
+    import pathlib
+    import re
+    root = pathlib.Path(root)
+    md = root / "profiles" / "gemv_w4a16_m1_g128_llama3_8b_stack.md"
+    src = root / "weight_only_int4_awq_amd" / "csrc" / "linear.hip"
+    try:
+        text = md.read_text()
+        sha = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    except OSError:
+        return None
+    m_t = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, flags=re.M)
+    m_s = re.search(r"^source_sha256_prefix:\s*([0-9a-f]+)", text, flags=re.M)
+    if not m_t or not m_s or m_s.group(1) != sha:
+        return None
+    return int(m_t.group(1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,7 +286,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(bytes_per_launch / avg_launch / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(bytes_per_launch / avg_launch / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "W4A16 decode GEMV (M=1, g=128)",
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "kernel": "W4A16 decode GEMV (M=1, g=128)",
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch * 1e6},
         "roofline_gemm": {"bound": "mfma", "achieved": round(rows["prefill_m2048"]["TFLOPs"], 2),
                           "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
