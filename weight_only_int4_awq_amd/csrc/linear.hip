@@ -23,10 +23,7 @@
 //    group, y += D * (C - T - z U) removes the offset and the zero point
 //    exactly in fp32.  Waves of a work-group split the groups of K; their
 //    partial sums meet in LDS in a fixed order.
-// Prefill path (m > 32): linear_gemm, 128 x 128 output tiles; each K-step
-// dequantizes a 128 x 32 weight tile ((q - z) * D * inv_s, rounded once to
-// fp16) into LDS next to the fp16 activation tile and runs
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation.
+// Prefill path (m > 32): linear_gemm (see its comment below).
 #include "awq_common.h"
 #include "awq_internal.h"
 
@@ -501,106 +498,200 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
 }
 
 // ---------------------------------------------------------------- prefill GEMM
-constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 32;
+// Work-group tile 256 tokens x 128 output columns, K-step 64, 4 waves in a
+// 2 x 2 arrangement, each wave 128 x 64 = 4 x 2 blocks of
+// v_mfma_f32_32x32x16_f16 (fp32 accumulators).
+//  * A (activations): each K-step the work-group loads the 256 x 64 tile with
+//    16-byte loads, multiplies by inv_s in fp16 (one rounding of x_tilde),
+//    permutes every 8-channel chunk into the nibble-unpack slot order and
+//    stores it into one of two LDS stages (16-byte chunks XOR-swizzled by row,
+//    so a wave's fragment reads hit distinct banks).
+//  * B (weights) never touches LDS: lane (column j, half c) of a wave loads
+//    the 4 qweight words of its column for the K-step directly (one 16-byte
+//    load), and dequantizes them in registers: nibbles masked into fp16
+//    (offset + q), the offset and zero point removed exactly with
+//    v_pk_add_f16, the step applied with v_pk_mul_f16 (one rounding).  MFMA
+//    step s of the K-step uses word 4c + s, and the A fragment of lane half c
+//    reads the matching channel chunk 4c + s, so both operands agree on the
+//    K order.
+//  * Scales and zero words of the work-group's 128 columns are staged in LDS
+//    once.  The next K-step's global loads are in flight while the current
+//    one is multiplied.
+constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 64;
+
+size_t gemm_lds_bytes(int64_t k, int32_t g) {
+  const size_t ng = (size_t)(k / g), nzw = (ng + 7) / 8;
+  const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
+  return (size_t)2 * kGemmBM * kGemmBK * 2 + s_bytes + (size_t)kGemmBN * nzw * 4;
+}
+
+__device__ __forceinline__ uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
 
 template <int G>
-__global__ __launch_bounds__(256) void linear_gemm_kernel(
+__global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
     const uint16_t* __restrict__ inv_s, int64_t m, int64_t n, int64_t k,
-    uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t a_l[kGemmBM * kGemmBK];
-  __shared__ __attribute__((aligned(16))) uint16_t b_l[kGemmBN * kGemmBK];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;     // 2 x 2 waves, 64 x 64 each
-  const int64_t m0 = (int64_t)blockIdx.y * kGemmBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kGemmBN;
-  const int64_t ng = k / G;
-  const int64_t nzw = (ng + 7) / 8;
-  const int64_t kw_row = k / 8;
+    uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int ng = (int)(k / G), nzw = (ng + 7) / 8;
+  uint16_t* a_st = reinterpret_cast<uint16_t*>(smem);                        // [2][256][8][8]
+  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem + 2 * kGemmBM * kGemmBK * 2);   // [128][ng]
+  const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
+  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + 2 * kGemmBM * kGemmBK * 2 + s_bytes);  // [128][nzw]
 
-  floatx16_t acc[2][2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  // XCD-aware tile order: each XCD gets a contiguous range of tiles, M fastest,
+  // so the work-groups that share a weight tile share that XCD's L2
+  const int total = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int per = total / 8, rem = total % 8;
+  const int xcd = bid % 8, slot = bid / 8;
+  const int tile = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int64_t m0 = (int64_t)tm * kGemmBM, n0 = (int64_t)tn * kGemmBN;
+  const int64_t kw_row = k / 8;
+  const int nk = (int)(k / kGemmBK);
+
+  // ---- scales and zero words of this tile's columns (rows of W)
+  for (int i = tid; i < kGemmBN * ng; i += 256) {
+    const int r = i / ng, gg = i % ng;
+    int64_t col = n0 + r;
+    col = col < n ? col : n - 1;
+    s_l[i] = scales[col * ng + gg];
+  }
+  for (int i = tid; i < kGemmBN * nzw; i += 256) {
+    const int r = i / nzw, w = i % nzw;
+    int64_t col = n0 + r;
+    col = col < n ? col : n - 1;
+    z_l[i] = qzeros[col * nzw + w];
+  }
+
+  // ---- A loader: thread owns chunk (tid % 8) of rows tid / 8 + 32 i, i = 0..7
+  const int a_ch = tid & 7, a_r0 = tid >> 3;
+  const bool has_inv = inv_s != nullptr;
+  uint4 xa[8];
+  uint4 iv;
+  auto load_a = [&](int kt) {
+    const int64_t kk = (int64_t)kt * kGemmBK + a_ch * 8;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i) {
+      int64_t row = m0 + a_r0 + 32 * i;
+      row = row < m ? row : m - 1;
+      xa[i] = *reinterpret_cast<const uint4*>(x + row * k + kk);
+    }
+    iv = has_inv ? *reinterpret_cast<const uint4*>(inv_s + kk)
+                 : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  };
+  auto store_a = [&](int stage) {
+    const half2_t i0 = __builtin_bit_cast(half2_t, iv.x), i1 = __builtin_bit_cast(half2_t, iv.y);
+    const half2_t i2 = __builtin_bit_cast(half2_t, iv.z), i3 = __builtin_bit_cast(half2_t, iv.w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // x_tilde = x * inv_s (fp16, one rounding), natural pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7)
+      const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].x) * i0);
+      const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].y) * i1);
+      const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].z) * i2);
+      const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].w) * i3);
+      // unpack slot order (k0,k4) (k1,k5) (k2,k6) (k3,k7)
+      uint4 v;
+      v.x = perm_bytes(p2, p0, 0x05040100u);
+      v.y = perm_bytes(p2, p0, 0x07060302u);
+      v.z = perm_bytes(p3, p1, 0x05040100u);
+      v.w = perm_bytes(p3, p1, 0x07060302u);
+      const int row = a_r0 + 32 * i;
+      const int sw = a_ch ^ (row & 7);
+      *reinterpret_cast<uint4*>(a_st + ((size_t)(stage * kGemmBM + row) * 8 + sw) * 8) = v;
+    }
+  };
+
+  // ---- B loader: lane (j = lane % 32, c = lane / 32) of block bn loads words 4c..4c+3
+  const int bj = lane & 31, bc = lane >> 5;
+  uint4 wb[2];
+  auto load_b = [&](int kt) {
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn) {
+      int64_t col = n0 + wn * 64 + bn * 32 + bj;
+      col = col < n ? col : n - 1;
+      wb[bn] = *reinterpret_cast<const uint4*>(qweight + col * kw_row + (int64_t)kt * 8 + 4 * bc);
+    }
+  };
+
+  floatx16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = floatx16_t{};
 
-  // loader roles
-  const int b_row = tid >> 1;                  // 0..127
-  const int b_half = tid & 1;                  // which 16 channels of the 32
-  const int64_t b_col = n0 + b_row;
+  load_a(0);
+  load_b(0);
+  store_a(0);
+  __syncthreads();
+  const UnpackConsts uc = unpack_consts();
+  const int a_row_base = wm * 128 + (lane & 31);
 
-  for (int64_t k0 = 0; k0 < k; k0 += kGemmBK) {
-    // A tile: 128 tokens x 32 channels, 2 x 16 bytes per thread
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint4 wcur[2] = {wb[0], wb[1]};
+    const int ktn = kt + 1 < nk ? kt + 1 : kt;        // the last step reloads itself (unused)
+    load_a(ktn);
+    load_b(ktn);
+    // dequantize this K-step's weights: bq[bn][s] is the B operand of MFMA step s
+    half8_t bq[2][4];
+    const int grp = (kt * kGemmBK + 32 * bc) / G;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int idx = tid + it * 256;          // 0..511
-      const int ar = idx >> 2, ac = (idx & 3) * 8;
-      const int64_t t = m0 + ar;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < m) v = *reinterpret_cast<const uint4*>(x + t * k + k0 + ac);
-      *reinterpret_cast<uint4*>(&a_l[ar * kGemmBK + ac]) = v;
-    }
-    // B tile: 128 output rows x 32 channels, dequantized to fp16
-    {
-      uint16_t outv[16];
-      if (b_col < n) {
-        const int64_t kk = k0 + b_half * 16;
-        const int64_t j = kk / G;
-        const uint2 wv = *reinterpret_cast<const uint2*>(qweight + b_col * kw_row + kk / 8);
-        const float d = h2f(scales[b_col * ng + j]);
-        const float z = (float)((qzeros[b_col * nzw + (j >> 3)] >> (4 * (j & 7))) & 0xFu);
-        const uint32_t ww[2] = {wv.x, wv.y};
+    for (int bn = 0; bn < 2; ++bn) {
+      const int r = wn * 64 + bn * 32 + bj;
+      const float d = h2f(s_l[r * ng + grp]);
+      const float z = (float)((z_l[r * nzw + (grp >> 3)] >> (4 * (grp & 7))) & 0xFu);
+      const half2_t dd = {(half_t)d, (half_t)d};
+      const half2_t o1024 = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};   // exact
+      const half2_t o64 = {(half_t)(-64.0f - z), (half_t)(-64.0f - z)};
+      const uint32_t ww[4] = {wcur[bn].x, wcur[bn].y, wcur[bn].z, wcur[bn].w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float q = (float)((ww[e >> 3] >> (4 * (e & 7))) & 0xFu);
-          float v = (q - z) * d;                                   // exact
-          if (inv_s != nullptr) v *= h2f(inv_s[kk + e]);
-          outv[e] = f2h_rn(v);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) outv[e] = 0;
+      for (int s = 0; s < 4; ++s) {
+        uint32_t u[4];
+        unpack_word(ww[s], u, uc);
+        const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024) * dd;
+        const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64) * dd;
+        const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024) * dd;
+        const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64) * dd;
+        bq[bn][s] = __builtin_bit_cast(half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0),
+                                                          __builtin_bit_cast(uint32_t, q1),
+                                                          __builtin_bit_cast(uint32_t, q2),
+                                                          __builtin_bit_cast(uint32_t, q3)));
       }
-      uint4 p0, p1;
-      p0.x = outv[0] | ((uint32_t)outv[1] << 16);  p0.y = outv[2] | ((uint32_t)outv[3] << 16);
-      p0.z = outv[4] | ((uint32_t)outv[5] << 16);  p0.w = outv[6] | ((uint32_t)outv[7] << 16);
-      p1.x = outv[8] | ((uint32_t)outv[9] << 16);  p1.y = outv[10] | ((uint32_t)outv[11] << 16);
-      p1.z = outv[12] | ((uint32_t)outv[13] << 16); p1.w = outv[14] | ((uint32_t)outv[15] << 16);
-      *reinterpret_cast<uint4*>(&b_l[b_row * kGemmBK + b_half * 16]) = p0;
-      *reinterpret_cast<uint4*>(&b_l[b_row * kGemmBK + b_half * 16 + 8]) = p1;
     }
-    __syncthreads();
+    const uint16_t* a_stage = a_st + (size_t)(kt & 1) * kGemmBM * 64;
 #pragma unroll
-    for (int ks = 0; ks < kGemmBK / 16; ++ks) {
-      half8_t av[2], bv[2];
+    for (int s = 0; s < 4; ++s) {
+      const int ch = 4 * bc + s;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ar = wm * 64 + i * 32 + (lane & 31);
-        av[i] = *reinterpret_cast<const half8_t*>(&a_l[ar * kGemmBK + ks * 16 + (lane >> 5) * 8]);
-        const int br = wn * 64 + i * 32 + (lane & 31);
-        bv[i] = *reinterpret_cast<const half8_t*>(&b_l[br * kGemmBK + ks * 16 + (lane >> 5) * 8]);
+      for (int bm = 0; bm < 4; ++bm) {
+        const int row = a_row_base + bm * 32;
+        const half8_t av = *reinterpret_cast<const half8_t*>(a_stage + ((size_t)row * 8 + (ch ^ (row & 7))) * 8);
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bq[bn][s], acc[bm][bn], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[jj], acc[i][jj], 0, 0, 0);
     }
+    if (kt + 1 < nk) store_a((kt + 1) & 1);
     __syncthreads();
   }
-  // epilogue: 32x32 accumulator layout, value e of lane l is
-  // row 8*(e/4) + 4*(l/32) + e%4, column l%32
+
+  // ---- epilogue: value e of lane l in block (bm, bn) is row 8(e/4) + 4(l/32) + e%4, column l%32
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int bn = 0; bn < 2; ++bn)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t t = m0 + wm * 64 + i * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
-        const int64_t c = n0 + wn * 64 + jj * 32 + (lane & 31);
-        if (t < m && c < n) y[t * n + c] = f2h_rn(acc[i][jj][e]);
+        const int64_t t = m0 + wm * 128 + bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+        const int64_t cidx = n0 + wn * 64 + bn * 32 + (lane & 31);
+        if (t < m && cidx < n) y[t * n + cidx] = f2h_rn(acc[bm][bn][e]);
       }
 }
 
@@ -610,9 +701,17 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
                                   const uint16_t* inv_s16, int64_t m, int64_t n, int64_t k,
                                   uint16_t* y, void* scratch, hipStream_t stream) {
   if (m > 32) {
-    dim3 grid((unsigned)((n + kGemmBN - 1) / kGemmBN), (unsigned)((m + kGemmBM - 1) / kGemmBM));
-    hipLaunchKernelGGL(linear_gemm_kernel<G>, grid, dim3(256), 0, stream, x, qweight, scales,
-                       qzeros, inv_s16, m, n, k, y);
+    const size_t lds = gemm_lds_bytes(k, G);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<G>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    const int tiles_m = (int)((m + kGemmBM - 1) / kGemmBM);
+    const int tiles_n = (int)((n + kGemmBN - 1) / kGemmBN);
+    hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), lds,
+                       stream, x, qweight, scales, qzeros, inv_s16, m, n, k, y, tiles_m, tiles_n);
     return hipGetLastError();
   }
   // the fused decode kernel needs its LDS plan to fit (160 KiB) and one
