@@ -35,7 +35,7 @@ constexpr int kSkinnyWaves = 8;        // waves per work-group
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g) {
-  if (m > 32) return 0;
+  if (m > 32) return align256((size_t)m * (size_t)k * 2);     // scaled, permuted activations
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / g;
   size_t a = (size_t)tc * (size_t)k * 16 * 2;          // [tc][ng][4][16][g/4] halves
@@ -501,11 +501,12 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
 // Work-group tile 256 tokens x 128 output columns, K-step 64, 4 waves in a
 // 2 x 2 arrangement, each wave 128 x 64 = 4 x 2 blocks of
 // v_mfma_f32_32x32x16_f16 (fp32 accumulators).
-//  * A (activations): each K-step the work-group loads the 256 x 64 tile with
-//    16-byte loads, multiplies by inv_s in fp16 (one rounding of x_tilde),
-//    permutes every 8-channel chunk into the nibble-unpack slot order and
-//    stores it into one of two LDS stages (16-byte chunks XOR-swizzled by row,
-//    so a wave's fragment reads hit distinct banks).
+//  * A (activations): linear_xprep first writes x_tilde = fp16(x * inv_s)
+//    once per call, every 8-channel chunk permuted into the nibble-unpack
+//    slot order.  Each K-step the work-group copies its 256 x 64 tile straight
+//    from global memory into one of two LDS stages (global_load_lds, 16 bytes
+//    per lane; 16-byte chunks XOR-swizzled by row, so the 16 lanes served per
+//    LDS cycle hit distinct banks).
 //  * B (weights) never touches LDS: lane (column j, half c) of a wave loads
 //    the 4 qweight words of its column for the K-step directly (one 16-byte
 //    load), and dequantizes them in registers: nibbles masked into fp16
@@ -518,29 +519,64 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
 //    once.  The next K-step's global loads are in flight while the current
 //    one is multiplied.
 constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 64;
-
-size_t gemm_lds_bytes(int64_t k, int32_t g) {
-  const size_t ng = (size_t)(k / g), nzw = (ng + 7) / 8;
-  const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
-  return (size_t)2 * kGemmBM * kGemmBK * 2 + s_bytes + (size_t)kGemmBN * nzw * 4;
-}
+#ifndef AWQ_GEMM_SWZ_SHIFT
+#define AWQ_GEMM_SWZ_SHIFT 1
+#endif
 
 __device__ __forceinline__ uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// x_tilde = fp16_rn(x * inv_s), every 8-channel chunk permuted into the
+// nibble-unpack slot order (k0,k4) (k1,k5) (k2,k6) (k3,k7); one pass over the
+// activations per call, so the GEMM's activation staging is a plain copy.
+__global__ __launch_bounds__(256) void linear_xprep_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ inv_s,
+                                                           int64_t m, int64_t k,
+                                                           uint16_t* __restrict__ xt) {
+  const int64_t chunks = m * (k / 8);
+  const bool has_inv = inv_s != nullptr;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * 256) {
+    const int64_t kk = (c % (k / 8)) * 8;
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + c * 8);
+    const uint4 iv = has_inv ? *reinterpret_cast<const uint4*>(inv_s + kk)
+                             : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, iv.x));
+    const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, iv.y));
+    const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, iv.z));
+    const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.w) * __builtin_bit_cast(half2_t, iv.w));
+    uint4 v;
+    v.x = perm_bytes(p2, p0, 0x05040100u);
+    v.y = perm_bytes(p2, p0, 0x07060302u);
+    v.z = perm_bytes(p3, p1, 0x05040100u);
+    v.w = perm_bytes(p3, p1, 0x07060302u);
+    *reinterpret_cast<uint4*>(xt + c * 8) = v;
+  }
+}
+
+// dynamic LDS of the GEMM (the two activation stages are static: 64 KiB)
+size_t gemm_lds_bytes(int64_t k, int32_t g) {
+  const size_t ng = (size_t)(k / g), nzw = (ng + 7) / 8;
+  const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
+  return s_bytes + (size_t)kGemmBN * nzw * 4;
 }
 
 template <int G>
 __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-    const uint16_t* __restrict__ inv_s, int64_t m, int64_t n, int64_t k,
-    uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
+    int64_t m, int64_t n, int64_t k, uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // two distinct stage objects: the compiler can see that the copies into one
+  // stage never alias the fragment reads of the other, so it does not wait for
+  // the copies before reading
+  __shared__ __attribute__((aligned(16))) uint16_t a_st0[kGemmBM * kGemmBK];
+  __shared__ __attribute__((aligned(16))) uint16_t a_st1[kGemmBM * kGemmBK];
   const int ng = (int)(k / G), nzw = (ng + 7) / 8;
-  uint16_t* a_st = reinterpret_cast<uint16_t*>(smem);                        // [2][256][8][8]
-  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem + 2 * kGemmBM * kGemmBK * 2);   // [128][ng]
+  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem);                          // [128][ng]
   const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
-  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + 2 * kGemmBM * kGemmBK * 2 + s_bytes);  // [128][nzw]
+  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + s_bytes);                // [128][nzw]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -571,55 +607,46 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
     z_l[i] = qzeros[col * nzw + w];
   }
 
-  // ---- A loader: thread owns chunk (tid % 8) of rows tid / 8 + 32 i, i = 0..7
-  const int a_ch = tid & 7, a_r0 = tid >> 3;
-  const bool has_inv = inv_s != nullptr;
-  uint4 xa[8];
-  uint4 iv;
-  auto load_a = [&](int kt) {
-    const int64_t kk = (int64_t)kt * kGemmBK + a_ch * 8;
+  // ---- A loader: direct global -> LDS copies (global_load_lds_dwordx4).  One
+  // wave instruction fills 64 consecutive 16-byte LDS slots (8 rows x 8
+  // chunks); lane i writes slot i, so the XOR swizzle of the chunk position is
+  // applied on the global side: lane (row r, slot p) fetches logical chunk
+  // p ^ ((r >> S) & 7).  Wave w fills rows 64 w .. 64 w + 63 of the stage.
+  // The activations arrive already scaled and slot-permuted (linear_xprep).
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const int a_lr = lane >> 3, a_p = lane & 7;
+  const uint16_t* a_src[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t row = m0 + a_r0 + 32 * i;
-      row = row < m ? row : m - 1;
-      xa[i] = *reinterpret_cast<const uint4*>(x + row * k + kk);
-    }
-    iv = has_inv ? *reinterpret_cast<const uint4*>(inv_s + kk)
-                 : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-  };
-  auto store_a = [&](int stage) {
-    const half2_t i0 = __builtin_bit_cast(half2_t, iv.x), i1 = __builtin_bit_cast(half2_t, iv.y);
-    const half2_t i2 = __builtin_bit_cast(half2_t, iv.z), i3 = __builtin_bit_cast(half2_t, iv.w);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // x_tilde = x * inv_s (fp16, one rounding), natural pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7)
-      const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].x) * i0);
-      const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].y) * i1);
-      const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].z) * i2);
-      const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xa[i].w) * i3);
-      // unpack slot order (k0,k4) (k1,k5) (k2,k6) (k3,k7)
-      uint4 v;
-      v.x = perm_bytes(p2, p0, 0x05040100u);
-      v.y = perm_bytes(p2, p0, 0x07060302u);
-      v.z = perm_bytes(p3, p1, 0x05040100u);
-      v.w = perm_bytes(p3, p1, 0x07060302u);
-      const int row = a_r0 + 32 * i;
-      const int sw = a_ch ^ (row & 7);
-      *reinterpret_cast<uint4*>(a_st + ((size_t)(stage * kGemmBM + row) * 8 + sw) * 8) = v;
-    }
-  };
+  for (int i = 0; i < 8; ++i) {
+    const int lrow = wave * 64 + 8 * i + a_lr;
+    int64_t row = m0 + lrow;
+    row = row < m ? row : m - 1;
+    a_src[i] = x + row * k + (a_p ^ ((lrow >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 8;
+  }
+#define AWQ_GEMM_LOAD_A(KT, STAGE_PTR)                                                  \
+  {                                                                                     \
+    const int64_t kk_ = (int64_t)(KT) * kGemmBK;                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                       \
+      __builtin_amdgcn_global_load_lds(                                                 \
+          (const void*)(a_src[i] + kk_),                                                \
+          (lds_void_t*)((STAGE_PTR) + (wave * 64 + 8 * i) * 64), 16, 0, 0);             \
+  }
 
   // ---- B loader: lane (j = lane % 32, c = lane / 32) of block bn loads words 4c..4c+3
   const int bj = lane & 31, bc = lane >> 5;
-  uint4 wb[2];
-  auto load_b = [&](int kt) {
+  const uint32_t* b_src[2];
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      int64_t col = n0 + wn * 64 + bn * 32 + bj;
-      col = col < n ? col : n - 1;
-      wb[bn] = *reinterpret_cast<const uint4*>(qweight + col * kw_row + (int64_t)kt * 8 + 4 * bc);
-    }
-  };
+  for (int bn = 0; bn < 2; ++bn) {
+    int64_t col = n0 + wn * 64 + bn * 32 + bj;
+    col = col < n ? col : n - 1;
+    b_src[bn] = qweight + col * kw_row + 4 * bc;
+  }
+  uint4 wb0, wb1;
+#define AWQ_GEMM_LOAD_B(KT)                                                        \
+  {                                                                                \
+    wb0 = *reinterpret_cast<const uint4*>(b_src[0] + (int64_t)(KT) * 8);           \
+    wb1 = *reinterpret_cast<const uint4*>(b_src[1] + (int64_t)(KT) * 8);           \
+  }
 
   floatx16_t acc[4][2];
 #pragma unroll
@@ -627,60 +654,68 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = floatx16_t{};
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
+  AWQ_GEMM_LOAD_A(0, a_st0);
+  AWQ_GEMM_LOAD_B(0);
+  __builtin_amdgcn_s_waitcnt(0);       // the direct-to-LDS copies have landed
   __syncthreads();
   const UnpackConsts uc = unpack_consts();
   const int a_row_base = wm * 128 + (lane & 31);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint4 wcur[2] = {wb[0], wb[1]};
-    const int ktn = kt + 1 < nk ? kt + 1 : kt;        // the last step reloads itself (unused)
-    load_a(ktn);
-    load_b(ktn);
-    // dequantize this K-step's weights: bq[bn][s] is the B operand of MFMA step s
-    half8_t bq[2][4];
-    const int grp = (kt * kGemmBK + 32 * bc) / G;
-#pragma unroll
-    for (int bn = 0; bn < 2; ++bn) {
-      const int r = wn * 64 + bn * 32 + bj;
-      const float d = h2f(s_l[r * ng + grp]);
-      const float z = (float)((z_l[r * nzw + (grp >> 3)] >> (4 * (grp & 7))) & 0xFu);
-      const half2_t dd = {(half_t)d, (half_t)d};
-      const half2_t o1024 = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};   // exact
-      const half2_t o64 = {(half_t)(-64.0f - z), (half_t)(-64.0f - z)};
-      const uint32_t ww[4] = {wcur[bn].x, wcur[bn].y, wcur[bn].z, wcur[bn].w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint32_t u[4];
-        unpack_word(ww[s], u, uc);
-        const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024) * dd;
-        const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64) * dd;
-        const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024) * dd;
-        const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64) * dd;
-        bq[bn][s] = __builtin_bit_cast(half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0),
-                                                          __builtin_bit_cast(uint32_t, q1),
-                                                          __builtin_bit_cast(uint32_t, q2),
-                                                          __builtin_bit_cast(uint32_t, q3)));
-      }
-    }
-    const uint16_t* a_stage = a_st + (size_t)(kt & 1) * kGemmBM * 64;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = 4 * bc + s;
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        const int row = a_row_base + bm * 32;
-        const half8_t av = *reinterpret_cast<const half8_t*>(a_stage + ((size_t)row * 8 + (ch ^ (row & 7))) * 8);
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bq[bn][s], acc[bm][bn], 0, 0, 0);
-      }
-    }
-    if (kt + 1 < nk) store_a((kt + 1) & 1);
-    __syncthreads();
+  // One K-step: copy the next step's activations into the other stage and
+  // load its weights, dequantize this step's weights, 32 MFMAs, then wait for
+  // the copies and meet at the barrier.
+#define AWQ_GEMM_STEP(KT, CUR, NXT)                                                     \
+  {                                                                                     \
+    const uint4 wc0 = wb0, wc1 = wb1;                                                   \
+    const int ktn_ = (KT) + 1 < nk ? (KT) + 1 : (KT);                                  \
+    AWQ_GEMM_LOAD_A(ktn_, NXT);                                                         \
+    AWQ_GEMM_LOAD_B(ktn_);                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    half8_t bq[2][4];                                                                   \
+    const int grp = ((KT) * kGemmBK + 32 * bc) / G;                                     \
+    _Pragma("unroll") for (int bn = 0; bn < 2; ++bn) {                                  \
+      const int r = wn * 64 + bn * 32 + bj;                                             \
+      const float d = h2f(s_l[r * ng + grp]);                                           \
+      const float z = (float)((z_l[r * nzw + (grp >> 3)] >> (4 * (grp & 7))) & 0xFu);   \
+      const half2_t dd = {(half_t)d, (half_t)d};                                        \
+      const half2_t o1024 = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};          \
+      const half2_t o64 = {(half_t)(-64.0f - z), (half_t)(-64.0f - z)};                 \
+      const uint4 wv = bn == 0 ? wc0 : wc1;                                             \
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};                                  \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                   \
+        uint32_t u[4];                                                                  \
+        unpack_word(ww[s], u, uc);                                                      \
+        const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024) * dd;            \
+        const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64) * dd;              \
+        const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024) * dd;            \
+        const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64) * dd;              \
+        bq[bn][s] = __builtin_bit_cast(                                                 \
+            half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1), \
+                                __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3))); \
+      }                                                                                 \
+    }                                                                                   \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                     \
+      const int ch = 4 * bc + s;                                                        \
+      _Pragma("unroll") for (int bm = 0; bm < 4; ++bm) {                                \
+        const int row = a_row_base + bm * 32;                                           \
+        const half8_t av = *reinterpret_cast<const half8_t*>(                           \
+            (CUR) + ((size_t)row * 8 + (ch ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7))) * 8);  \
+        _Pragma("unroll") for (int bn = 0; bn < 2; ++bn)                                \
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bq[bn][s], acc[bm][bn], 0, 0, 0); \
+      }                                                                                 \
+    }                                                                                   \
+    __builtin_amdgcn_s_waitcnt(0);                                                      \
+    __syncthreads();                                                                    \
   }
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    AWQ_GEMM_STEP(kt, a_st0, a_st1);
+    AWQ_GEMM_STEP(kt + 1, a_st1, a_st0);
+  }
+  if (kt < nk) AWQ_GEMM_STEP(kt, a_st0, a_st1);
+#undef AWQ_GEMM_STEP
+#undef AWQ_GEMM_LOAD_A
+#undef AWQ_GEMM_LOAD_B
 
   // ---- epilogue: value e of lane l in block (bm, bn) is row 8(e/4) + 4(l/32) + e%4, column l%32
 #pragma unroll
@@ -702,16 +737,22 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
                                   uint16_t* y, void* scratch, hipStream_t stream) {
   if (m > 32) {
     const size_t lds = gemm_lds_bytes(k, G);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-    if (lds > 65536) {
+    const size_t lds_static = (size_t)2 * kGemmBM * kGemmBK * 2;
+    if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
+    if (lds + lds_static > 65536) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<G>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
+    uint16_t* xt = static_cast<uint16_t*>(scratch);
+    const int64_t chunks = m * (k / 8);
+    const int64_t pgrid = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
+    hipLaunchKernelGGL(linear_xprep_kernel, dim3((unsigned)pgrid), dim3(256), 0, stream, x, inv_s16,
+                       m, k, xt);
     const int tiles_m = (int)((m + kGemmBM - 1) / kGemmBM);
     const int tiles_n = (int)((n + kGemmBN - 1) / kGemmBN);
     hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), lds,
-                       stream, x, qweight, scales, qzeros, inv_s16, m, n, k, y, tiles_m, tiles_n);
+                       stream, xt, qweight, scales, qzeros, m, n, k, y, tiles_m, tiles_n);
     return hipGetLastError();
   }
   // the fused decode kernel needs its LDS plan to fit (160 KiB) and one
