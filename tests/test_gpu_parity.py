@@ -305,10 +305,24 @@ def test_linear_deterministic(P):
         assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("n,k,g", [(40, 16384, 32), (24, 28672, 64), (33, 8192, 32)])
+@pytest.mark.parametrize("n,k,g", [(40, 16384, 32), (24, 28672, 64), (33, 8192, 32), (20, 40960, 128)])
 def test_linear_decode_wide_k(P, n, k, g):
-    # long K with small groups: the decode kernel's LDS plan does not fit and the
-    # staged two-kernel path runs at m = 1; other shapes exercise the boundaries
+    # long K with small groups: fewer column blocks per work-group fit the
+    # decode kernel's prologue and LDS plan (down to one at 28672 / 64); at
+    # K = 40960 the activations alone exceed LDS and the staged two-kernel path
+    # runs at m = 1
     w = S.weights(n, k, 0.02, 440 + n)
     x = S.activations(1, k, 441 + n, S.outlier_channels(k, 0.01, 442), 20.0)
     _check_linear(P, w, x, None, g)
+
+
+@pytest.mark.parametrize("n,k,g", [(8261, 256, 64), (40000, 512, 128), (12345, 2048, 32)])
+def test_linear_decode_multiblock(P, n, k, g):
+    # more column blocks than resident work-groups: several blocks per
+    # work-group (up to four), a ragged last block, and (k / g < 8) waves that
+    # own no group and only meet the barriers
+    w = S.weights(n, k, 0.02, 450 + n)
+    x = S.activations(1, k, 451 + n, S.outlier_channels(k, 0.01, 452), 20.0)
+    xc = S.activations(64, k, 453, S.outlier_channels(k, 0.01, 452), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.3)
+    _check_linear(P, w, x, s16, g)

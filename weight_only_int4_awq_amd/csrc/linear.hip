@@ -229,35 +229,68 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
   }
 }
 
+// fp32 accumulate of a two-term fp16 dot product (v_dot2_f32_f16)
+__device__ __forceinline__ float dot2_f16(half2_t a, half2_t b, float c) {
+  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2_t, a), __builtin_bit_cast(fp16x2_t, b), c,
+                                false);
+}
+
+// Sum over aligned groups of N = 4, 8 or 16 lanes, returned in every lane of
+// the group, with DPP lane moves inside a 16-lane row: swap neighbours, swap
+// pairs (quad permutes), then the mirror of each 8-lane half and of the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                   CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float row_group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  v = dpp_add<0xB1>(v);                       // quad_perm [1, 0, 3, 2]
+  v = dpp_add<0x4E>(v);                       // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v = dpp_add<0x141>(v);    // row_half_mirror
+  if constexpr (N >= 16) v = dpp_add<0x140>(v);   // row_mirror
+  return v;
+}
+
 // ---------------------------------------------------------------- decode GEMV (m = 1)
-// Persistent work-groups of 8 waves.  A work-group stages x_tilde once in LDS
-// as the two live rows of the MFMA A operand (row 0 = fp16 hi, row 8 = fp16
-// lo; the other 14 rows read a zero block) together with the per-group offset
-// sums T and U, then walks its 16-column blocks (block b, b + grid, ...).
-// Every wave owns a fixed contiguous range of groups along K; it walks the
-// flattened sequence (block, group) with a double-buffered prefetch of packed
-// weights that runs across block boundaries.  The per-group scales and zero
-// points of a block are staged in LDS one block ahead with 16-byte loads (one
-// per 8 groups of a column), as packed words (fp16 scale | zero << 16) laid
-// out [group][column]: scattered 2- and 4-byte loads of them would cost as
-// many memory requests as the weights themselves.  At the end of a block the
-// waves meet at one barrier; a designated wave sums the 8 partial rows in a
-// fixed order and stores 16 outputs while the others go on.
+// Work-groups of W = 8 or 16 waves (16 where one work-group per CU is all
+// that fits or is needed, so that as many weight bytes are in flight per CU);
+// work-group b owns the 16-column blocks b, b + grid,
+// ... (at most kGemvMaxBlk of them: the grid is sized for that).
+//  * Prologue.  Every load is issued before the first wait, in the order the
+//    data is needed: the scale and zero words of all the work-group's blocks,
+//    the activations (x and inv_s), then the first kGemvPF weight items of
+//    every wave.  The activations are staged in LDS as rows 0 (fp16 hi) and 8
+//    (fp16 lo) of the MFMA A operand (the other 14 rows read a zero block),
+//    with the per-group offset sums T and U; the scales and zero points as
+//    packed words (fp16 scale | zero << 16) laid out [block][group][column].
+//  * Main loop.  Every wave owns a contiguous range of groups along K and walks
+//    the flattened sequence (block, group) with a double-buffered prefetch of
+//    packed weights that runs across block boundaries.  Weight loads are the
+//    only memory instructions in the loop: memory counters retire in order,
+//    and a load or store of anything else there (behind the branch of a block
+//    end) would make the compiler wait for the whole prefetch.
+//  * At the end of a block the waves meet at one barrier and a designated wave
+//    sums the W partial rows in a fixed order into an LDS output row; the
+//    outputs are written after the last block.
 #ifndef AWQ_GEMV_PF
 #define AWQ_GEMV_PF 4
 #endif
-#ifndef AWQ_GEMV_WG_PER_CU
-#define AWQ_GEMV_WG_PER_CU 2
-#endif
-constexpr int kGemvWaves = 8;
 constexpr int kGemvPF = AWQ_GEMV_PF;
 constexpr int kGemvCUs = 256;
+constexpr int kGemvMaxBlk = 4;         // column blocks per work-group
+constexpr int kGemvSzRounds = 4;       // scale/zero octets per thread in the prologue
+constexpr int kGemvXPre = 4;           // activation chunks per thread loaded up front
 
-// LDS: x_tilde [ng][4][2][g/4] halves, T/U [ng] float4, zero block, scale|zero
-// words [2][ng][16], reduction rows [2][8][16] floats.
-size_t gemv_lds_bytes(int64_t k, int32_t g) {
+// LDS: x_tilde [ng][4][2][g/4] halves, T/U [ng] float4, zero block [g/4]
+// halves, scale|zero words [nb][ng][16], reduction rows [2][W][16] floats,
+// outputs [nb][16] floats.
+size_t gemv_lds_bytes(int64_t k, int32_t g, int nb, int waves) {
   const size_t ng = (size_t)(k / g);
-  return (size_t)k * 4 + ng * 16 + (size_t)(g / 4) * 2 + 2 * ng * 16 * 4 + 2 * kGemvWaves * 16 * 4;
+  return (size_t)k * 4 + ng * 16 + (size_t)(g / 4) * 2 + (size_t)nb * ng * 16 * 4 +
+         (size_t)2 * waves * 16 * 4 + (size_t)nb * 16 * 4;
 }
 
 template <int WPL>
@@ -273,81 +306,98 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_gemv_kernel(
+// SZV: the scale rows are 16-byte aligned octets (k / g a multiple of 8 and an
+// aligned base), read with one 16-byte load per octet.
+template <int G, bool SZV, int W>
+__global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, int64_t n, int64_t k, uint16_t* __restrict__ y) {
   constexpr int WPL = G / 32;            // qweight words per lane per group
   constexpr int HPL = G / 4;             // staged halves per (group, lane group, row)
   constexpr int LPG = G / 8;             // words per group
+  constexpr int kGemvWaves = W;
+  constexpr int kGemvThreads = W * 64;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int ng = (int)(k / G);
+  const int nblk = (int)((n + 15) / 16);
+  const int grid = (int)gridDim.x;
+  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // 1 .. kGemvMaxBlk
   unsigned char* sp = smem;
   uint16_t* xa = reinterpret_cast<uint16_t*>(sp);          sp += (size_t)k * 4;     // [ng][4][2][HPL]
   float4* tu = reinterpret_cast<float4*>(sp);              sp += (size_t)ng * 16;   // (T_hi, U_hi, T_lo, U_lo)
   uint16_t* zblk = reinterpret_cast<uint16_t*>(sp);        sp += HPL * 2;           // zeros
-  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);         sp += (size_t)2 * ng * 16 * 4;  // [2][ng][16]
-  float* red = reinterpret_cast<float*>(sp);                                         // [2][8][16]
+  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);         sp += (size_t)my_blocks * ng * 16 * 4;
+  float* red = reinterpret_cast<float*>(sp);               sp += 2 * kGemvWaves * 16 * 4;   // [2][W][16]
+  float* ybuf = reinterpret_cast<float*>(sp);                                        // [nb][16]
 
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave: keep it (and every group index
   // and group base address derived from it) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane >> 4, r = lane & 15;
-  const int nblk = (int)((n + 15) / 16);
-  const int grid = (int)gridDim.x;
-  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // >= 1
   const int jb = ng * wave / kGemvWaves, je = ng * (wave + 1) / kGemvWaves;
   const int cnt = je - jb;                            // groups of this wave per block
   const int total = my_blocks * cnt;                  // (block, group) items of this wave
   const int nzw = (ng + 7) / 8, kw_row = (int)(k / 8);
 
-  // ---- scale / zero staging: thread t < 16 * nzw owns (column t / nzw, octet t % nzw)
-  const bool sz_thread = tid < 16 * nzw;
-  const int sz_row = sz_thread ? tid / nzw : 0;
-  const int sz_oct = sz_thread ? tid % nzw : 0;
-  const bool sz_vec = (ng % 8) == 0;                  // 16-byte aligned octets
-  auto sz_load = [&](int blk, uint4& ss, uint32_t& zz) {   // registers <- global, block blk
-    blk = blk < nblk ? blk : nblk - 1;
-    int col = blk * 16 + sz_row;
-    col = col < (int)n ? col : (int)n - 1;
-    if (sz_thread) {
-      const uint16_t* srow = scales + (int64_t)col * ng + sz_oct * 8;
-      if (sz_vec) {
-        ss = *reinterpret_cast<const uint4*>(srow);
+  // ---- 1. scale and zero words of every block of the work-group.  Octet o
+  // (8 groups of one column) of block slot bs: o = (bs * 16 + row) * nzw + oct.
+  // These loads are lane-predicated; they come first, so that the waits for
+  // the loads after them stay exact.
+  const int n_oct = my_blocks * 16 * nzw;
+  uint4 sz_s[kGemvSzRounds];
+  uint32_t sz_z[kGemvSzRounds];
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    sz_s[i] = make_uint4(0, 0, 0, 0);
+    sz_z[i] = 0;
+    const int o = tid + i * kGemvThreads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      int col = ((int)blockIdx.x + bs * grid) * 16 + row;
+      col = col < (int)n ? col : (int)n - 1;
+      const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
+      if constexpr (SZV) {
+        sz_s[i] = *reinterpret_cast<const uint4*>(srow);
       } else {
         uint16_t h[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = (sz_oct * 8 + i < ng) ? srow[i] : (uint16_t)0;
-        ss = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                        h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+        for (int e = 0; e < 8; ++e) h[e] = (oct * 8 + e < ng) ? srow[e] : (uint16_t)0;
+        sz_s[i] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                             h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
       }
-      zz = qzeros[(int64_t)col * nzw + sz_oct];
+      sz_z[i] = qzeros[(int64_t)col * nzw + oct];
     }
-  };
-  uint4 sz_s = make_uint4(0, 0, 0, 0);                // block staged at the next block end
-  uint32_t sz_z = 0;
-  auto sz_store_regs = [&](int buf, const uint4& ss, uint32_t zz) {   // LDS <- registers
-    if (sz_thread) {
-      const uint32_t sw[4] = {ss.x, ss.y, ss.z, ss.w};
-      const uint32_t sz_zv = zz;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = sz_oct * 8 + i;
-        if (j < ng)
-          szw[((size_t)buf * ng + j) * 16 + sz_row] =
-              ((sw[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu) | (((sz_zv >> (4 * i)) & 0xFu) << 16);
-      }
-    }
-  };
+  }
 
-  // Prefetch slots hold raw loaded bits only (converting at issue time would
-  // make the wave wait there: memory counters retire in order), and every
-  // load is unconditional (the cursor stops on the last item, the column is
-  // clamped), so no branch separates a load from its use and the waits stay
-  // precise.  The (block, group) cursors advance incrementally in scalar
-  // registers: no division per item.
+  // ---- 2. activations: chunk i of thread t is the 8 channels of word
+  // t + 512 i.  Clamped indices: the loads are unconditional.
+  const bool has_inv = inv_s != nullptr;
+  const uint16_t* sbase = has_inv ? inv_s : x;        // any readable row when inv_s is absent
+  uint4 xv[kGemvXPre], sv[kGemvXPre];
+#pragma unroll
+  for (int i = 0; i < kGemvXPre; ++i) { xv[i] = make_uint4(0, 0, 0, 0); sv[i] = xv[i]; }
+  {
+    const int wi = tid < kw_row ? tid : kw_row - 1;
+    xv[0] = *reinterpret_cast<const uint4*>(x + (int64_t)wi * 8);
+    sv[0] = *reinterpret_cast<const uint4*>(sbase + (int64_t)wi * 8);
+  }
+  if (kw_row > kGemvThreads) {                        // uniform
+#pragma unroll
+    for (int i = 1; i < kGemvXPre; ++i) {
+      int wi = tid + i * kGemvThreads;
+      wi = wi < kw_row ? wi : kw_row - 1;
+      xv[i] = *reinterpret_cast<const uint4*>(x + (int64_t)wi * 8);
+      sv[i] = *reinterpret_cast<const uint4*>(sbase + (int64_t)wi * 8);
+    }
+  }
+
+  // ---- 3. first weights.  Prefetch slots hold raw loaded bits only
+  // (converting at issue time would make the wave wait there), every load is
+  // unconditional (the cursor stops on the last item, the column and group are
+  // clamped), and the (block, group) cursors advance in scalar registers.
   uint32_t wq[2 * kGemvPF][WPL];
   const char* qbase = reinterpret_cast<const char*>(qweight);
   int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;    // issue cursor
@@ -355,47 +405,49 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
     int col = i_blk * 16 + r;
     col = col < (int)n ? col : (int)n - 1;
     // 32-bit per-lane byte offset (the packed tensors of one call are below 4 GiB)
-    const uint32_t qoff = ((uint32_t)col * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
-    load_words<WPL>(reinterpret_cast<const uint32_t*>(qbase + (int64_t)i_j * (LPG * 4) + qoff), wq[slot]);
+    uint32_t qoff = ((uint32_t)col * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
+    // opaque to the optimiser: a clamped cursor repeats an address, and the
+    // compiler would otherwise replace that load by a copy of the previous
+    // slot behind a branch and a full wait
+    asm volatile("" : "+v"(qoff));
+    const int jj = i_j < ng ? i_j : ng - 1;
+    load_words<WPL>(reinterpret_cast<const uint32_t*>(qbase + (int64_t)jj * (LPG * 4) + qoff), wq[slot]);
     if (i_left > 1) {
       --i_left;
       if (++i_j == je) { i_j = jb; i_blk += grid; }
     }
   };
-  const bool active = cnt > 0;                        // wave-uniform
-  if (active) {
 #pragma unroll
-    for (int p = 0; p < kGemvPF; ++p) issue(p);
-  }
-  // every prologue load is issued before anything waits on one (memory
-  // counters retire in order): weights, the scales of blocks 0 and 1, then x
-  uint4 sz_s0 = make_uint4(0, 0, 0, 0);
-  uint32_t sz_z0 = 0;
-  sz_load((int)blockIdx.x, sz_s0, sz_z0);             // block 0 of this work-group
-  sz_load((int)blockIdx.x + grid, sz_s, sz_z);        // block 1, stored at the first block end
+  for (int p = 0; p < kGemvPF; ++p) issue(p);         // a wave without groups loads group ng - 1
 
-  // ---- stage x_tilde (hi, lo) and the offset sums in LDS
+  // ---- 4. stage x_tilde (hi, lo) and the offset sums in LDS
   if (tid < HPL / 2) reinterpret_cast<uint32_t*>(zblk)[tid] = 0u;
-  const bool has_inv = inv_s != nullptr;
-  for (int wi = tid; wi < kw_row; wi += kGemvWaves * 64) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + (int64_t)wi * 8);
-    uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-    if (has_inv) sv = *reinterpret_cast<const uint4*>(inv_s + (int64_t)wi * 8);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-    uint16_t hi[8], lo[8];
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  auto stage = [&](int wi, const uint4& xq, const uint4& sq) {
+    const uint4 sv_ = has_inv ? sq : ones;
+    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+    const uint32_t sw[4] = {sv_.x, sv_.y, sv_.z, sv_.w};
+    // hi = fp16_rn(x s) (v_pk_mul_f16) and lo = fp16_rn(x s - hi)
+    // (v_pk_fma_f16): each is one rounding of an exact value, and
+    // x_tilde = hi + lo to about 22 bits.  T and U accumulate in fp32 with
+    // v_dot2 against (1024, 64) and (1, 1): channels 2i and 2i + 1 of a pair
+    // carry the unpack offsets 1024 and 64.
+    const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
+    const half2_t off2 = {(half_t)1024.0f, (half_t)64.0f};
+    uint32_t hw[4], lw[4];
     float th = 0.f, uh = 0.f, tl = 0.f, ul = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float xt = h2f((uint16_t)(xw[e >> 1] >> ((e & 1) * 16))) *
-                       h2f((uint16_t)(sw[e >> 1] >> ((e & 1) * 16)));     // exact
-      hi[e] = f2h_rn(xt);
-      lo[e] = f2h_rn(xt - h2f(hi[e]));
-      const float off = (e & 1) ? 64.0f : 1024.0f;
-      th += off * h2f(hi[e]);
-      uh += h2f(hi[e]);
-      tl += off * h2f(lo[e]);
-      ul += h2f(lo[e]);
+    for (int i = 0; i < 4; ++i) {
+      const half2_t xx = __builtin_bit_cast(half2_t, xw[i]);
+      const half2_t ss = __builtin_bit_cast(half2_t, sw[i]);
+      const half2_t h = xx * ss;
+      const half2_t l = __builtin_elementwise_fma(xx, ss, -h);
+      hw[i] = __builtin_bit_cast(uint32_t, h);
+      lw[i] = __builtin_bit_cast(uint32_t, l);
+      uh = dot2_f16(h, one2, uh);
+      th = dot2_f16(h, off2, th);
+      ul = dot2_f16(l, one2, ul);
+      tl = dot2_f16(l, off2, tl);
     }
     const int j = wi / LPG;
     const int wg = wi % LPG;
@@ -404,20 +456,51 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
     uint16_t* dl = xa + ((j * 4 + cc) * 2 + 1) * HPL + i * 8;
     // slot order (k0, k4, k1, k5, k2, k6, k3, k7) matches unpack_word
     uint4 vh, vl;
-    vh.x = hi[0] | ((uint32_t)hi[4] << 16); vh.y = hi[1] | ((uint32_t)hi[5] << 16);
-    vh.z = hi[2] | ((uint32_t)hi[6] << 16); vh.w = hi[3] | ((uint32_t)hi[7] << 16);
-    vl.x = lo[0] | ((uint32_t)lo[4] << 16); vl.y = lo[1] | ((uint32_t)lo[5] << 16);
-    vl.z = lo[2] | ((uint32_t)lo[6] << 16); vl.w = lo[3] | ((uint32_t)lo[7] << 16);
+    vh.x = __builtin_amdgcn_perm(hw[2], hw[0], 0x05040100u);
+    vh.y = __builtin_amdgcn_perm(hw[2], hw[0], 0x07060302u);
+    vh.z = __builtin_amdgcn_perm(hw[3], hw[1], 0x05040100u);
+    vh.w = __builtin_amdgcn_perm(hw[3], hw[1], 0x07060302u);
+    vl.x = __builtin_amdgcn_perm(lw[2], lw[0], 0x05040100u);
+    vl.y = __builtin_amdgcn_perm(lw[2], lw[0], 0x07060302u);
+    vl.z = __builtin_amdgcn_perm(lw[3], lw[1], 0x05040100u);
+    vl.w = __builtin_amdgcn_perm(lw[3], lw[1], 0x07060302u);
     *reinterpret_cast<uint4*>(dh) = vh;
     *reinterpret_cast<uint4*>(dl) = vl;
-#pragma unroll
-    for (int off = 1; off < LPG; off <<= 1) {
-      th += shfl_xor_f(th, off); uh += shfl_xor_f(uh, off);
-      tl += shfl_xor_f(tl, off); ul += shfl_xor_f(ul, off);
-    }
+    // the LPG words of a group sit in LPG consecutive, aligned lanes, all
+    // active or all inactive together (kw_row and the thread count are
+    // multiples of LPG)
+    th = row_group_sum<LPG>(th); uh = row_group_sum<LPG>(uh);
+    tl = row_group_sum<LPG>(tl); ul = row_group_sum<LPG>(ul);
     if (wg == 0) tu[j] = make_float4(th, uh, tl, ul);
+  };
+#pragma unroll
+  for (int i = 0; i < kGemvXPre; ++i) {
+    const int wi = tid + i * kGemvThreads;
+    if (wi < kw_row) stage(wi, xv[i], sv[i]);
   }
-  sz_store_regs(0, sz_s0, sz_z0);
+  for (int wi = tid + kGemvXPre * kGemvThreads; wi < kw_row; wi += kGemvThreads) {
+    const uint4 xq = *reinterpret_cast<const uint4*>(x + (int64_t)wi * 8);
+    const uint4 sq = *reinterpret_cast<const uint4*>(sbase + (int64_t)wi * 8);
+    stage(wi, xq, sq);
+  }
+
+  // ---- 5. scale|zero words into LDS
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    const int o = tid + i * kGemvThreads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      const uint32_t sw[4] = {sz_s[i].x, sz_s[i].y, sz_s[i].z, sz_s[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = oct * 8 + e;
+        if (j < ng)
+          szw[((size_t)bs * ng + j) * 16 + row] =
+              ((sw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) | (((sz_z[i] >> (4 * e)) & 0xFu) << 16);
+      }
+    }
+  }
   __syncthreads();
 
   // rows 0 (hi) and 8 (lo) of the A operand are live; the others read zeros
@@ -432,10 +515,9 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
   float yacc = 0.0f;
   int blocks_done = 0;
 
-  // end of a column block: stage the scales of the block after next, combine
-  // hi + lo rows, meet the other waves, reduce
-  auto finish_block = [&](int blk) {
-    sz_store_regs((blocks_done + 1) & 1, sz_s, sz_z);
+  // end of a column block: combine the hi + lo rows, meet the other waves,
+  // reduce into the output row of the block (LDS only)
+  auto finish_block = [&]() {
     const float other = __shfl_xor(yacc, 32, 64);
     float* rb = red + (blocks_done & 1) * (kGemvWaves * 16);
     if (lane < 16) rb[wave * 16 + lane] = yacc + other;
@@ -445,13 +527,11 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
       float sum = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < kGemvWaves; ++wv) sum += rb[wv * 16 + lane];
-      const int64_t col = (int64_t)blk * 16 + lane;
-      if (col < n) y[col] = f2h_rn(sum);
+      ybuf[blocks_done * 16 + lane] = sum;
     }
     ++blocks_done;
-    sz_load(blk + 2 * grid, sz_s, sz_z);
   };
-  int c_blk = (int)blockIdx.x, c_j = jb, c_left = total;    // consume cursor
+  int c_j = jb, c_left = total;                       // consume cursor
   auto consume = [&](int p) {
     if (c_left > 0) {                                 // wave-uniform
       const int j = c_j;
@@ -460,7 +540,7 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
 #pragma unroll
       for (int i = 0; i < WPL; ++i) aop[i] = *reinterpret_cast<const half8_t*>(asrc + 16 * i);
       const float2 tv = *reinterpret_cast<const float2*>(tu_lane + (uint32_t)j * 16);
-      const uint32_t szv = szw[((blocks_done & 1) * ng + j) * 16 + r];
+      const uint32_t szv = szw[((size_t)blocks_done * ng + j) * 16 + r];
       floatx4_t cacc = floatx4_t{};
 #pragma unroll
       for (int i = 0; i < WPL; ++i) {
@@ -474,26 +554,52 @@ __global__ __launch_bounds__(kGemvWaves * 64, AWQ_GEMV_WG_PER_CU) void linear_ge
       yacc = __builtin_fmaf(h2f((uint16_t)szv), __builtin_fmaf(-zf, tv.y, cacc[0] - tv.x), yacc);
       --c_left;
       if (++c_j == je) {
-        finish_block(c_blk);
+        finish_block();
         c_j = jb;
-        c_blk += grid;
       }
     }
   };
-  if (active) {
-    for (int s0 = 0; s0 < total; s0 += 2 * kGemvPF) {
+  if (cnt > 0) {
+    // Half A (slots 0..PF-1) is in flight on entry.  The next half is issued
+    // only while items remain beyond the current one, so no load outlives the
+    // last item; the branches are wave-uniform and each path has a fixed
+    // number of loads in flight at every wait.
+    int left = total;
+    while (true) {
+      if (left > kGemvPF) {
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p);
+        for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p);
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) consume(p);
+        for (int p = 0; p < kGemvPF; ++p) consume(p);
+        left -= kGemvPF;
+      } else {
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) issue(p);
+        for (int p = 0; p < kGemvPF; ++p) consume(p);
+        break;
+      }
+      if (left > kGemvPF) {
 #pragma unroll
-      for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p);
+        for (int p = 0; p < kGemvPF; ++p) issue(p);
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p);
+        left -= kGemvPF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p);
+        break;
+      }
     }
   } else {
-    // a wave without groups (fewer than 8 groups in k) still meets every block's barrier
-    for (int bi = 0; bi < my_blocks; ++bi) finish_block((int)blockIdx.x + bi * grid);
+    // a wave without groups (fewer than W groups in k) still meets every block's barrier
+    for (int bi = 0; bi < my_blocks; ++bi) finish_block();
+  }
+
+  // ---- outputs: the reducer wave wrote every row of ybuf itself
+  if (wave == reducer && lane < 16) {
+    for (int bi = 0; bi < my_blocks; ++bi) {
+      const int64_t col = ((int64_t)blockIdx.x + (int64_t)bi * grid) * 16 + lane;
+      if (col < n) y[col] = f2h_rn(ybuf[bi * 16 + lane]);
+    }
   }
 }
 
@@ -755,28 +861,70 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
                        stream, xt, qweight, scales, qzeros, m, n, k, y, tiles_m, tiles_n);
     return hipGetLastError();
   }
-  // the fused decode kernel needs its LDS plan to fit (160 KiB) and one
-  // scale/zero octet per thread (16 columns x ceil(ng/8) octets <= 512);
-  // other shapes take the staged two-kernel path below
-  const int64_t ng_all = k / G;
-  if (m == 1 && gemv_lds_bytes(k, G) <= 160 * 1024 && 16 * ((ng_all + 7) / 8) <= kGemvWaves * 64) {
-    const size_t lds = gemv_lds_bytes(k, G);
-    const void* fn = reinterpret_cast<const void*>(&linear_gemv_kernel<G>);
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
+  // the fused decode kernel: at most kGemvMaxBlk column blocks per
+  // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
+  // thread) and whose LDS plan fits 160 KiB; other shapes take the staged
+  // two-kernel path below
+  if (m == 1) {
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
     const int64_t nblk = (n + 15) / 16;
-    // work-groups resident at once: bounded by the launch bound and by LDS
-    int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)lds;
-    per_cu = per_cu < AWQ_GEMV_WG_PER_CU ? per_cu : AWQ_GEMV_WG_PER_CU;
-    per_cu = per_cu > 0 ? per_cu : 1;
-    const int64_t slots = (int64_t)kGemvCUs * per_cu;
-    // as many work-groups as fit at once; blocks go round-robin
-    const int64_t grid = nblk < slots ? nblk : slots;
-    hipLaunchKernelGGL((linear_gemv_kernel<G>), dim3((unsigned)grid), dim3(kGemvWaves * 64), lds,
-                       stream, x, inv_s16, qweight, scales, qzeros, n, k, y);
-    return hipGetLastError();
+    auto plan = [&](int waves, int& nb_cap, int64_t& per_cu) {
+      nb_cap = kGemvMaxBlk;
+      while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * waves * 64 ||
+                            gemv_lds_bytes(k, G, nb_cap, waves) > 160 * 1024))
+        --nb_cap;
+      per_cu = nb_cap > 0 ? (int64_t)(160 * 1024) / (int64_t)gemv_lds_bytes(k, G, nb_cap, waves) : 0;
+      const int64_t wg_cap = 16 / waves;            // 16 waves per CU (4 per SIMD)
+      per_cu = per_cu < wg_cap ? per_cu : wg_cap;
+    };
+    int nb_cap = 0;
+    int64_t per_cu = 0;
+    plan(8, nb_cap, per_cu);
+    int waves = 8;
+    // LDS leaves room for one 8-wave work-group per CU: 16 waves put twice
+    // the weight bytes in flight
+    if (nb_cap > 0 && per_cu < 2) {
+      int nb16 = 0;
+      int64_t pc16 = 0;
+      plan(16, nb16, pc16);
+      if (nb16 > 0 && pc16 >= 1) { waves = 16; nb_cap = nb16; per_cu = pc16; }
+    }
+    if (nb_cap > 0 && per_cu >= 1) {
+      const int64_t slots = (int64_t)kGemvCUs * per_cu;
+      // fill the chip first, then give each work-group up to nb_cap blocks
+      int64_t grid = nblk < slots ? nblk : slots;
+      const int64_t need = (nblk + nb_cap - 1) / nb_cap;
+      grid = grid > need ? grid : need;
+      const int nb = (int)((nblk + grid - 1) / grid);
+      const size_t lds = gemv_lds_bytes(k, G, nb, waves);
+      const bool szv = (ng_all % 8 == 0) && (reinterpret_cast<uintptr_t>(scales) % 16 == 0);
+      const void* fn =
+          waves == 16 ? (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 16>)
+                             : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 16>))
+                      : (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 8>)
+                             : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 8>));
+      if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      const dim3 gd((unsigned)grid), bd((unsigned)(waves * 64));
+      if (waves == 16) {
+        if (szv)
+          hipLaunchKernelGGL((linear_gemv_kernel<G, true, 16>), gd, bd, lds, stream, x, inv_s16,
+                             qweight, scales, qzeros, n, k, y);
+        else
+          hipLaunchKernelGGL((linear_gemv_kernel<G, false, 16>), gd, bd, lds, stream, x, inv_s16,
+                             qweight, scales, qzeros, n, k, y);
+      } else {
+        if (szv)
+          hipLaunchKernelGGL((linear_gemv_kernel<G, true, 8>), gd, bd, lds, stream, x, inv_s16,
+                             qweight, scales, qzeros, n, k, y);
+        else
+          hipLaunchKernelGGL((linear_gemv_kernel<G, false, 8>), gd, bd, lds, stream, x, inv_s16,
+                             qweight, scales, qzeros, n, k, y);
+      }
+      return hipGetLastError();
+    }
   }
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / G;
