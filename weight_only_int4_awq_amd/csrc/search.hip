@@ -2,23 +2,26 @@
 // 二.1 (3): scale the salient input channels of W by s, divide the activation
 // by s, choose s to minimise the output error of the quantized layer).
 //
-// Three kernels, all on the caller's stream:
+// Four kernels, all on the caller's stream:
 //  1. search_prep: s_ik = fp16_rn(max(a_k^alpha_i, 2^-14)) and 1/s_ik (fp32)
 //     for every grid point and channel (float64 pow, single fp16 rounding).
-//  2. search_blockscale: a power-of-two factor per 32-row block that keeps the
+//  2. search_blockscale: a power-of-two factor per 64-row block that keeps the
 //     fp16 split of the weight error in the normal range (see below).
-//  3. search_loss: one work-group per (32-row block, alpha).  For every group
-//     of g channels it fake-quantizes the 32 x g block of W' = fp16(W s_i)
+//  3. search_loss: one work-group per (64-row block, alpha).  For every group
+//     of g channels it fake-quantizes the 64 x g block of W' = fp16(W s_i)
 //     (exact per-element codes, see awq_common.h), forms the weight error
 //     dW = ((q - z) D - W s) / s in fp32 (no cancellation: both terms of the
-//     difference are exact), splits it into fp16 hi + lo, stages both
-//     in LDS in the MFMA A-operand layout and multiplies them with the
-//     calibration tokens (B operand, straight from global memory) into fp32
+//     difference are exact), splits it into fp16 hi + lo, stages both in LDS
+//     in the MFMA A-operand layout and multiplies them with the calibration
+//     tokens (B operand, from global memory one step ahead) into fp32
 //     accumulators E = dW X^T.  After the last group it squares E in float64
 //     and writes the block's partial loss.
 //  4. search_select: sums the partials of each alpha in block order (fixed),
 //     takes the first minimum over finite losses and writes s16 and
 //     inv_s16 = fp16_rn(1/s16) (float64 quotient).
+// A non-finite W' (W s overflowing fp16, or a NaN scale) makes its group's
+// step D non-finite or its own error NaN; either reaches E through the MFMAs,
+// so that alpha's loss is not finite and it is never chosen.
 #include <math.h>
 
 #include "awq_common.h"
@@ -26,8 +29,7 @@
 
 namespace awq {
 
-constexpr int kSearchRows = 32;        // rows of W per work-group
-constexpr int kSearchTokPass = 512;    // tokens per pass (4 waves x 4 tiles x 32)
+constexpr int kSearchRows = 64;        // rows of W per work-group
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void search_prep_kernel(const double* __restri
   rs[(int64_t)i * k + col] = 1.0f / h2f(sb);
 }
 
-// Per 32-row block: a power-of-two factor c for the weight error dW.  Every
+// Per 64-row block: a power-of-two factor c for the weight error dW.  Every
 // |dW_nk| is at most about 1.03 |W_nk| (an element on quantization level 0 has
 // dW = -W; on any other level |W'| >= D/2, so |deq - W'| <= 0.51 D <= 1.02 |W'|).
 // With max|W| < 2^e the factor c = 2^(14 - e) keeps c |dW| below 17000, inside
@@ -109,16 +111,80 @@ __global__ __launch_bounds__(256) void search_blockscale_kernel(const uint16_t* 
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void search_loss_kernel(
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i
+// writes LDS bytes lds_base + 16 i .. +15.  Issued from inline asm so that the
+// compiler, which would otherwise drain every outstanding copy before any read
+// of the destination array, leaves the waits to the caller: the destination
+// must not be read before an explicit s_waitcnt vmcnt that covers the copy,
+// and every copy must have landed before the wave ends.  No output register.
+// M0 is reserved for the compiler, which uses it only to address LDS copies
+// of its own; none is live across this statement in the kernels below.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* gsrc, uint32_t lds_base) {
+  // one wait state between the M0 write and the copy that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt on the vector memory counter only, as inline asm: the compiler
+// does not see the copies above and would drop a wait it thinks is idle.  The
+// memory clobber keeps the LDS reads that follow below it.
+#define AWQ_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory")
+
+// Lane moves inside aligned groups of 4 lanes (DPP quad permutes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+// Work-group: 64 rows of W (two 32-row MFMA blocks) x one alpha x all tokens
+// in passes of 128 NT, as 8 waves in two roles that run concurrently on each
+// SIMD, one group of g channels apart:
+//  * producer waves 4..7 (stage 1): thread (row t/4, quarter t%4) fake-
+//    quantizes g/4 elements of group i: W' = fp16(W s) two at a time
+//    (v_pk_mul_f16), the group max/min two at a time and across the quad
+//    (DPP), then per element the exact code, deq = (q - z) D, the scaled error
+//    dW c = (deq - W s)(c/s) and its fp16 split hi = rtz(dW c),
+//    lo = rtz(dW c - hi) (v_cvt_pkrtz, two at a time), stored in LDS buffer
+//    i % 2 in the MFMA A layout with 16-byte stores.  The next group's
+//    weights, scales and scaled reciprocals load meanwhile.
+//  * consumer waves 0..3 (stage 2): E += dW_hi X^T + dW_lo X^T for group
+//    i - 1 from the other buffer; wave w owns the token tiles w, w + 4, ... of
+//    the pass and both row blocks, so each activation fragment feeds four
+//    MFMAs.  A wave copies its own activation fragments straight into a
+//    private 4-slot LDS ring (global_load_lds, 16 bytes per lane, read back
+//    by the same lane), three 16-channel steps ahead of the MFMAs.
+//  * dW sits in LDS as [step][k half][row][8 halves]: the 32 lanes that read
+//    one k half of an A fragment read 512 contiguous bytes (no bank
+//    conflicts).
+// One barrier per group separates the roles.  Every load is unconditional
+// (indices clamped), so the waits stay exact.  After the last group of a pass
+// the consumers square E in float64 over the valid tokens; fixed-order
+// reductions give one partial loss per (alpha, block).
+template <int G, int NT>
+__global__ __launch_bounds__(512, 1) void search_loss_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ x, int64_t n, int64_t k,
     int64_t m, int32_t n_grid, int64_t n_blocks, const uint16_t* __restrict__ s16_all,
     const float* __restrict__ rs_all, const float* __restrict__ cblk, double* __restrict__ part) {
-  constexpr int EPT = G / 8;          // elements of one row-group per thread
-  constexpr int KSTEPS = G / 16;      // MFMA k-steps per group
-  __shared__ __attribute__((aligned(16))) uint16_t a_hi[KSTEPS * 32 * 16];
-  __shared__ __attribute__((aligned(16))) uint16_t a_lo[KSTEPS * 32 * 16];
+  constexpr int EPT = G / 4;          // elements of one row-group per producer thread
+  constexpr int KSTEPS = G / 16;      // MFMA k-steps per group (even)
+  constexpr int TOK = 128 * NT;       // tokens per pass
+  constexpr int WLD = EPT / 8;        // 16-byte weight loads per producer thread per group
+  constexpr int DWN = KSTEPS * kSearchRows * 16;   // halves per dW buffer
+  __shared__ __attribute__((aligned(16))) uint16_t dh0[DWN];
+  __shared__ __attribute__((aligned(16))) uint16_t dl0[DWN];
+  __shared__ __attribute__((aligned(16))) uint16_t dh1[DWN];
+  __shared__ __attribute__((aligned(16))) uint16_t dl1[DWN];
+  __shared__ __attribute__((aligned(16))) uint16_t s_l[2][G];     // candidate scales
+  __shared__ __attribute__((aligned(16))) float rc_l[2][G];       // c / s
   __shared__ double red[4];
+  // activation ring: [slot][wave][tile][lane][8 halves]
+  constexpr int XSN = 4 * NT * 64 * 8;
+  __shared__ __attribute__((aligned(16))) uint16_t xring[4 * XSN];
 
   // XCD-aware order: consecutive logical ids (the alphas of one row block)
   // land on the same XCD, so they share W through that XCD's L2.
@@ -135,123 +201,234 @@ __global__ __launch_bounds__(256) void search_loss_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r = tid >> 3;             // row of the block this thread quantizes
-  const int sub = tid & 7;            // which EPT-slice of the group
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool consumer = wave < 4;     // wave-uniform role
+  const float cscale = cblk[rb];
+  const int ng = (int)(k / G);
+
+  // ---- producer state
+  const int ptid = tid & 255;
+  const int r = ptid >> 2;            // row of the block this thread quantizes
+  const int sub = ptid & 3;           // which quarter of the group
   const int64_t row = rb * kSearchRows + r;
   const bool row_ok = row < n;
-  const float cscale = cblk[rb];
+  const uint32_t row_mask = row_ok ? 0xFFFFFFFFu : 0u;    // rows past n contribute zero errors
+  const uint16_t* wrow = w + (row_ok ? row : n - 1) * k + sub * EPT;
+  // scale / reciprocal staging: producer thread t loads halves 8 (t % (G/8))
+  // of the scales and floats 4 (t % (G/4)) of the reciprocals (clamped: every
+  // producer loads, the first G/8 resp. G/4 store)
+  const int s_i = ptid % (G / 8), r_i = ptid % (G / 4);
+  uint4 wa[WLD], wb[WLD];             // weights of the current / next group
+  uint4 sn;                           // scales / reciprocals of the next group:
+  float4 rn;                          // loaded at the top of an iteration, stored to LDS at its end
+  auto store_sr = [&](int buf, const uint4& sv, const float4& rv) {
+    if (ptid < G / 8) *reinterpret_cast<uint4*>(&s_l[buf][8 * s_i]) = sv;
+    if (ptid < G / 4)
+      *reinterpret_cast<float4*>(&rc_l[buf][4 * r_i]) =
+          make_float4(rv.x * cscale, rv.y * cscale, rv.z * cscale, rv.w * cscale);
+  };
+#define AWQ_LOAD_W(WV, J)                                                                   \
+  {                                                                                         \
+    _Pragma("unroll") for (int q_ = 0; q_ < WLD; ++q_)                                      \
+      WV[q_] = *reinterpret_cast<const uint4*>(wrow + (int64_t)(J) * G + 8 * q_);          \
+  }
+#define AWQ_LOAD_SR(SV, RV, J)                                                              \
+  {                                                                                         \
+    SV = *reinterpret_cast<const uint4*>(s16 + (int64_t)(J) * G + 8 * s_i);                \
+    RV = *reinterpret_cast<const float4*>(rs + (int64_t)(J) * G + 4 * r_i);                \
+  }
+  // With four token tiles per consumer wave the accumulators leave no room
+  // for a second weight buffer: the next group's weights are then loaded right
+  // after stage 1 (still under the consumers' MFMAs) into the same registers.
+  constexpr bool kWDouble = NT < 4;
+
+  // stage 1 for one group: weights in WV, scales / reciprocals in LDS buffer
+  // SB, errors into LDS buffers DH / DL
+#define AWQ_PRODUCE(WV, SB, DH, DL)                                                         \
+  {                                                                                         \
+    half2_t pmx = {(half_t)-__builtin_inff(), (half_t)-__builtin_inff()};                   \
+    half2_t pmn = {(half_t)__builtin_inff(), (half_t)__builtin_inff()};                     \
+    _Pragma("unroll") for (int q = 0; q < WLD; ++q) {                                       \
+      const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * EPT + 8 * q]);        \
+      const uint32_t wq4[4] = {WV[q].x, WV[q].y, WV[q].z, WV[q].w};                         \
+      const uint32_t sq4[4] = {sv.x, sv.y, sv.z, sv.w};                                     \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
+        const half2_t wp = __builtin_bit_cast(half2_t, wq4[i]) * __builtin_bit_cast(half2_t, sq4[i]); \
+        pmx = __builtin_elementwise_max(pmx, wp);                                           \
+        pmn = __builtin_elementwise_min(pmn, wp);                                           \
+      }                                                                                     \
+    }                                                                                       \
+    float mx = __builtin_fmaxf((float)pmx.x, (float)pmx.y);                                 \
+    float mn = __builtin_fminf((float)pmn.x, (float)pmn.y);                                 \
+    mx = __builtin_fmaxf(mx, dpp_mov<0xB1>(mx));                                            \
+    mn = __builtin_fminf(mn, dpp_mov<0xB1>(mn));                                            \
+    mx = __builtin_fmaxf(mx, dpp_mov<0x4E>(mx));                                            \
+    mn = __builtin_fminf(mn, dpp_mov<0x4E>(mn));                                            \
+    const GroupQ gq = group_q(mx, mn);                                                      \
+    _Pragma("unroll") for (int q = 0; q < WLD; ++q) {                                       \
+      __builtin_amdgcn_sched_barrier(0);                                                    \
+      const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * EPT + 8 * q]);        \
+      const float4 rc0 = *reinterpret_cast<const float4*>(&rc_l[SB][sub * EPT + 8 * q]);    \
+      const float4 rc1 = *reinterpret_cast<const float4*>(&rc_l[SB][sub * EPT + 8 * q + 4]); \
+      const uint32_t wq4[4] = {WV[q].x, WV[q].y, WV[q].z, WV[q].w};                         \
+      const uint32_t sq4[4] = {sv.x, sv.y, sv.z, sv.w};                                     \
+      const float rcv[8] = {rc0.x, rc0.y, rc0.z, rc0.w, rc1.x, rc1.y, rc1.z, rc1.w};        \
+      uint32_t hw[4], lw[4];                                                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
+        const half2_t wv = __builtin_bit_cast(half2_t, wq4[i]);                             \
+        const half2_t sv2 = __builtin_bit_cast(half2_t, sq4[i]);                            \
+        const half2_t wp = wv * sv2;                                                        \
+        float dw[2];                                                                        \
+        _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                     \
+          const float deq = code_minus_zero((float)wp[e], gq) * gq.d;                       \
+          const float wsx = __builtin_fmaf((float)wv[e], (float)sv2[e], 0.0f);              \
+          dw[e] = __builtin_bit_cast(                                                       \
+              float, __builtin_bit_cast(uint32_t, (deq - wsx) * rcv[2 * i + e]) & row_mask);   \
+        }                                                                                   \
+        const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(dw[0], dw[1])); \
+        const half2_t lo = __builtin_bit_cast(                                              \
+            half2_t, __builtin_amdgcn_cvt_pkrtz(dw[0] - (float)hi[0], dw[1] - (float)hi[1])); \
+        hw[i] = __builtin_bit_cast(uint32_t, hi);                                           \
+        lw[i] = __builtin_bit_cast(uint32_t, lo);                                           \
+      }                                                                                     \
+      const int kloc = sub * EPT + 8 * q;                                                   \
+      const int off = ((kloc / 8) * kSearchRows + r) * 8;   /* [step][half][row][8] */     \
+      *reinterpret_cast<uint4*>(&DH[off]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);         \
+      *reinterpret_cast<uint4*>(&DL[off]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);         \
+    }                                                                                       \
+  }
+
+  // ---- consumer state
+  floatx16_t acc[2][NT];
+  uint32_t xoff[NT];                  // byte offsets of this lane's fragment rows (m k < 2^31)
+  const char* xbytes = reinterpret_cast<const char*>(x);
+  // LDS byte address of this wave's part of ring slot 0
+  const uint32_t xring_wave =
+      (uint32_t)(uintptr_t)(&xring[0]) + (uint32_t)(wave * NT * 64 * 16);
+  // copy step T of the pass (group T / KSTEPS, step T % KSTEPS; groups past
+  // the last are clamped) into ring slot T % 4
+#define AWQ_LOAD_X(T)                                                                       \
+  {                                                                                         \
+    int jj_ = (T) / KSTEPS;                                                                 \
+    jj_ = jj_ < ng ? jj_ : ng - 1;                                                          \
+    const char* xs_ = xbytes + ((int64_t)jj_ * G + 16 * ((T) % KSTEPS)) * 2;                \
+    const uint32_t slot_ = xring_wave + (uint32_t)(((T) % 4) * XSN * 2);                    \
+    _Pragma("unroll") for (int ti_ = 0; ti_ < NT; ++ti_)                                    \
+      lds_copy16(xs_ + xoff[ti_], slot_ + (uint32_t)(ti_ * 64 * 16));                      \
+  }
+  // stage 2 for group J from LDS buffers DH / DL; the last step loads the
+  // first fragments of group JN (KSTEPS is even: they land in buffer 0)
+#define AWQ_CONSUME(J, DH, DL)                                                              \
+  {                                                                                         \
+    _Pragma("unroll") for (int s = 0; s < KSTEPS; ++s) {                                    \
+      /* pass step t = J KSTEPS + s: copy step t + 3, then wait for step t's copies */      \
+      const int t_ = (J) * KSTEPS + s;                                                      \
+      AWQ_LOAD_X(t_ + 3)                                                                    \
+      AWQ_WAIT_VMCNT(3 * NT);                                                               \
+      const uint16_t* xsl_ = xring + (t_ % 4) * XSN;                                        \
+      const int aoff0 = ((s * 2 + (lane >> 5)) * kSearchRows + (lane & 31)) * 8;            \
+      const int aoff1 = aoff0 + 32 * 8;                                                     \
+      const half8_t ah0 = *reinterpret_cast<const half8_t*>(&DH[aoff0]);                    \
+      const half8_t al0 = *reinterpret_cast<const half8_t*>(&DL[aoff0]);                    \
+      const half8_t ah1 = *reinterpret_cast<const half8_t*>(&DH[aoff1]);                    \
+      const half8_t al1 = *reinterpret_cast<const half8_t*>(&DL[aoff1]);                    \
+      _Pragma("unroll") for (int ti = 0; ti < NT; ++ti) {                                   \
+        const half8_t b = *reinterpret_cast<const half8_t*>(                                \
+            xsl_ + ((wave * NT + ti) * 64 + lane) * 8);                                     \
+        acc[0][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah0, b, acc[0][ti], 0, 0, 0);   \
+        acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah1, b, acc[1][ti], 0, 0, 0);   \
+        acc[0][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al0, b, acc[0][ti], 0, 0, 0);   \
+        acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al1, b, acc[1][ti], 0, 0, 0);   \
+      }                                                                                     \
+    }                                                                                       \
+  }
+
+  // iteration I: producers quantize group I (weights CUR, scales buffer I%2,
+  // errors into dW buffer I%2) and load group I+1 into NXT; consumers multiply
+  // group I-1 from the other dW buffer.  PB is I%2, known statically.
+#define AWQ_STEP(I, PB, WCUR, WNXT, DHP, DLP, DHC, DLC)                                      \
+  {                                                                                         \
+    if (consumer) {                                                                         \
+      if ((I) >= 1) {                                                                       \
+        const int jc_ = (I) - 1;                                                            \
+        AWQ_CONSUME(jc_, DHC, DLC)                                                          \
+      }                                                                                     \
+    } else if ((I) < ng) {                                                                  \
+      const int jn_ = (I) + 1 < ng ? (I) + 1 : ng - 1;                                      \
+      AWQ_LOAD_SR(sn, rn, jn_)                                                              \
+      if constexpr (kWDouble) AWQ_LOAD_W(WNXT, jn_)                                         \
+      AWQ_PRODUCE(WCUR, PB, DHP, DLP)                                                       \
+      if constexpr (!kWDouble) AWQ_LOAD_W(WCUR, jn_)                                        \
+      store_sr((PB) ^ 1, sn, rn);                                                           \
+    }                                                                                       \
+    __syncthreads();                                                                        \
+  }
 
   double loss = 0.0;
-  for (int64_t t0 = 0; t0 < m; t0 += kSearchTokPass) {
-    const int64_t tpass = (m - t0) < kSearchTokPass ? (m - t0) : kSearchTokPass;
-    const int ntiles = (int)((tpass + 31) / 32);
-    floatx16_t acc[4];
+  for (int64_t t0 = 0; t0 < m; t0 += TOK) {
+    if (consumer) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = floatx16_t{};
-
-    for (int64_t j = 0; j < k / G; ++j) {
-      // ---- stage 1: fake-quantize this thread's EPT elements, stage dW in LDS
-      const int64_t kb = j * G + sub * EPT;
-      float wsx[EPT], wp[EPT], rsv[EPT];
-      float mx = -__builtin_inff(), mn = __builtin_inff();
-      int bad = 0;
-      if (row_ok) {
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-          uint2 wr = *reinterpret_cast<const uint2*>(w + row * k + kb + e);
-          uint2 sr = *reinterpret_cast<const uint2*>(s16 + kb + e);
-          float4 rr = *reinterpret_cast<const float4*>(rs + kb + e);
-          uint32_t ww[2] = {wr.x, wr.y};
-          uint32_t ss[2] = {sr.x, sr.y};
-          float rq[4] = {rr.x, rr.y, rr.z, rr.w};
+        for (int i = 0; i < NT; ++i) acc[b][i] = floatx16_t{};
+      // activation fragment rows of this wave's tiles (clamped tokens; tokens
+      // past m are left out of the squares)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint16_t wb = (uint16_t)(ww[i >> 1] >> ((i & 1) * 16));
-            uint16_t sb = (uint16_t)(ss[i >> 1] >> ((i & 1) * 16));
-            const float prod = h2f(wb) * h2f(sb);      // W s, exact in fp32
-            uint16_t pb = f2h_rn(prod);
-            bad |= f16_nonfinite(pb) ? 1 : 0;
-            wsx[e + i] = prod;
-            wp[e + i] = h2f(pb);
-            rsv[e + i] = rq[i];
-            mx = __builtin_fmaxf(mx, wp[e + i]);
-            mn = __builtin_fminf(mn, wp[e + i]);
-          }
-        }
+      for (int ti = 0; ti < NT; ++ti) {
+        int64_t tok = t0 + (int64_t)(wave + 4 * ti) * 32 + (lane & 31);
+        tok = tok < m ? tok : m - 1;
+        xoff[ti] = (uint32_t)((tok * k + 8 * (lane >> 5)) * 2);
       }
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        mx = __builtin_fmaxf(mx, shfl_xor_f(mx, off));
-        mn = __builtin_fminf(mn, shfl_xor_f(mn, off));
-        bad |= __shfl_xor(bad, off, 64);
-      }
-      uint16_t hi[EPT], lo[EPT];
-      if (row_ok) {
-        GroupQ gq = group_q(mx, mn);
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          // dW = (deq - W s) / s: deq and W s are exact, so the small difference is
-          // rounded once, then scaled by the block factor c (a power of two)
-          float deq = code_minus_zero(wp[e], gq) * gq.d;          // exact
-          float dw = bad ? __builtin_nanf("") : (deq - wsx[e]) * (rsv[e] * cscale);
-          uint16_t h = f2h_rn(dw);
-          hi[e] = h;
-          lo[e] = f2h_rn(dw - h2f(h));
-        }
+      AWQ_LOAD_X(0)
+      AWQ_LOAD_X(1)
+      AWQ_LOAD_X(2)
+    } else {
+      AWQ_LOAD_W(wa, 0)
+      AWQ_LOAD_SR(sn, rn, 0)
+      store_sr(0, sn, rn);
+    }
+    __syncthreads();
+    for (int i = 0; i <= ng; i += 2) {
+      if constexpr (kWDouble) {
+        AWQ_STEP(i, 0, wa, wb, dh0, dl0, dh1, dl1)
+        if (i + 1 <= ng) AWQ_STEP(i + 1, 1, wb, wa, dh1, dl1, dh0, dl0)
       } else {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) { hi[e] = 0; lo[e] = 0; }
-      }
-      {
-        const int kloc = sub * EPT;
-        const int s = kloc / 16, kk = kloc % 16;
-        const int base = (s * 32 + r) * 16 + kk;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          a_hi[base + e] = hi[e];
-          a_lo[base + e] = lo[e];
-        }
-      }
-      __syncthreads();
-      // ---- stage 2: E += dW_hi X^T + dW_lo X^T on the matrix cores
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int aoff = (s * 32 + (lane & 31)) * 16 + (lane >> 5) * 8;
-        half8_t ah = *reinterpret_cast<const half8_t*>(&a_hi[aoff]);
-        half8_t al = *reinterpret_cast<const half8_t*>(&a_lo[aoff]);
-        const int64_t kx = j * G + s * 16 + (lane >> 5) * 8;
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const int tile = wave + 4 * ti;
-          if (tile < ntiles) {
-            const int64_t tok = t0 + tile * 32 + (lane & 31);
-            half8_t b = half8_t{};
-            if (tok < m) b = *reinterpret_cast<const half8_t*>(x + tok * k + kx);
-            acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, b, acc[ti], 0, 0, 0);
-            acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, b, acc[ti], 0, 0, 0);
-          }
-        }
-      }
-      __syncthreads();
-    }
-    // ---- square and reduce (float64, fixed order)
-    double sq = 0.0;
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        double e = (double)acc[ti][i];
-        sq += e * e;
+        AWQ_STEP(i, 0, wa, wa, dh0, dl0, dh1, dl1)
+        if (i + 1 <= ng) AWQ_STEP(i + 1, 1, wa, wa, dh1, dl1, dh0, dl0)
       }
     }
+    // ---- square and reduce (float64, fixed order) over the valid tokens
+    if (consumer) {
+      AWQ_WAIT_VMCNT(0);              // the ring's look-ahead copies have landed
+      double sq = 0.0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sq += shfl_xor_d(sq, off);
-    if (lane == 0) red[wave] = sq;
+      for (int ti = 0; ti < NT; ++ti) {
+        const int64_t tok = t0 + (int64_t)(wave + 4 * ti) * 32 + (lane & 31);
+        if (tok < m) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const double e = (double)acc[b][ti][i];
+              sq += e * e;
+            }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sq += shfl_xor_d(sq, off);
+      if (lane == 0) red[wave] = sq;
+    }
     __syncthreads();
     loss += ((red[0] + red[1]) + red[2]) + red[3];
     __syncthreads();
   }
+#undef AWQ_STEP
+#undef AWQ_CONSUME
+
+#undef AWQ_LOAD_X
+#undef AWQ_PRODUCE
+#undef AWQ_LOAD_SR
+#undef AWQ_LOAD_W
   const double inv_c = 1.0 / (double)cscale;       // exact: c is a power of two
   if (tid == 0) part[(int64_t)ai * n_blocks + rb] = loss * inv_c * inv_c;
 }
@@ -306,20 +483,24 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
   hipLaunchKernelGGL(search_blockscale_kernel, dim3((unsigned)L.n_blocks), dim3(256), 0, stream, w,
                      n, k, cblk);
   const unsigned nwg = (unsigned)(L.n_blocks * n_grid);
-  switch (g) {
-    case 32:
-      hipLaunchKernelGGL(search_loss_kernel<32>, dim3(nwg), dim3(256), 0, stream, w, x, n, k, m,
-                         n_grid, L.n_blocks, s16_all, rs_all, cblk, part);
-      break;
-    case 64:
-      hipLaunchKernelGGL(search_loss_kernel<64>, dim3(nwg), dim3(256), 0, stream, w, x, n, k, m,
-                         n_grid, L.n_blocks, s16_all, rs_all, cblk, part);
-      break;
-    default:
-      hipLaunchKernelGGL(search_loss_kernel<128>, dim3(nwg), dim3(256), 0, stream, w, x, n, k, m,
-                         n_grid, L.n_blocks, s16_all, rs_all, cblk, part);
-      break;
+  // token tiles per wave and pass: 128 NT tokens per pass
+  const int nt = m <= 128 ? 1 : (m <= 256 ? 2 : 4);
+#define AWQ_SEARCH_LAUNCH(GG, NTT)                                                              \
+  hipLaunchKernelGGL((search_loss_kernel<GG, NTT>), dim3(nwg), dim3(512), 0, stream, w, x, n, k, \
+                     m, n_grid, L.n_blocks, s16_all, rs_all, cblk, part)
+#define AWQ_SEARCH_NT(GG)                     \
+  switch (nt) {                               \
+    case 1: AWQ_SEARCH_LAUNCH(GG, 1); break;  \
+    case 2: AWQ_SEARCH_LAUNCH(GG, 2); break;  \
+    default: AWQ_SEARCH_LAUNCH(GG, 4); break; \
   }
+  switch (g) {
+    case 32: AWQ_SEARCH_NT(32); break;
+    case 64: AWQ_SEARCH_NT(64); break;
+    default: AWQ_SEARCH_NT(128); break;
+  }
+#undef AWQ_SEARCH_NT
+#undef AWQ_SEARCH_LAUNCH
   hipLaunchKernelGGL(search_select_kernel, dim3(1), dim3(256), 0, stream, part, L.n_blocks,
                      n_grid, k, s16_all, best_idx, s16, inv_s16, losses);
   return hipGetLastError();
