@@ -15,7 +15,7 @@ hipError_t launch_calib_stats(const uint16_t* x, int64_t m, int64_t k, double* o
 //   s16  [n_grid][k]        fp16 candidate scales
 //   rs   [n_grid][k]        fp32 reciprocals of the candidates
 //   part [n_grid][n_blocks] float64 per-row-block partial losses
-//   cblk [n_blocks]         fp32 power-of-two scale of the weight error per block
+//   cblk [n_blocks]         uint32 largest finite |W| (fp16 bits) of each 64-row block
 struct SearchLayout {
   size_t off_s16, off_rs, off_part, off_cblk, total;
   int64_t n_blocks;

@@ -721,20 +721,23 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
   // The activations arrive already scaled and slot-permuted (linear_xprep).
   typedef __attribute__((address_space(3))) void lds_void_t;
   const int a_lr = lane >> 3, a_p = lane & 7;
-  const uint16_t* a_src[8];
+  // 32-bit byte offsets from the activation base (one launch covers fewer
+  // than 2^31 bytes of x_tilde; the host splits larger M)
+  const char* xbytes = reinterpret_cast<const char*>(x);
+  uint32_t a_off[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int lrow = wave * 64 + 8 * i + a_lr;
     int64_t row = m0 + lrow;
     row = row < m ? row : m - 1;
-    a_src[i] = x + row * k + (a_p ^ ((lrow >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 8;
+    a_off[i] = (uint32_t)((row * k + (a_p ^ ((lrow >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 8) * 2);
   }
 #define AWQ_GEMM_LOAD_A(KT, STAGE_PTR)                                                  \
   {                                                                                     \
-    const int64_t kk_ = (int64_t)(KT) * kGemmBK;                                        \
+    const char* xk_ = xbytes + (int64_t)(KT) * kGemmBK * 2;                             \
     _Pragma("unroll") for (int i = 0; i < 8; ++i)                                       \
       __builtin_amdgcn_global_load_lds(                                                 \
-          (const void*)(a_src[i] + kk_),                                                \
+          (const void*)(xk_ + a_off[i]),                                                \
           (lds_void_t*)((STAGE_PTR) + (wave * 64 + 8 * i) * 64), 16, 0, 0);             \
   }
 
@@ -768,8 +771,19 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
   const int a_row_base = wm * 128 + (lane & 31);
 
   // One K-step: copy the next step's activations into the other stage and
-  // load its weights, dequantize this step's weights, 32 MFMAs, then wait for
-  // the copies and meet at the barrier.
+  // load its weights, then four 16-channel sub-steps: the A fragments of the
+  // next sub-step are read from LDS while the current one's 8 MFMAs run, and
+  // each sub-step dequantizes only its own two weight words; then wait for the
+  // copies and meet at the barrier.
+#define AWQ_GEMM_A_READ(CUR, S, DST)                                                    \
+  {                                                                                     \
+    const int ch_ = 4 * bc + (S);                                                       \
+    _Pragma("unroll") for (int bm = 0; bm < 4; ++bm) {                                  \
+      const int row = a_row_base + bm * 32;                                             \
+      DST[bm] = *reinterpret_cast<const half8_t*>(                                      \
+          (CUR) + ((size_t)row * 8 + (ch_ ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7))) * 8);   \
+    }                                                                                   \
+  }
 #define AWQ_GEMM_STEP(KT, CUR, NXT)                                                     \
   {                                                                                     \
     const uint4 wc0 = wb0, wc1 = wb1;                                                   \
@@ -777,37 +791,43 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
     AWQ_GEMM_LOAD_A(ktn_, NXT);                                                         \
     AWQ_GEMM_LOAD_B(ktn_);                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                  \
-    half8_t bq[2][4];                                                                   \
     const int grp = ((KT) * kGemmBK + 32 * bc) / G;                                     \
+    half2_t dd[2], o1024[2], o64[2];                                                    \
     _Pragma("unroll") for (int bn = 0; bn < 2; ++bn) {                                  \
       const int r = wn * 64 + bn * 32 + bj;                                             \
       const float d = h2f(s_l[r * ng + grp]);                                           \
       const float z = (float)((z_l[r * nzw + (grp >> 3)] >> (4 * (grp & 7))) & 0xFu);   \
-      const half2_t dd = {(half_t)d, (half_t)d};                                        \
-      const half2_t o1024 = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};          \
-      const half2_t o64 = {(half_t)(-64.0f - z), (half_t)(-64.0f - z)};                 \
-      const uint4 wv = bn == 0 ? wc0 : wc1;                                             \
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};                                  \
-      _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                   \
+      dd[bn] = half2_t{(half_t)d, (half_t)d};                                           \
+      o1024[bn] = half2_t{(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};             \
+      o64[bn] = half2_t{(half_t)(-64.0f - z), (half_t)(-64.0f - z)};                    \
+    }                                                                                   \
+    const uint32_t ww0[4] = {wc0.x, wc0.y, wc0.z, wc0.w};                               \
+    const uint32_t ww1[4] = {wc1.x, wc1.y, wc1.z, wc1.w};                               \
+    half8_t af[4];                                                                      \
+    AWQ_GEMM_A_READ(CUR, 0, af)                                                         \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                     \
+      half8_t bq[2];                                                                    \
+      _Pragma("unroll") for (int bn = 0; bn < 2; ++bn) {                                \
         uint32_t u[4];                                                                  \
-        unpack_word(ww[s], u, uc);                                                      \
-        const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024) * dd;            \
-        const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64) * dd;              \
-        const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024) * dd;            \
-        const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64) * dd;              \
-        bq[bn][s] = __builtin_bit_cast(                                                 \
+        unpack_word(bn == 0 ? ww0[s] : ww1[s], u, uc);                                  \
+        const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024[bn]) * dd[bn];    \
+        const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64[bn]) * dd[bn];      \
+        const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024[bn]) * dd[bn];    \
+        const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64[bn]) * dd[bn];      \
+        bq[bn] = __builtin_bit_cast(                                                    \
             half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1), \
                                 __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3))); \
       }                                                                                 \
-    }                                                                                   \
-    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                     \
-      const int ch = 4 * bc + s;                                                        \
+      /* each A fragment is reloaded for the next sub-step right after its last use */  \
+      const int chn_ = 4 * bc + (s + 1 < 4 ? s + 1 : s);                                \
       _Pragma("unroll") for (int bm = 0; bm < 4; ++bm) {                                \
-        const int row = a_row_base + bm * 32;                                           \
-        const half8_t av = *reinterpret_cast<const half8_t*>(                           \
-            (CUR) + ((size_t)row * 8 + (ch ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7))) * 8);  \
         _Pragma("unroll") for (int bn = 0; bn < 2; ++bn)                                \
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bq[bn][s], acc[bm][bn], 0, 0, 0); \
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bm], bq[bn], acc[bm][bn], 0, 0, 0); \
+        if (s + 1 < 4) {                                                                \
+          const int row = a_row_base + bm * 32;                                         \
+          af[bm] = *reinterpret_cast<const half8_t*>(                                   \
+              (CUR) + ((size_t)row * 8 + (chn_ ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7))) * 8); \
+        }                                                                               \
       }                                                                                 \
     }                                                                                   \
     __builtin_amdgcn_s_waitcnt(0);                                                      \
@@ -820,6 +840,7 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
   }
   if (kt < nk) AWQ_GEMM_STEP(kt, a_st0, a_st1);
 #undef AWQ_GEMM_STEP
+#undef AWQ_GEMM_A_READ
 #undef AWQ_GEMM_LOAD_A
 #undef AWQ_GEMM_LOAD_B
 
@@ -855,10 +876,18 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
     const int64_t pgrid = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
     hipLaunchKernelGGL(linear_xprep_kernel, dim3((unsigned)pgrid), dim3(256), 0, stream, x, inv_s16,
                        m, k, xt);
-    const int tiles_m = (int)((m + kGemmBM - 1) / kGemmBM);
+    // the kernel addresses its activations with 32-bit byte offsets: launch
+    // in row chunks of fewer than 2^31 bytes of x_tilde
+    int64_t chunk = (((int64_t)1 << 31) / (k * 2)) / kGemmBM * kGemmBM;
+    chunk = chunk > 0 ? chunk : kGemmBM;
     const int tiles_n = (int)((n + kGemmBN - 1) / kGemmBN);
-    hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), lds,
-                       stream, xt, qweight, scales, qzeros, m, n, k, y, tiles_m, tiles_n);
+    for (int64_t r0 = 0; r0 < m; r0 += chunk) {
+      const int64_t mc = (m - r0) < chunk ? (m - r0) : chunk;
+      const int tiles_m = (int)((mc + kGemmBM - 1) / kGemmBM);
+      hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), lds,
+                         stream, xt + r0 * k, qweight, scales, qzeros, mc, n, k, y + r0 * n, tiles_m,
+                         tiles_n);
+    }
     return hipGetLastError();
   }
   // the fused decode kernel: at most kGemvMaxBlk column blocks per

@@ -5,8 +5,9 @@
 // Four kernels, all on the caller's stream:
 //  1. search_prep: s_ik = fp16_rn(max(a_k^alpha_i, 2^-14)) and 1/s_ik (fp32)
 //     for every grid point and channel (float64 pow, single fp16 rounding).
-//  2. search_blockscale: a power-of-two factor per 64-row block that keeps the
-//     fp16 split of the weight error in the normal range (see below).
+//  2. search_blockmax: the largest finite |W| of every 64-row block, from
+//     which the loss kernel takes a power-of-two factor that keeps the fp16
+//     split of the weight error in the normal range (see below).
 //  3. search_loss: one work-group per (64-row block, alpha).  For every group
 //     of g channels it fake-quantizes the 64 x g block of W' = fp16(W s_i)
 //     (exact per-element codes, see awq_common.h), forms the weight error
@@ -49,9 +50,13 @@ SearchLayout search_layout(int64_t n, int64_t k, int64_t m, int32_t g, int32_t n
 __global__ __launch_bounds__(256) void search_prep_kernel(const double* __restrict__ a,
                                                           int64_t k, int32_t n_grid,
                                                           uint16_t* __restrict__ s16,
-                                                          float* __restrict__ rs) {
+                                                          float* __restrict__ rs,
+                                                          uint32_t* __restrict__ bmax,
+                                                          int64_t n_blocks) {
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int i = blockIdx.y;
+  if (i == 0)   // the block maxima of |W| start from zero (filled by search_blockmax)
+    for (int64_t b = col; b < n_blocks; b += (int64_t)gridDim.x * 256) bmax[b] = 0u;
   if (col >= k) return;
   const double alpha = (double)i / (double)n_grid;
   double p;
@@ -72,28 +77,36 @@ __global__ __launch_bounds__(256) void search_prep_kernel(const double* __restri
 // With max|W| < 2^e the factor c = 2^(14 - e) keeps c |dW| below 17000, inside
 // fp16, while lifting small errors far above the fp16 subnormal range, so the
 // fp16 hi + lo split of c dW keeps about 22 significant bits.
-__global__ __launch_bounds__(256) void search_blockscale_kernel(const uint16_t* __restrict__ w,
-                                                                int64_t n, int64_t k,
-                                                                float* __restrict__ cblk) {
+//
+// search_blockmax: work-group (block, 512-column chunk) folds the finite |W|
+// of its 64 x 512 tile into the block maximum with an integer atomic max on
+// the fp16 bit patterns (|fp16| bits order like the values; max is
+// order-independent, so the result is deterministic).
+constexpr int kBlockMaxCols = 512;
+__global__ __launch_bounds__(256) void search_blockmax_kernel(const uint16_t* __restrict__ w,
+                                                              int64_t n, int64_t k,
+                                                              uint32_t* __restrict__ bmax) {
   __shared__ uint32_t red[4];
   const int64_t rb = blockIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.y * kBlockMaxCols;
   const int64_t r0 = rb * kSearchRows;
   const int64_t rows = (n - r0) < kSearchRows ? (n - r0) : kSearchRows;
-  const int64_t words = rows * k / 8;          // 8 halves per 16-byte load
-  const uint4* base = reinterpret_cast<const uint4*>(w + r0 * k);
+  const int64_t cols = (k - c0) < kBlockMaxCols ? (k - c0) : kBlockMaxCols;   // multiple of 8
+  const int64_t cw = cols / 8;
   uint32_t mx = 0;
-  for (int64_t i = threadIdx.x; i < words; i += 256) {
-    uint4 v = base[i];
-    uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+  for (int64_t i = threadIdx.x; i < rows * cw; i += 256) {
+    const int64_t rr = i / cw, cc = i % cw;
+    const uint4 v = *reinterpret_cast<const uint4*>(w + (r0 + rr) * k + c0 + cc * 8);
+    const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
-      uint32_t b = (ww[h >> 1] >> ((h & 1) * 16)) & 0x7FFFu;
-      if (b < 0x7C00u && b > mx) mx = b;         // |fp16| bits order like the values
+      const uint32_t bits = (ww[h >> 1] >> ((h & 1) * 16)) & 0x7FFFu;
+      if (bits < 0x7C00u && bits > mx) mx = bits;
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(mx, off, 64);
+    const uint32_t o = __shfl_xor(mx, off, 64);
     mx = o > mx ? o : mx;
   }
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -101,14 +114,16 @@ __global__ __launch_bounds__(256) void search_blockscale_kernel(const uint16_t* 
   if (threadIdx.x == 0) {
     uint32_t m = red[0];
     for (int i = 1; i < 4; ++i) m = red[i] > m ? red[i] : m;
-    float c = 1.0f;
-    if (m != 0) {
-      int e;
-      (void)__builtin_frexpf(h2f((uint16_t)m), &e);   // max|W| < 2^e
-      c = __builtin_ldexpf(1.0f, 14 - e);
-    }
-    cblk[rb] = c;
+    if (m != 0) atomicMax(&bmax[rb], m);
   }
+}
+
+// c = 2^(14 - e) for a block whose largest finite |W| (fp16 bits m) is below 2^e
+__device__ __forceinline__ float block_factor(uint32_t m) {
+  if (m == 0) return 1.0f;
+  int e;
+  (void)__builtin_frexpf(h2f((uint16_t)m), &e);
+  return __builtin_ldexpf(1.0f, 14 - e);
 }
 
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane i
@@ -169,7 +184,7 @@ template <int G, int NT>
 __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ x, int64_t n, int64_t k,
     int64_t m, int32_t n_grid, int64_t n_blocks, const uint16_t* __restrict__ s16_all,
-    const float* __restrict__ rs_all, const float* __restrict__ cblk, double* __restrict__ part) {
+    const float* __restrict__ rs_all, const uint32_t* __restrict__ bmax, double* __restrict__ part) {
   constexpr int EPT = G / 4;          // elements of one row-group per producer thread
   constexpr int KSTEPS = G / 16;      // MFMA k-steps per group (even)
   constexpr int TOK = 128 * NT;       // tokens per pass
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool consumer = wave < 4;     // wave-uniform role
-  const float cscale = cblk[rb];
+  const float cscale = block_factor(bmax[rb]);
   const int ng = (int)(k / G);
 
   // ---- producer state
@@ -433,18 +448,28 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   if (tid == 0) part[(int64_t)ai * n_blocks + rb] = loss * inv_c * inv_c;
 }
 
+// One wave per alpha (alpha = wave, wave + 4, ...): lane l sums the partials
+// of blocks l, l + 64, ... in order, then a fixed butterfly combines the lanes,
+// so the sum is deterministic.  Thread 0 takes the first minimum over finite
+// losses.  Every work-group of the grid computes the same sums and minimum and
+// writes s16 and inv_s16 for its 256 channels; work-group 0 also writes the
+// losses and the index.
 __global__ __launch_bounds__(256) void search_select_kernel(
     const double* __restrict__ part, int64_t n_blocks, int32_t n_grid, int64_t k,
     const uint16_t* __restrict__ s16_all, int32_t* __restrict__ best_idx,
     uint16_t* __restrict__ s16, uint16_t* __restrict__ inv_s16, double* __restrict__ losses) {
   __shared__ double L[64];
   __shared__ int best_s;
-  const int tid = threadIdx.x;
-  if (tid < n_grid) {
-    double s = 0.0;
-    for (int64_t b = 0; b < n_blocks; ++b) s += part[(int64_t)tid * n_blocks + b];
-    L[tid] = s;
-    if (losses != nullptr) losses[tid] = s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = wave; i < n_grid; i += 4) {
+    double sacc = 0.0;
+    for (int64_t b = lane; b < n_blocks; b += 64) sacc += part[(int64_t)i * n_blocks + b];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sacc += shfl_xor_d(sacc, off);
+    if (lane == 0) {
+      L[i] = sacc;
+      if (losses != nullptr && blockIdx.x == 0) losses[i] = sacc;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -456,11 +481,12 @@ __global__ __launch_bounds__(256) void search_select_kernel(
       if (best < 0 || v < bv) { best = i; bv = v; }
     }
     best_s = best;
-    *best_idx = best;
+    if (blockIdx.x == 0) *best_idx = best;
   }
   __syncthreads();
   const int best = best_s;
-  for (int64_t col = tid; col < k; col += 256) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + tid;
+  if (col < k) {
     uint16_t sb = best >= 0 ? s16_all[(int64_t)best * k + col] : kF16One;
     s16[col] = sb;
     inv_s16[col] = f64_to_f16_rn(1.0 / (double)h2f(sb));
@@ -476,18 +502,19 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
   uint16_t* s16_all = reinterpret_cast<uint16_t*>(ws + L.off_s16);
   float* rs_all = reinterpret_cast<float*>(ws + L.off_rs);
   double* part = reinterpret_cast<double*>(ws + L.off_part);
-  float* cblk = reinterpret_cast<float*>(ws + L.off_cblk);
+  uint32_t* bmax = reinterpret_cast<uint32_t*>(ws + L.off_cblk);
 
   hipLaunchKernelGGL(search_prep_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)n_grid),
-                     dim3(256), 0, stream, mean_abs, k, n_grid, s16_all, rs_all);
-  hipLaunchKernelGGL(search_blockscale_kernel, dim3((unsigned)L.n_blocks), dim3(256), 0, stream, w,
-                     n, k, cblk);
+                     dim3(256), 0, stream, mean_abs, k, n_grid, s16_all, rs_all, bmax, L.n_blocks);
+  hipLaunchKernelGGL(search_blockmax_kernel,
+                     dim3((unsigned)L.n_blocks, (unsigned)((k + kBlockMaxCols - 1) / kBlockMaxCols)),
+                     dim3(256), 0, stream, w, n, k, bmax);
   const unsigned nwg = (unsigned)(L.n_blocks * n_grid);
   // token tiles per wave and pass: 128 NT tokens per pass
   const int nt = m <= 128 ? 1 : (m <= 256 ? 2 : 4);
 #define AWQ_SEARCH_LAUNCH(GG, NTT)                                                              \
   hipLaunchKernelGGL((search_loss_kernel<GG, NTT>), dim3(nwg), dim3(512), 0, stream, w, x, n, k, \
-                     m, n_grid, L.n_blocks, s16_all, rs_all, cblk, part)
+                     m, n_grid, L.n_blocks, s16_all, rs_all, bmax, part)
 #define AWQ_SEARCH_NT(GG)                     \
   switch (nt) {                               \
     case 1: AWQ_SEARCH_LAUNCH(GG, 1); break;  \
@@ -501,7 +528,8 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
   }
 #undef AWQ_SEARCH_NT
 #undef AWQ_SEARCH_LAUNCH
-  hipLaunchKernelGGL(search_select_kernel, dim3(1), dim3(256), 0, stream, part, L.n_blocks,
+  hipLaunchKernelGGL(search_select_kernel, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, stream,
+                     part, L.n_blocks,
                      n_grid, k, s16_all, best_idx, s16, inv_s16, losses);
   return hipGetLastError();
 }
