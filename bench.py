@@ -19,6 +19,7 @@ on.  The stack is 3.6 GB, far beyond the 256 MB Infinity Cache, so every
 weight byte comes from HBM.
 
     python bench.py [--steps K] [--warmup W] [--layers 32] [--no-cpu]
+    python bench.py --copy-calibration      (counter calibration only)
 """
 from __future__ import annotations
 
@@ -75,11 +76,17 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 10 plain device-to-device copies of 256 MiB (the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import synthetic as S
@@ -298,6 +305,22 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration():
+    """Ten device-to-device copies of 256 MiB (read 256 MiB, write 256 MiB
+    each): a known byte count against which the HBM traffic counters are scaled."""
+    import torch
+    nbytes = 256 * 1024 * 1024
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": nbytes,
+                                           "bytes_written_per_copy": nbytes, "copies": 10}}),
+          flush=True)
 
 
 def cpu_baseline(budget_s):

@@ -768,7 +768,16 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
   __builtin_amdgcn_s_waitcnt(0);       // the direct-to-LDS copies have landed
   __syncthreads();
   const UnpackConsts uc = unpack_consts();
-  const int a_row_base = wm * 128 + (lane & 31);
+  // byte offset of this lane's A fragment of row block bm at sub-step 0: row
+  // r = wm 128 + bm 32 + lane % 32 holds logical chunk ch = 4 (lane / 32) + s
+  // at physical chunk ch ^ ((r >> S) & 7); s only flips chunk bits 0-1, so
+  // sub-step s reads a_base[bm] ^ (16 s)
+  uint32_t a_base[4];
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+    const int row = wm * 128 + bm * 32 + (lane & 31);
+    a_base[bm] = (uint32_t)(row * 128 + ((4 * bc) ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 16);
+  }
 
   // One K-step: copy the next step's activations into the other stage and
   // load its weights, then four 16-channel sub-steps: the A fragments of the
@@ -777,12 +786,9 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
   // copies and meet at the barrier.
 #define AWQ_GEMM_A_READ(CUR, S, DST)                                                    \
   {                                                                                     \
-    const int ch_ = 4 * bc + (S);                                                       \
-    _Pragma("unroll") for (int bm = 0; bm < 4; ++bm) {                                  \
-      const int row = a_row_base + bm * 32;                                             \
+    _Pragma("unroll") for (int bm = 0; bm < 4; ++bm)                                    \
       DST[bm] = *reinterpret_cast<const half8_t*>(                                      \
-          (CUR) + ((size_t)row * 8 + (ch_ ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7))) * 8);   \
-    }                                                                                   \
+          reinterpret_cast<const char*>(CUR) + (a_base[bm] ^ (uint32_t)(16 * (S))));     \
   }
 #define AWQ_GEMM_STEP(KT, CUR, NXT)                                                     \
   {                                                                                     \
@@ -819,15 +825,12 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
                                 __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3))); \
       }                                                                                 \
       /* each A fragment is reloaded for the next sub-step right after its last use */  \
-      const int chn_ = 4 * bc + (s + 1 < 4 ? s + 1 : s);                                \
       _Pragma("unroll") for (int bm = 0; bm < 4; ++bm) {                                \
         _Pragma("unroll") for (int bn = 0; bn < 2; ++bn)                                \
           acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bm], bq[bn], acc[bm][bn], 0, 0, 0); \
-        if (s + 1 < 4) {                                                                \
-          const int row = a_row_base + bm * 32;                                         \
+        if (s + 1 < 4)                                                                  \
           af[bm] = *reinterpret_cast<const half8_t*>(                                   \
-              (CUR) + ((size_t)row * 8 + (chn_ ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7))) * 8); \
-        }                                                                               \
+              reinterpret_cast<const char*>(CUR) + (a_base[bm] ^ (uint32_t)(16 * (s + 1)))); \
       }                                                                                 \
     }                                                                                   \
     __builtin_amdgcn_s_waitcnt(0);                                                      \

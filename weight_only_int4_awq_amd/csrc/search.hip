@@ -14,7 +14,7 @@
 //     dW = ((q - z) D - W s) / s in fp32 (no cancellation: both terms of the
 //     difference are exact), splits it into fp16 hi + lo, stages both in LDS
 //     in the MFMA A-operand layout and multiplies them with the calibration
-//     tokens (B operand, from global memory one step ahead) into fp32
+//     tokens (B operand, copied into LDS three steps ahead) into fp32
 //     accumulators E = dW X^T.  After the last group it squares E in float64
 //     and writes the block's partial loss.
 //  4. search_select: sums the partials of each alpha in block order (fixed),
