@@ -305,15 +305,17 @@ def test_linear_deterministic(P):
         assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("n,k,g", [(40, 16384, 32), (24, 28672, 64), (33, 8192, 32), (20, 40960, 128)])
+@pytest.mark.parametrize("n,k,g", [(40, 16384, 32), (24, 28672, 64), (33, 8192, 32), (20, 40960, 128),
+                                   (16, 65536, 128)])
 def test_linear_decode_wide_k(P, n, k, g):
     # long K with small groups: fewer column blocks per work-group fit the
-    # decode kernel's prologue and LDS plan (down to one at 28672 / 64); at
-    # K = 40960 the activations alone exceed LDS and the staged two-kernel path
-    # runs at m = 1
+    # decode kernels' prologue and LDS plans (down to one at 28672 / 64); at
+    # K = 40960 with g = 128 the m = 1 activations alone exceed LDS and the
+    # staged two-kernel path runs at m = 1; at K = 65536 it runs at every m
     w = S.weights(n, k, 0.02, 440 + n)
-    x = S.activations(1, k, 441 + n, S.outlier_channels(k, 0.01, 442), 20.0)
-    _check_linear(P, w, x, None, g)
+    for m in (1, 8, 24):
+        x = S.activations(m, k, 441 + n + m, S.outlier_channels(k, 0.01, 442), 20.0)
+        _check_linear(P, w, x, None, g)
 
 
 @pytest.mark.parametrize("n,k,g", [(8261, 256, 64), (40000, 512, 128), (12345, 2048, 32)])

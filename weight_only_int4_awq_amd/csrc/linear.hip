@@ -532,8 +532,11 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
     ++blocks_done;
   };
   int c_j = jb, c_left = total;                       // consume cursor
-  auto consume = [&](int p) {
-    if (c_left > 0) {                                 // wave-uniform
+  // GUARDED only in the tail: a consume skipped behind a branch would leave
+  // its slot's loads pending in the compiler's view, and the next reuse of
+  // those registers would then wait for every outstanding load
+  auto consume = [&](int p, bool guarded) {
+    if (!guarded || c_left > 0) {                     // wave-uniform
       const int j = c_j;
       const char* asrc = a_base + a_lane + (uint32_t)j * a_step;
       half8_t aop[WPL];
@@ -570,22 +573,22 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
 #pragma unroll
         for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p);
 #pragma unroll
-        for (int p = 0; p < kGemvPF; ++p) consume(p);
+        for (int p = 0; p < kGemvPF; ++p) consume(p, false);
         left -= kGemvPF;
       } else {
 #pragma unroll
-        for (int p = 0; p < kGemvPF; ++p) consume(p);
+        for (int p = 0; p < kGemvPF; ++p) consume(p, true);
         break;
       }
       if (left > kGemvPF) {
 #pragma unroll
         for (int p = 0; p < kGemvPF; ++p) issue(p);
 #pragma unroll
-        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p);
+        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p, false);
         left -= kGemvPF;
       } else {
 #pragma unroll
-        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p);
+        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p, true);
         break;
       }
     }
@@ -601,6 +604,591 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
       if (col < n) y[col] = f2h_rn(ybuf[bi * 16 + lane]);
     }
   }
+}
+
+// Raw buffer loads: the resource records the tensor's byte size, and the
+// hardware returns zero for any lane whose offset reaches it, so a partial
+// last column block needs no per-lane clamp, and each load is a loop-invariant
+// per-lane offset plus a scalar offset (no vector address arithmetic in the
+// loop).  Sizes are below 4 GiB (checked at the C ABI).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+template <int WPL>
+__device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                          uint32_t (&w)[WPL]) {
+  if constexpr (WPL == 4) {
+    const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (WPL == 2) {
+    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0));
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+  }
+}
+
+// ---------------------------------------------------------------- skinny, 2 <= m <= 32
+// linear_prep16 writes x_tilde = fp16_rn(x * inv_s) once per call as the MFMA
+// A operand, 16 tokens per chunk (one chunk for m <= 16, two for m <= 32):
+// [chunk][group][lane group c][row][g/4 halves], channels of every 8-channel
+// word in the nibble-unpack order, plus the offset sums T, U per (chunk,
+// group, row).  linear_skinny16 follows the decode GEMV: 8 waves split K,
+// 16-column blocks (up to 4 per work-group), scale|zero words and the offset
+// sums staged in LDS up front, each wave's (block, group) items prefetched
+// with their weight words and activation fragments (unconditional loads, so
+// the waits stay exact), one barrier per block and outputs stored at the end.
+template <int G>
+__global__ __launch_bounds__(256) void linear_prep16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s, int64_t m, int64_t k,
+    int64_t n_pairs, uint16_t* __restrict__ a16, float2* __restrict__ tu16) {
+  constexpr int WPL = G / 32, HPL = G / 4;
+  const int64_t ng = k / G;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (chunk, group)
+  if (pair >= n_pairs) return;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, c = lane >> 4;
+  const int64_t tc = pair / ng, j = pair % ng;
+  const int64_t t = tc * 16 + r;
+  uint16_t vals[HPL];
+  double tsum = 0.0, usum = 0.0;
+#pragma unroll
+  for (int i = 0; i < WPL; ++i) {
+    const int64_t kw = j * G + 8 * (WPL * c + i);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int nib = slot_nibble(s);
+      uint16_t h = 0;
+      if (t < m) {
+        float xv = h2f(x[t * k + kw + nib]);
+        if (inv_s != nullptr) xv *= h2f(inv_s[kw + nib]);   // exact: fp16 x fp16
+        h = f2h_rn(xv);
+      }
+      vals[i * 8 + s] = h;
+      const double hv = (double)h2f(h);
+      usum += hv;
+      tsum += hv * ((nib & 1) ? 64.0 : 1024.0);
+    }
+  }
+  uint16_t* dst = a16 + ((pair * 4 + c) * 16 + r) * HPL;
+#pragma unroll
+  for (int i = 0; i < HPL; i += 8) {
+    uint4 v;
+    v.x = (uint32_t)vals[i + 0] | ((uint32_t)vals[i + 1] << 16);
+    v.y = (uint32_t)vals[i + 2] | ((uint32_t)vals[i + 3] << 16);
+    v.z = (uint32_t)vals[i + 4] | ((uint32_t)vals[i + 5] << 16);
+    v.w = (uint32_t)vals[i + 6] | ((uint32_t)vals[i + 7] << 16);
+    *reinterpret_cast<uint4*>(dst + i) = v;
+  }
+  tsum += shfl_xor_d(tsum, 16);
+  tsum += shfl_xor_d(tsum, 32);
+  usum += shfl_xor_d(usum, 16);
+  usum += shfl_xor_d(usum, 32);
+  if (c == 0) tu16[pair * 16 + r] = make_float2((float)tsum, (float)usum);
+}
+
+constexpr int kSk16Waves = 8;
+constexpr int kSk16Threads = kSk16Waves * 64;
+
+// LDS: scale|zero words [nb][ng][16], offset sums [tc][ng][16] float2 (rounded
+// up to whole 1 KiB copies), reduction rows [2][8][tc][64] float4, outputs
+// [nb][tc][64] float4.
+size_t skinny16_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
+  const size_t ng = (size_t)(k / g);
+  const size_t tu = ((size_t)tc * ng * 16 * 8 + 1023) & ~(size_t)1023;
+  return (size_t)nb * ng * 16 * 4 + tu + (size_t)2 * kSk16Waves * tc * 64 * 16 +
+         (size_t)nb * tc * 64 * 16;
+}
+
+template <int G, int TC, bool SZV, int PF>
+__global__ __launch_bounds__(kSk16Threads, 4) void linear_skinny16_kernel(
+    const uint16_t* __restrict__ a16, const float2* __restrict__ tu16,
+    const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
+    uint16_t* __restrict__ y) {
+  constexpr int WPL = G / 32, HPL = G / 4, LPG = G / 8;
+  constexpr int W = kSk16Waves;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int ng = (int)(k / G);
+  const int nblk = (int)((n + 15) / 16);
+  const int grid = (int)gridDim.x;
+  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // 1 .. kGemvMaxBlk
+  const size_t tu_bytes = ((size_t)TC * ng * 16 * 8 + 1023) & ~(size_t)1023;
+  unsigned char* sp = smem;
+  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);   sp += (size_t)my_blocks * ng * 16 * 4;
+  float2* tu_l = reinterpret_cast<float2*>(sp);      sp += tu_bytes;
+  floatx4_t* red = reinterpret_cast<floatx4_t*>(sp); sp += (size_t)2 * W * TC * 64 * 16;
+  floatx4_t* ybuf = reinterpret_cast<floatx4_t*>(sp);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int jb = ng * wave / W, je = ng * (wave + 1) / W;
+  const int cnt = je - jb;
+  const int total = my_blocks * cnt;
+  const int nzw = (ng + 7) / 8, kw_row = (int)(k / 8);
+
+  // ---- 1. offset sums: straight global -> LDS copies of 1 KiB per wave
+  // instruction (lane i copies 16 bytes; the tail is clamped to the last
+  // 16 bytes of the source and lands in the rounded-up LDS pad)
+  {
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    const int64_t src_bytes = (int64_t)TC * ng * 16 * 8;
+    const char* srcb = reinterpret_cast<const char*>(tu16);
+    const int n_copy = (int)(tu_bytes / 1024);
+    for (int i = wave; i < n_copy; i += W) {
+      int64_t off = (int64_t)i * 1024 + lane * 16;
+      off = off + 16 <= src_bytes ? off : src_bytes - 16;
+      __builtin_amdgcn_global_load_lds((const void*)(srcb + off),
+                                       (lds_void_t*)(reinterpret_cast<char*>(tu_l) + i * 1024),
+                                       16, 0, 0);
+    }
+  }
+  // ---- 2. scale and zero words of every block (lane-predicated, first)
+  const int n_oct = my_blocks * 16 * nzw;
+  uint4 sz_s[kGemvSzRounds];
+  uint32_t sz_z[kGemvSzRounds];
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    sz_s[i] = make_uint4(0, 0, 0, 0);
+    sz_z[i] = 0;
+    const int o = tid + i * kSk16Threads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      int col = ((int)blockIdx.x + bs * grid) * 16 + row;
+      col = col < (int)n ? col : (int)n - 1;
+      const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
+      if constexpr (SZV) {
+        sz_s[i] = *reinterpret_cast<const uint4*>(srow);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (oct * 8 + e < ng) ? srow[e] : (uint16_t)0;
+        sz_s[i] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                             h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+      }
+      sz_z[i] = qzeros[(int64_t)col * nzw + oct];
+    }
+  }
+
+  // ---- 3. first items: weight words and activation fragments (unconditional
+  // buffer loads; a lane past the last column reads zeros)
+  uint32_t wq[2 * PF][WPL];
+  uint4 aq[2 * PF][TC][WPL];          // raw bits, like the weight words
+  const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(qweight, (uint32_t)((uint64_t)n * (uint64_t)k / 2));
+  const __amdgpu_buffer_rsrc_t rs_a = buf_rsrc(a16, (uint32_t)((uint64_t)TC * (uint64_t)k * 32));
+  const uint32_t w_voff = ((uint32_t)r * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
+  const uint32_t a_voff = (uint32_t)((c * 16 + r) * HPL) * 2u;
+  int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;
+  auto issue = [&](int slot) {
+    const int jj = i_j < ng ? i_j : ng - 1;
+    const uint32_t wso = ((uint32_t)i_blk * 16u * (uint32_t)kw_row + (uint32_t)(jj * LPG)) * 4u;
+    buf_words<WPL>(rs_w, w_voff, wso, wq[slot]);
+#pragma unroll
+    for (int tc = 0; tc < TC; ++tc) {
+      const uint32_t aso = (uint32_t)((tc * ng + jj) * 64 * HPL) * 2u;
+#pragma unroll
+      for (int i = 0; i < WPL; ++i)
+        aq[slot][tc][i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_voff + 16u * i, aso, 0));
+    }
+    if (i_left > 1) {
+      --i_left;
+      if (++i_j == je) { i_j = jb; i_blk += grid; }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(p);
+
+  // ---- 4. scale|zero words into LDS as [block][group][column]
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    const int o = tid + i * kSk16Threads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      const uint32_t sw[4] = {sz_s[i].x, sz_s[i].y, sz_s[i].z, sz_s[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = oct * 8 + e;
+        if (j < ng)
+          szw[((size_t)bs * ng + j) * 16 + row] =
+              ((sw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) | (((sz_z[i] >> (4 * e)) & 0xFu) << 16);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);      // the offset-sum copies have landed
+  __syncthreads();
+
+  const UnpackConsts uc = unpack_consts();
+  const int reducer = W - 1;          // always owns at least one group
+  floatx4_t yacc[TC];
+#pragma unroll
+  for (int tc = 0; tc < TC; ++tc) yacc[tc] = floatx4_t{};
+  int blocks_done = 0;
+  auto finish_block = [&]() {
+    floatx4_t* rb = red + (size_t)(blocks_done & 1) * W * TC * 64;
+#pragma unroll
+    for (int tc = 0; tc < TC; ++tc) {
+      rb[(wave * TC + tc) * 64 + lane] = yacc[tc];
+      yacc[tc] = floatx4_t{};
+    }
+    __syncthreads();
+    if (wave == reducer) {
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc) {
+        floatx4_t sacc = rb[tc * 64 + lane];
+#pragma unroll
+        for (int wv = 1; wv < W; ++wv) sacc += rb[(wv * TC + tc) * 64 + lane];
+        ybuf[((size_t)blocks_done * TC + tc) * 64 + lane] = sacc;
+      }
+    }
+    ++blocks_done;
+  };
+  int c_j = jb, c_left = total;
+  auto consume = [&](int p, bool guarded) {   // guarded only in the tail (see the GEMV)
+    if (!guarded || c_left > 0) {
+      const int j = c_j;
+      const uint32_t szv = szw[((size_t)blocks_done * ng + j) * 16 + r];
+      const float dsc = h2f((uint16_t)szv), zf = (float)(szv >> 16);
+      half8_t bop[WPL];
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        uint32_t u[4];
+        unpack_word(wq[p][i], u, uc);
+        bop[i] = __builtin_bit_cast(half8_t, make_uint4(u[0], u[1], u[2], u[3]));
+      }
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc) {
+        floatx4_t cacc = floatx4_t{};
+#pragma unroll
+        for (int i = 0; i < WPL; ++i)
+          cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, aq[p][tc][i]), bop[i],
+                                                        cacc, 0, 0, 0);
+        // rows 4c .. 4c+3 of the chunk (tokens) for column r
+        const float4* tup = reinterpret_cast<const float4*>(tu_l + ((size_t)tc * ng + j) * 16 + 4 * c);
+        const float4 t01 = tup[0], t23 = tup[1];
+        const float tt[4] = {t01.x, t01.z, t23.x, t23.z};
+        const float uu[4] = {t01.y, t01.w, t23.y, t23.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          yacc[tc][e] = __builtin_fmaf(dsc, __builtin_fmaf(-zf, uu[e], cacc[e] - tt[e]), yacc[tc][e]);
+      }
+      --c_left;
+      if (++c_j == je) {
+        finish_block();
+        c_j = jb;
+      }
+    }
+  };
+  if (cnt > 0) {
+    int left = total;
+    while (true) {
+      if (left > PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(PF + p);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(p, false);
+        left -= PF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(p, true);
+        break;
+      }
+      if (left > PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(p);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(PF + p, false);
+        left -= PF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(PF + p, true);
+        break;
+      }
+    }
+  } else {
+    for (int bi = 0; bi < my_blocks; ++bi) finish_block();
+  }
+
+  // ---- outputs: the reducer wave wrote every row of ybuf itself
+  if (wave == reducer) {
+    for (int bi = 0; bi < my_blocks; ++bi) {
+      const int64_t col = ((int64_t)blockIdx.x + (int64_t)bi * grid) * 16 + r;
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc) {
+        const floatx4_t v = ybuf[((size_t)bi * TC + tc) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = (int64_t)tc * 16 + 4 * c + e;
+          if (t < m && col < n) y[t * n + col] = f2h_rn(v[e]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- skinny, fused
+// linear_skinny_fused: one kernel for 2 <= m <= 32 with the decode GEMV's
+// layout (8 waves split K, 16-column blocks, scale|zero words staged up front,
+// one barrier per block, outputs stored at the end), but no staged activation
+// operand: every (block, group) item loads, next to its weight words, the raw
+// 16-byte activation rows of its tokens (tokens 16 tc + lane % 16; buffer
+// loads, so rows past m read zeros and cost nothing), and the MFMA A operand
+// x_tilde = fp16_rn(x * inv_s) is formed in registers (v_pk_mul_f16 against
+// inv_s staged in LDS, then the channels permuted into the unpack order).
+// The weights are dequantized in registers to fp16_rn((q - z) D) as in the
+// prefill GEMM, so the MFMA accumulates whole groups with no offset sums.
+template <int G, int TC, bool SZV, int PF>
+__global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
+    const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
+    uint16_t* __restrict__ y) {
+  constexpr int WPL = G / 32, LPG = G / 8;
+  constexpr int W = kSk16Waves;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int ng = (int)(k / G);
+  const int nblk = (int)((n + 15) / 16);
+  const int grid = (int)gridDim.x;
+  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // 1 .. kGemvMaxBlk
+  const size_t inv_bytes = ((size_t)k * 2 + 1023) & ~(size_t)1023;
+  unsigned char* sp = smem;
+  uint16_t* inv_l = reinterpret_cast<uint16_t*>(sp);  sp += inv_bytes;
+  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);    sp += (size_t)my_blocks * ng * 16 * 4;
+  floatx4_t* red = reinterpret_cast<floatx4_t*>(sp);  sp += (size_t)2 * W * TC * 64 * 16;
+  floatx4_t* ybuf = reinterpret_cast<floatx4_t*>(sp);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int jb = ng * wave / W, je = ng * (wave + 1) / W;
+  const int cnt = je - jb;
+  const int total = my_blocks * cnt;
+  const int nzw = (ng + 7) / 8, kw_row = (int)(k / 8);
+  const bool has_inv = inv_s != nullptr;
+
+  // ---- 1. inv_s into LDS: straight global -> LDS copies of 1 KiB per wave
+  // instruction (the tail clamped to the last 16 source bytes, landing in the
+  // rounded-up pad)
+  if (has_inv) {
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    const int64_t src_bytes = k * 2;
+    const char* srcb = reinterpret_cast<const char*>(inv_s);
+    const int n_copy = (int)(inv_bytes / 1024);
+    for (int i = wave; i < n_copy; i += W) {
+      int64_t off = (int64_t)i * 1024 + lane * 16;
+      off = off + 16 <= src_bytes ? off : src_bytes - 16;
+      __builtin_amdgcn_global_load_lds((const void*)(srcb + off),
+                                       (lds_void_t*)(reinterpret_cast<char*>(inv_l) + i * 1024),
+                                       16, 0, 0);
+    }
+  }
+  // ---- 2. scale and zero words of every block (lane-predicated, first)
+  const int n_oct = my_blocks * 16 * nzw;
+  uint4 sz_s[kGemvSzRounds];
+  uint32_t sz_z[kGemvSzRounds];
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    sz_s[i] = make_uint4(0, 0, 0, 0);
+    sz_z[i] = 0;
+    const int o = tid + i * kSk16Threads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      int col = ((int)blockIdx.x + bs * grid) * 16 + row;
+      col = col < (int)n ? col : (int)n - 1;
+      const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
+      if constexpr (SZV) {
+        sz_s[i] = *reinterpret_cast<const uint4*>(srow);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (oct * 8 + e < ng) ? srow[e] : (uint16_t)0;
+        sz_s[i] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                             h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+      }
+      sz_z[i] = qzeros[(int64_t)col * nzw + oct];
+    }
+  }
+
+  // ---- 3. first items (unconditional buffer loads; rows past m and columns
+  // past n read zeros)
+  uint32_t wq[2 * PF][WPL];
+  uint4 xq[2 * PF][TC][WPL];
+  const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(qweight, (uint32_t)((uint64_t)n * (uint64_t)k / 2));
+  const __amdgpu_buffer_rsrc_t rs_x = buf_rsrc(x, (uint32_t)((uint64_t)m * (uint64_t)k * 2));
+  const uint32_t w_voff = ((uint32_t)r * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
+  const uint32_t x_voff = ((uint32_t)r * (uint32_t)k + (uint32_t)(8 * WPL * c)) * 2u;
+  int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;
+  auto issue = [&](int slot) {
+    const int jj = i_j < ng ? i_j : ng - 1;
+    const uint32_t wso = ((uint32_t)i_blk * 16u * (uint32_t)kw_row + (uint32_t)(jj * LPG)) * 4u;
+    buf_words<WPL>(rs_w, w_voff, wso, wq[slot]);
+#pragma unroll
+    for (int tc = 0; tc < TC; ++tc) {
+      const uint32_t xso = ((uint32_t)tc * 16u * (uint32_t)k + (uint32_t)(jj * G)) * 2u;
+#pragma unroll
+      for (int i = 0; i < WPL; ++i)
+        xq[slot][tc][i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, x_voff + 16u * i, xso, 0));
+    }
+    if (i_left > 1) {
+      --i_left;
+      if (++i_j == je) { i_j = jb; i_blk += grid; }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(p);
+
+  // ---- 4. scale|zero words into LDS as [block][group][column]
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    const int o = tid + i * kSk16Threads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      const uint32_t sw[4] = {sz_s[i].x, sz_s[i].y, sz_s[i].z, sz_s[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = oct * 8 + e;
+        if (j < ng)
+          szw[((size_t)bs * ng + j) * 16 + row] =
+              ((sw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) | (((sz_z[i] >> (4 * e)) & 0xFu) << 16);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);      // the inv_s copies have landed
+  __syncthreads();
+
+  const UnpackConsts uc = unpack_consts();
+  const int reducer = W - 1;
+  floatx4_t acc[TC];
+#pragma unroll
+  for (int tc = 0; tc < TC; ++tc) acc[tc] = floatx4_t{};
+  int blocks_done = 0;
+  auto finish_block = [&]() {
+    floatx4_t* rb = red + (size_t)(blocks_done & 1) * W * TC * 64;
+#pragma unroll
+    for (int tc = 0; tc < TC; ++tc) {
+      rb[(wave * TC + tc) * 64 + lane] = acc[tc];
+      acc[tc] = floatx4_t{};
+    }
+    __syncthreads();
+    if (wave == reducer) {
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc) {
+        floatx4_t sacc = rb[tc * 64 + lane];
+#pragma unroll
+        for (int wv = 1; wv < W; ++wv) sacc += rb[(wv * TC + tc) * 64 + lane];
+        ybuf[((size_t)blocks_done * TC + tc) * 64 + lane] = sacc;
+      }
+    }
+    ++blocks_done;
+  };
+  int c_j = jb, c_left = total;
+  auto consume = [&](int p, bool guarded) {   // guarded only in the tail (see the GEMV)
+    if (!guarded || c_left > 0) {
+      const int j = c_j;
+      const uint32_t szv = szw[((size_t)blocks_done * ng + j) * 16 + r];
+      const float d = h2f((uint16_t)szv), z = (float)(szv >> 16);
+      const half2_t dd = {(half_t)d, (half_t)d};
+      const half2_t o1024 = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};
+      const half2_t o64 = {(half_t)(-64.0f - z), (half_t)(-64.0f - z)};
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        // B: the 8 weights of word i, fp16_rn((q - z) D) in unpack order
+        uint32_t u[4];
+        unpack_word(wq[p][i], u, uc);
+        const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024) * dd;
+        const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64) * dd;
+        const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024) * dd;
+        const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64) * dd;
+        const half8_t bop = __builtin_bit_cast(
+            half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+                                __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)));
+        // inv_s of the same 8 channels
+        const uint4 sv = has_inv ? *reinterpret_cast<const uint4*>(inv_l + j * G + 8 * (WPL * c + i))
+                                 : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+#pragma unroll
+        for (int tc = 0; tc < TC; ++tc) {
+          const uint4 xv = xq[p][tc][i];
+          const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, sv.x));
+          const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
+          const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
+          const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.w) * __builtin_bit_cast(half2_t, sv.w));
+          // channels (k0..k7) -> unpack order (k0, k4, k1, k5, k2, k6, k3, k7)
+          const uint4 av = make_uint4(__builtin_amdgcn_perm(p2, p0, 0x05040100u),
+                                      __builtin_amdgcn_perm(p2, p0, 0x07060302u),
+                                      __builtin_amdgcn_perm(p3, p1, 0x05040100u),
+                                      __builtin_amdgcn_perm(p3, p1, 0x07060302u));
+          acc[tc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bop,
+                                                           acc[tc], 0, 0, 0);
+        }
+      }
+      --c_left;
+      if (++c_j == je) {
+        finish_block();
+        c_j = jb;
+      }
+    }
+  };
+  if (cnt > 0) {
+    int left = total;
+    while (true) {
+      if (left > PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(PF + p);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(p, false);
+        left -= PF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(p, true);
+        break;
+      }
+      if (left > PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(p);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(PF + p, false);
+        left -= PF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(PF + p, true);
+        break;
+      }
+    }
+  } else {
+    for (int bi = 0; bi < my_blocks; ++bi) finish_block();
+  }
+
+  // ---- outputs: lane (c, r) holds tokens 16 tc + 4c + e of column r
+  if (wave == reducer) {
+    for (int bi = 0; bi < my_blocks; ++bi) {
+      const int64_t col = ((int64_t)blockIdx.x + (int64_t)bi * grid) * 16 + r;
+#pragma unroll
+      for (int tc = 0; tc < TC; ++tc) {
+        const floatx4_t v = ybuf[((size_t)bi * TC + tc) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = (int64_t)tc * 16 + 4 * c + e;
+          if (t < m && col < n) y[t * n + col] = f2h_rn(v[e]);
+        }
+      }
+    }
+  }
+}
+
+// LDS of the fused skinny kernel: inv_s (rounded up to whole 1 KiB copies),
+// scale|zero words [nb][ng][16], reduction rows [2][8][tc][64] float4,
+// outputs [nb][tc][64] float4.
+size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
+  const size_t ng = (size_t)(k / g);
+  const size_t inv = ((size_t)k * 2 + 1023) & ~(size_t)1023;
+  return inv + (size_t)nb * ng * 16 * 4 + (size_t)2 * kSk16Waves * tc * 64 * 16 +
+         (size_t)nb * tc * 64 * 16;
 }
 
 // ---------------------------------------------------------------- prefill GEMM
@@ -955,6 +1543,83 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
           hipLaunchKernelGGL((linear_gemv_kernel<G, false, 8>), gd, bd, lds, stream, x, inv_s16,
                              qweight, scales, qzeros, n, k, y);
       }
+      return hipGetLastError();
+    }
+  }
+  // skinny 2 <= m <= 16: one fused kernel when its LDS plan fits
+  if (m >= 2 && m <= 16) {
+    const int tcs = 1;
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
+    const int64_t nblk = (n + 15) / 16;
+    int nb_cap = kGemvMaxBlk;
+    while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * kSk16Threads ||
+                          skinny_fused_lds_bytes(k, G, nb_cap, tcs) > 160 * 1024))
+      --nb_cap;
+    if (nb_cap > 0) {
+      int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)skinny_fused_lds_bytes(k, G, nb_cap, tcs);
+      per_cu = per_cu < 2 ? per_cu : 2;
+      const int64_t slots = (int64_t)kGemvCUs * per_cu;
+      int64_t grid = nblk < slots ? nblk : slots;
+      const int64_t need = (nblk + nb_cap - 1) / nb_cap;
+      grid = grid > need ? grid : need;
+      const int nb = (int)((nblk + grid - 1) / grid);
+      const size_t lds = skinny_fused_lds_bytes(k, G, nb, tcs);
+      const bool szv = (ng_all % 8 == 0) && (reinterpret_cast<uintptr_t>(scales) % 16 == 0);
+      const dim3 gd((unsigned)grid), bd(kSk16Threads);
+#define AWQ_SKF(TCC, SZ, PFF)                                                                  \
+  {                                                                                            \
+    const void* fn_ = reinterpret_cast<const void*>(&linear_skinny_fused_kernel<G, TCC, SZ, PFF>); \
+    if (lds > 65536) {                                                                         \
+      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((linear_skinny_fused_kernel<G, TCC, SZ, PFF>), gd, bd, lds, stream, x,   \
+                       inv_s16, qweight, scales, qzeros, m, n, k, y);                          \
+  }
+      if (szv) AWQ_SKF(1, true, 2) else AWQ_SKF(1, false, 2)
+#undef AWQ_SKF
+      return hipGetLastError();
+    }
+  }
+  // 16 < m <= 32: prep16 + skinny16 when its LDS plan fits (with 32 tokens the
+  // activation operand formed once per call beats forming it per item)
+  if (m > 16 && m <= 32) {
+    const int tcs = 2;
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
+    const int64_t nblk = (n + 15) / 16;
+    int nb_cap = kGemvMaxBlk;
+    while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * kSk16Threads ||
+                          skinny16_lds_bytes(k, G, nb_cap, tcs) > 160 * 1024))
+      --nb_cap;
+    if (nb_cap > 0) {
+      int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)skinny16_lds_bytes(k, G, nb_cap, tcs);
+      per_cu = per_cu < 2 ? per_cu : 2;
+      const int64_t slots = (int64_t)kGemvCUs * per_cu;
+      int64_t grid = nblk < slots ? nblk : slots;
+      const int64_t need = (nblk + nb_cap - 1) / nb_cap;
+      grid = grid > need ? grid : need;
+      const int nb = (int)((nblk + grid - 1) / grid);
+      const size_t lds = skinny16_lds_bytes(k, G, nb, tcs);
+      const bool szv = (ng_all % 8 == 0) && (reinterpret_cast<uintptr_t>(scales) % 16 == 0);
+      char* sp16 = static_cast<char*>(scratch);
+      uint16_t* a16 = reinterpret_cast<uint16_t*>(sp16);
+      float2* tu16 = reinterpret_cast<float2*>(sp16 + align256((size_t)tcs * (size_t)k * 16 * 2));
+      const int64_t n_pairs = tcs * ng_all;
+      hipLaunchKernelGGL(linear_prep16_kernel<G>, dim3((unsigned)((n_pairs + 3) / 4)), dim3(256), 0,
+                         stream, x, inv_s16, m, k, n_pairs, a16, tu16);
+      const dim3 gd((unsigned)grid), bd(kSk16Threads);
+#define AWQ_SK16(SZ)                                                                           \
+  {                                                                                            \
+    const void* fn_ = reinterpret_cast<const void*>(&linear_skinny16_kernel<G, 2, SZ, 1>);      \
+    if (lds > 65536) {                                                                         \
+      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((linear_skinny16_kernel<G, 2, SZ, 1>), gd, bd, lds, stream, a16, tu16,   \
+                       qweight, scales, qzeros, m, n, k, y);                                   \
+  }
+      if (szv) AWQ_SK16(true) else AWQ_SK16(false)
+#undef AWQ_SK16
       return hipGetLastError();
     }
   }
