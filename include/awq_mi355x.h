@@ -158,8 +158,11 @@ awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n,
  *   5e-3 * max(|y_ref|, rms of the row of y_ref) per output.
  *   x        [m][k] fp16, 16-byte aligned;  inv_s16 [k] fp16 or NULL;
  *   qweight/scales/qzeros in layout v1 (awq_pack_int4);  y [m][n] fp16 out.
- *   m = 1..8 runs the decode kernel (GEMV mode); m = 9..32 the same kernel
- *   over token chunks; m > 32 the prefill GEMM.  Both dequantize in-kernel.
+ *   m = 1 runs the decode GEMV; 2 <= m <= 16 one fused skinny kernel;
+ *   17 <= m <= 32 a small activation-staging kernel and a skinny kernel
+ *   (GEMV mode); m > 32 the prefill GEMM.  Shapes whose activations or
+ *   scale rows do not fit LDS for these take a staged two-kernel decode
+ *   path.  Every path dequantizes in-kernel.
  *   The library keeps one device scratch buffer per device for the staged
  *   activations (grown on demand with hipMalloc, never freed); calls that
  *   overlap on one device from different host threads must be serialised
