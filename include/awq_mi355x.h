@@ -176,6 +176,41 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight,
                             const uint16_t* inv_s16, int64_t m, int64_t n,
                             int64_t k, int32_t g, uint16_t* y, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * awq_linear_w4a16_group -- independent linears of one decode step in one
+ * launch.
+ * Passage: as awq_linear_w4a16 (bjdmk.com.cn page, section "量化参数配置":
+ * GEMV mode for batch-1 decode).  In a decoder layer the q, k and v
+ * projections read the same input and do not depend on one another, and so
+ * do gate and up; one launch for such a group saves the fixed launch and
+ * ramp time of the others.
+ *
+ *   items    host array of `count` (1..4) linears with the same m, k and g:
+ *            x [m][k] fp16 (16-byte aligned), inv_s16 [k] fp16 or NULL,
+ *            qweight [n][k/8] (16-byte aligned), scales [n][k/g],
+ *            qzeros [n][ceil(k/(8g))] in layout v1, y [m][n] fp16 out, n.
+ *            The linears may share x; no y may overlap an x, a packed
+ *            tensor, an inv_s16 or another y of the group.
+ *   Every y holds exactly the bits awq_linear_w4a16 writes for that linear
+ *   alone (the arithmetic of a column block does not depend on the launch).
+ *   m = 1 and 2 <= m <= 16 run the whole group in one launch of the decode
+ *   GEMV or of the fused skinny kernel when their shared-memory plans fit
+ *   the k; otherwise the linears run one after another on the stream.
+ *   Limits: those of awq_linear_w4a16 for every linear; 1 <= count <= 4.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const uint16_t* x;
+  const uint16_t* inv_s16;
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint32_t* qzeros;
+  uint16_t* y;
+  int64_t n;
+} awq_linear_item;
+
+awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count,
+                                  int64_t m, int64_t k, int32_t g, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

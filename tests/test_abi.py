@@ -150,3 +150,28 @@ def test_product_package_never_imports_the_oracle():
             text = f.read_text()
             assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), f
             assert "awq_oracle" not in text, f
+
+
+def _items(count, **over):
+    from weight_only_int4_awq_amd import _lib
+    arr = (_lib.LinearItem * max(count, 1))()
+    for i in range(max(count, 1)):
+        a = arr[i]
+        a.x = a.qweight = a.scales = a.qzeros = a.y = FAKE
+        a.inv_s16 = None
+        a.n = 64
+        for key, val in over.items():
+            setattr(a, key, val)
+    return arr
+
+
+def test_linear_group_argument_errors(lib):
+    assert _status(lib, "awq_linear_w4a16_group", None, 1, 1, 256, 128, None)[0] == 1
+    assert _status(lib, "awq_linear_w4a16_group", _items(1), 0, 1, 256, 128, None)[0] == 2
+    assert _status(lib, "awq_linear_w4a16_group", _items(5), 5, 1, 256, 128, None)[0] == 2
+    assert _status(lib, "awq_linear_w4a16_group", _items(2, y=None), 2, 1, 256, 128, None)[0] == 1
+    assert _status(lib, "awq_linear_w4a16_group", _items(2, n=0), 2, 1, 256, 128, None)[0] == 2
+    assert _status(lib, "awq_linear_w4a16_group", _items(2), 2, 1, 200, 128, None)[0] == 2
+    assert _status(lib, "awq_linear_w4a16_group", _items(2), 2, 0, 256, 128, None)[0] == 2
+    st, msg = _status(lib, "awq_linear_w4a16_group", _items(2, x=MISALIGNED), 2, 1, 256, 128, None)
+    assert st == 3 and "awq_linear_w4a16_group" in msg

@@ -328,3 +328,68 @@ def test_linear_decode_multiblock(P, n, k, g):
     xc = S.activations(64, k, 453, S.outlier_channels(k, 0.01, 452), 20.0)
     s16 = O.scale_candidate(O.calib_stats(xc), 0.3)
     _check_linear(P, w, x, s16, g)
+
+
+# ----------------------------------------------------------------- linear groups
+
+
+def _group_case(P, m, k, g, specs, seed):
+    """Linears (n, alpha or None, seed) reading two inputs; returns the group
+    items and, per linear, its host packed tensors, inv_s16 and input."""
+    xa = S.activations(m, k, seed, S.outlier_channels(k, 0.01, seed + 1), 20.0)
+    xb = S.activations(m, k, seed + 2, S.outlier_channels(k, 0.01, seed + 1), 20.0)
+    xs = [(dev(xa), xa), (dev(xb), xb)]
+    items, meta = [], []
+    for i, (n, alpha, sd) in enumerate(specs):
+        w = S.weights(n, k, 0.02, sd)
+        if alpha is None:
+            s16 = inv = None
+        else:
+            xc = S.activations(64, k, sd + 1, S.outlier_channels(k, 0.01, sd + 2), 20.0)
+            s16 = O.scale_candidate(O.calib_stats(xc), alpha)
+            inv = O.fp16_rn(1.0 / s16.astype(np.float64))
+        qw, sc, qz, _ = P.awq_pack_int4(dev(w), None if s16 is None else dev(s16), g=g)
+        del w
+        x_d, x_h = xs[i % 2]
+        inv_d = None if inv is None else dev(inv)
+        items.append((x_d, qw, sc, qz, inv_d, None))
+        meta.append((x_d, x_h, qw, sc, qz, inv, inv_d))
+    return items, meta
+
+
+def _check_group(P, items, meta, k, g, cols_per=None):
+    ys = P.awq_linear_w4a16_group(items, g=g)
+    for y, (x_d, x_h, qw, sc, qz, inv, inv_d) in zip(ys, meta):
+        y1 = P.awq_linear_w4a16(x_d, qw, sc, qz, inv_d, g=g)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+        n = qw.shape[0]
+        hq, hs, hz = host_u32(qw), sc.cpu().numpy(), host_u32(qz)
+        if cols_per is None or n <= cols_per:
+            yr = O.linear_ref(x_h, hq, hs, hz, inv, k, g)
+            ok, worst, raw = O.check_linear(host16(y), yr)
+        else:
+            cols = np.sort(np.random.Generator(np.random.PCG64(n + 5)).choice(n, cols_per, replace=False))
+            yr = O.linear_ref_rows(x_h, hq, hs, hz, inv, k, g, cols)
+            ok, worst, raw = O.check_linear(host16(y)[:, cols], yr)
+        assert ok, (n, worst, raw)
+
+
+@pytest.mark.parametrize("m", [1, 8, 24, 40])
+@pytest.mark.parametrize("g", [128, 64])
+def test_linear_group_matches_single_and_oracle(P, m, g):
+    # m = 1 and m = 8: one grouped launch; m = 24 and 40: one launch per linear
+    specs = [(1000, 0.5, 460), (256, 0.3, 470), (264, None, 480), (16, 0.4, 490)]
+    items, meta = _group_case(P, m, 2048, g, specs, 461 + m)
+    _check_group(P, items, meta, 2048, g)
+    _check_group(P, items[1:3], meta[1:3], 2048, g)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_linear_group_llama3_8b_full_size_sampled(P, m):
+    qkv = [(4096, 0.5, 500), (1024, 0.4, 510), (1024, 0.45, 520)]
+    items, meta = _group_case(P, m, 4096, 128, qkv, 530 + m)
+    _check_group(P, items, meta, 4096, 128, cols_per=128)
+    gate_up = [(14336, 0.5, 540), (14336, 0.35, 550)]
+    items, meta = _group_case(P, m, 4096, 128, gate_up, 560 + m)
+    _check_group(P, items, meta, 4096, 128, cols_per=128)

@@ -10,6 +10,7 @@ the library's HIP kernels; there is no fallback.
     awq_search_scale(w, x, mean_abs, g, n_grid) -> (best_idx int32 [1], s16, inv_s16, losses)
     awq_pack_int4(w, s16, g)                    -> (qweight, scales, qzeros, nonfinite int32 [1])
     awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16, g) -> y fp16 [m, n]
+    awq_linear_w4a16_group([(x, qweight, scales, qzeros, inv_s16, out), ...], g) -> [y, ...]
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ from . import _lib
 from ._lib import AWQError  # noqa: F401
 
 __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_pack_int4",
-           "awq_linear_w4a16", "AWQError", "load"]
+           "awq_linear_w4a16", "awq_linear_w4a16_group", "AWQError", "load"]
 
 
 def load():
@@ -162,3 +163,42 @@ def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
                                       _ptr(inv_s16), m, n, k, g, _ptr(y), _stream())
     _lib.check("awq_linear_w4a16", st)
     return y
+
+
+def awq_linear_w4a16_group(items, g=128):
+    """Independent linears with the same m and k (q, k, v of a layer; gate and
+    up) in one call.  ``items`` holds up to four tuples (x, qweight, scales,
+    qzeros, inv_s16, out) with x fp16 [m, k] and out fp16 [m, n] or None.
+    Returns the list of outputs; each equals awq_linear_w4a16 of that linear."""
+    torch = _torch()
+    if not 1 <= len(items) <= 4:
+        raise ValueError("a group holds 1 to 4 linears")
+    arr = (_lib.LinearItem * len(items))()
+    outs = []
+    m = k = None
+    for i, (x, qweight, scales, qzeros, inv_s16, out) in enumerate(items):
+        _dev_tensor(x, torch.float16, "x", 2)
+        _dev_tensor(qweight, torch.int32, "qweight", 2)
+        _dev_tensor(scales, torch.float16, "scales", 2)
+        _dev_tensor(qzeros, torch.int32, "qzeros", 2)
+        mi, ki = x.shape
+        if m is None:
+            m, k = mi, ki
+        elif (mi, ki) != (m, k):
+            raise ValueError("the linears of a group must share m and k")
+        n = qweight.shape[0]
+        if qweight.shape[1] * 8 != k or scales.shape != (n, k // g) or qzeros.shape != (n, -(-k // (8 * g))):
+            raise ValueError(f"linear {i}: packed tensors do not match x and g")
+        if inv_s16 is not None:
+            _dev_tensor(inv_s16, torch.float16, "inv_s16", 1)
+            if inv_s16.shape[0] != k:
+                raise ValueError(f"linear {i}: inv_s16 must have k entries")
+        y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
+        _out_tensor(y, torch.float16, (m, n), "y")
+        a = arr[i]
+        a.x, a.inv_s16, a.qweight = _ptr(x), _ptr(inv_s16), _ptr(qweight)
+        a.scales, a.qzeros, a.y, a.n = _ptr(scales), _ptr(qzeros), _ptr(y), n
+        outs.append(y)
+    st = _lib.load().awq_linear_w4a16_group(arr, len(items), m, k, g, _stream())
+    _lib.check("awq_linear_w4a16_group", st)
+    return outs

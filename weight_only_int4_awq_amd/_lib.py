@@ -29,6 +29,18 @@ SIGNATURES = {
                                    C.c_void_p]),
 }
 
+
+
+class LinearItem(C.Structure):
+    """awq_linear_item of the C header."""
+    _fields_ = [("x", C.c_void_p), ("inv_s16", C.c_void_p), ("qweight", C.c_void_p),
+                ("scales", C.c_void_p), ("qzeros", C.c_void_p), ("y", C.c_void_p),
+                ("n", C.c_int64)]
+
+
+SIGNATURES["awq_linear_w4a16_group"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                                  C.c_int32, C.c_void_p])
+
 _lib = None
 
 

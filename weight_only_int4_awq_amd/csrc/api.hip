@@ -123,28 +123,91 @@ awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n, int6
   return AWQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// checks shared by awq_linear_w4a16 and awq_linear_w4a16_group
+awq_status check_linear_args(const char* fn, const uint16_t* x, const uint32_t* qweight,
+                             const uint16_t* scales, const uint32_t* qzeros,
+                             const uint16_t* inv_s16, int64_t m, int64_t n, int64_t k, int32_t g,
+                             const uint16_t* y) {
+  if (!x || !qweight || !scales || !qzeros || !y) {
+    snprintf(g_err, sizeof(g_err), "%s: null pointer", fn);
+    return AWQ_ERR_NULL;
+  }
+  if (!group_ok(g)) {
+    snprintf(g_err, sizeof(g_err), "%s: g=%lld not in {32,64,128}", fn, (long long)g);
+    return AWQ_ERR_SHAPE;
+  }
+  if (k < 64 || k % g != 0 || k % 64 != 0) {
+    snprintf(g_err, sizeof(g_err), "%s: k=%lld must be a multiple of g=%lld and of 64", fn, (long long)k,
+             (long long)g);
+    return AWQ_ERR_SHAPE;
+  }
+  if (m < 1 || m > 0x7FFFFFFF) {
+    snprintf(g_err, sizeof(g_err), "%s: m=%lld out of range", fn, (long long)m);
+    return AWQ_ERR_SHAPE;
+  }
+  if (n < 1 || n > 0x7FFFFFFF) {
+    snprintf(g_err, sizeof(g_err), "%s: n=%lld out of range", fn, (long long)n);
+    return AWQ_ERR_SHAPE;
+  }
+  if (!aligned(x, 16) || !aligned(qweight, 16)) {
+    snprintf(g_err, sizeof(g_err), "%s: x and qweight must be 16-byte aligned", fn);
+    return AWQ_ERR_ALIGN;
+  }
+  if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2) || (inv_s16 && !aligned(inv_s16, 2))) {
+    snprintf(g_err, sizeof(g_err), "%s: misaligned pointer", fn);
+    return AWQ_ERR_ALIGN;
+  }
+  if ((unsigned long long)n * (unsigned long long)k / 2 >= (1ull << 32)) {
+    snprintf(g_err, sizeof(g_err), "%s: packed weights of n=%lld x k=%lld exceed 4 GiB", fn, (long long)n,
+             (long long)k);
+    return AWQ_ERR_SHAPE;
+  }
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                             const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
                             int64_t k, int32_t g, uint16_t* y, void* stream) {
   g_err[0] = 0;
-  if (!x || !qweight || !scales || !qzeros || !y) return fail(AWQ_ERR_NULL, "awq_linear_w4a16: null pointer");
-  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: g=%lld not in {32,64,128}", g);
-  if (k < 64 || k % g != 0 || k % 64 != 0)
-    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: k=%lld must be a multiple of g=%lld and of 64", k, g);
-  if (m < 1 || m > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: m=%lld out of range", m);
-  if (n < 1 || n > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: n=%lld out of range", n);
-  if (!aligned(x, 16) || !aligned(qweight, 16))
-    return fail(AWQ_ERR_ALIGN, "awq_linear_w4a16: x and qweight must be 16-byte aligned");
-  if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2) || (inv_s16 && !aligned(inv_s16, 2)))
-    return fail(AWQ_ERR_ALIGN, "awq_linear_w4a16: misaligned pointer");
-  if ((unsigned long long)n * (unsigned long long)k / 2 >= (1ull << 32))
-    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16: packed weights of n=%lld x k=%lld exceed 4 GiB", n, k);
+  awq_status st0 = check_linear_args("awq_linear_w4a16", x, qweight, scales, qzeros, inv_s16, m, n, k,
+                                     g, y);
+  if (st0 != AWQ_OK) return st0;
   void* scratch = nullptr;
   awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g), &scratch);
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, scratch,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16 launch");
+  return AWQ_OK;
+}
+
+awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count, int64_t m, int64_t k,
+                                  int32_t g, void* stream) {
+  g_err[0] = 0;
+  if (!items) return fail(AWQ_ERR_NULL, "awq_linear_w4a16_group: null items");
+  if (count < 1 || count > awq::kGroupMax)
+    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16_group: count=%lld outside 1..%lld", count, awq::kGroupMax);
+  awq::LinItem li[awq::kGroupMax];
+  for (int32_t i = 0; i < count; ++i) {
+    const awq_linear_item& it = items[i];
+    awq_status st = check_linear_args("awq_linear_w4a16_group", it.x, it.qweight, it.scales, it.qzeros,
+                                      it.inv_s16, m, it.n, k, g, it.y);
+    if (st != AWQ_OK) return st;
+    li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
+  }
+  void* scratch = nullptr;
+  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g), &scratch);
+  if (st != AWQ_OK) return st;
+  hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group launch");
   return AWQ_OK;
 }
 

@@ -31,6 +31,21 @@ hipError_t launch_pack(const uint16_t* w, const uint16_t* s16, int64_t n, int64_
                        int32_t g, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
                        int32_t* nonfinite, hipStream_t stream);
 
+// Most linears one grouped decode launch takes.
+constexpr int kGroupMax = 4;
+
+// One linear of a group (device pointers, validated by the caller): x [m][k],
+// inv_s16 [k] or null, packed weights in layout v1, y [m][n].
+struct LinItem {
+  const uint16_t* x;
+  const uint16_t* inv;
+  const uint32_t* qw;
+  const uint16_t* sc;
+  const uint32_t* qz;
+  uint16_t* y;
+  int64_t n;
+};
+
 // Scratch bytes the linear needs for the staged activations.
 size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g);
 
@@ -38,5 +53,11 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint1
                          const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
                          int64_t n, int64_t k, int32_t g, uint16_t* y, void* scratch,
                          hipStream_t stream);
+
+// 1..kGroupMax independent linears of the same m, k and g: one launch for the
+// decode kernels that take groups, consecutive launches otherwise.  Each y
+// holds the bits launch_linear writes for that linear alone.
+hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
+                               void* scratch, hipStream_t stream);
 
 }  // namespace awq

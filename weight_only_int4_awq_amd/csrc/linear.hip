@@ -198,6 +198,52 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
 }
 
 
+// ---------------------------------------------------------------- linear groups
+// The decode kernels take up to kGroupMax independent linears of the same k
+// (and m) in one launch: work-groups [wg0[l], wg0[l + 1]) serve linear l,
+// each exactly as a launch of that linear alone with wg0[l + 1] - wg0[l]
+// work-groups would (the arithmetic of a column block does not depend on the
+// grid, so the outputs are the same bits).
+struct LinGroup {
+  const uint16_t* x[kGroupMax];
+  const uint16_t* inv[kGroupMax];
+  const uint32_t* qw[kGroupMax];
+  const uint16_t* sc[kGroupMax];
+  const uint32_t* qz[kGroupMax];
+  uint16_t* y[kGroupMax];
+  int64_t n[kGroupMax];
+  int32_t wg0[kGroupMax + 1];
+  int32_t count;
+};
+struct LinPick {
+  const uint16_t* x;
+  const uint16_t* inv;
+  const uint32_t* qw;
+  const uint16_t* sc;
+  const uint32_t* qz;
+  uint16_t* y;
+  int64_t n;
+  int bid, grid;
+};
+__device__ __forceinline__ LinPick pick_linear(const LinGroup& gp) {
+  const int b = (int)blockIdx.x;
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kGroupMax; ++i)
+    if (i < gp.count && b >= gp.wg0[i]) li = i;
+  LinPick L;
+  L.x = gp.x[li];
+  L.inv = gp.inv[li];
+  L.qw = gp.qw[li];
+  L.sc = gp.sc[li];
+  L.qz = gp.qz[li];
+  L.y = gp.y[li];
+  L.n = gp.n[li];
+  L.bid = b - gp.wg0[li];
+  L.grid = gp.wg0[li + 1] - gp.wg0[li];
+  return L;
+}
+
 // ---------------------------------------------------------------- decode GEMV (m = 1)
 // Work-groups of W = 8 or 16 waves (16 where one work-group per CU is all
 // that fits or is needed, so that as many weight bytes are in flight per CU);
@@ -253,10 +299,11 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
 // SZV: the scale rows are 16-byte aligned octets (k / g a multiple of 8 and an
 // aligned base), read with one 16-byte load per octet.
 template <int G, bool SZV, int W>
-__global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
+__device__ __forceinline__ void gemv_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, int64_t n, int64_t k, uint16_t* __restrict__ y) {
+    const uint32_t* __restrict__ qzeros, int64_t n, int64_t k, uint16_t* __restrict__ y,
+    int bid, int grid_in) {
   constexpr int WPL = G / 32;            // qweight words per lane per group
   constexpr int HPL = G / 4;             // staged halves per (group, lane group, row)
   constexpr int LPG = G / 8;             // words per group
@@ -265,8 +312,8 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int ng = (int)(k / G);
   const int nblk = (int)((n + 15) / 16);
-  const int grid = (int)gridDim.x;
-  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // 1 .. kGemvMaxBlk
+  const int grid = grid_in;
+  const int my_blocks = (nblk - bid + grid - 1) / grid;   // 1 .. kGemvMaxBlk
   unsigned char* sp = smem;
   uint16_t* xa = reinterpret_cast<uint16_t*>(sp);          sp += (size_t)k * 4;     // [ng][4][2][HPL]
   float4* tu = reinterpret_cast<float4*>(sp);              sp += (size_t)ng * 16;   // (T_hi, U_hi, T_lo, U_lo)
@@ -300,7 +347,7 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
     if (o < n_oct) {
       const int row_all = o / nzw, oct = o - row_all * nzw;
       const int bs = row_all >> 4, row = row_all & 15;
-      int col = ((int)blockIdx.x + bs * grid) * 16 + row;
+      int col = (bid + bs * grid) * 16 + row;
       col = col < (int)n ? col : (int)n - 1;
       const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
       if constexpr (SZV) {
@@ -344,7 +391,7 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
   // clamped), and the (block, group) cursors advance in scalar registers.
   uint32_t wq[2 * kGemvPF][WPL];
   const char* qbase = reinterpret_cast<const char*>(qweight);
-  int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;    // issue cursor
+  int i_blk = bid, i_j = jb, i_left = total;    // issue cursor
   auto issue = [&](int slot) {
     int col = i_blk * 16 + r;
     col = col < (int)n ? col : (int)n - 1;
@@ -544,12 +591,17 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(
   // ---- outputs: the reducer wave wrote every row of ybuf itself
   if (wave == reducer && lane < 16) {
     for (int bi = 0; bi < my_blocks; ++bi) {
-      const int64_t col = ((int64_t)blockIdx.x + (int64_t)bi * grid) * 16 + lane;
+      const int64_t col = ((int64_t)bid + (int64_t)bi * grid) * 16 + lane;
       if (col < n) y[col] = f2h_rn(ybuf[bi * 16 + lane]);
     }
   }
 }
 
+template <int G, bool SZV, int W>
+__global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(const LinGroup gp, int64_t k) {
+  const LinPick L = pick_linear(gp);
+  gemv_body<G, SZV, W>(L.x, L.inv, L.qw, L.sc, L.qz, L.n, k, L.y, L.bid, L.grid);
+}
 
 // ---------------------------------------------------------------- skinny, 2 <= m <= 32
 // linear_prep16 writes x_tilde = fp16_rn(x * inv_s) once per call as the MFMA
@@ -864,18 +916,18 @@ __global__ __launch_bounds__(kSk16Threads, 4) void linear_skinny16_kernel(
 // The weights are dequantized in registers to fp16_rn((q - z) D) as in the
 // prefill GEMM, so the MFMA accumulates whole groups with no offset sums.
 template <int G, int TC, bool SZV, int PF>
-__global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(
+__device__ __forceinline__ void skinny_fused_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, int bid, int grid_in) {
   constexpr int WPL = G / 32, LPG = G / 8;
   constexpr int W = kSk16Waves;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int ng = (int)(k / G);
   const int nblk = (int)((n + 15) / 16);
-  const int grid = (int)gridDim.x;
-  const int my_blocks = (nblk - (int)blockIdx.x + grid - 1) / grid;   // 1 .. kGemvMaxBlk
+  const int grid = grid_in;
+  const int my_blocks = (nblk - bid + grid - 1) / grid;   // 1 .. kGemvMaxBlk
   const size_t inv_bytes = ((size_t)k * 2 + 1023) & ~(size_t)1023;
   unsigned char* sp = smem;
   uint16_t* inv_l = reinterpret_cast<uint16_t*>(sp);  sp += inv_bytes;
@@ -920,7 +972,7 @@ __global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(
     if (o < n_oct) {
       const int row_all = o / nzw, oct = o - row_all * nzw;
       const int bs = row_all >> 4, row = row_all & 15;
-      int col = ((int)blockIdx.x + bs * grid) * 16 + row;
+      int col = (bid + bs * grid) * 16 + row;
       col = col < (int)n ? col : (int)n - 1;
       const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
       if constexpr (SZV) {
@@ -944,7 +996,7 @@ __global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(
   const __amdgpu_buffer_rsrc_t rs_x = buf_rsrc(x, (uint32_t)((uint64_t)m * (uint64_t)k * 2));
   const uint32_t w_voff = ((uint32_t)r * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
   const uint32_t x_voff = ((uint32_t)r * (uint32_t)k + (uint32_t)(8 * WPL * c)) * 2u;
-  int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;
+  int i_blk = bid, i_j = jb, i_left = total;
   auto issue = [&](int slot) {
     const int jj = i_j < ng ? i_j : ng - 1;
     const uint32_t wso = ((uint32_t)i_blk * 16u * (uint32_t)kw_row + (uint32_t)(jj * LPG)) * 4u;
@@ -1090,7 +1142,7 @@ __global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(
   // ---- outputs: lane (c, r) holds tokens 16 tc + 4c + e of column r
   if (wave == reducer) {
     for (int bi = 0; bi < my_blocks; ++bi) {
-      const int64_t col = ((int64_t)blockIdx.x + (int64_t)bi * grid) * 16 + r;
+      const int64_t col = ((int64_t)bid + (int64_t)bi * grid) * 16 + r;
 #pragma unroll
       for (int tc = 0; tc < TC; ++tc) {
         const floatx4_t v = ybuf[((size_t)bi * TC + tc) * 64 + lane];
@@ -1107,6 +1159,14 @@ __global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(
 // LDS of the fused skinny kernel: inv_s (rounded up to whole 1 KiB copies),
 // scale|zero words [nb][ng][16], reduction rows [2][8][tc][64] float4,
 // outputs [nb][tc][64] float4.
+
+template <int G, int TC, bool SZV, int PF>
+__global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(const LinGroup gp,
+                                                                              int64_t m, int64_t k) {
+  const LinPick L = pick_linear(gp);
+  skinny_fused_body<G, TC, SZV, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid);
+}
+
 size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
   const size_t ng = (size_t)(k / g);
   const size_t inv = ((size_t)k * 2 + 1023) & ~(size_t)1023;
@@ -1371,11 +1431,66 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
       }
 }
 
+// Work-groups of a group launch: the grid one launch of all the column blocks
+// would take (fill the chip first, then at most nb_cap blocks per
+// work-group), split over the linears in proportion to their blocks.  For a
+// single linear this is that launch's grid.  Returns the most blocks any
+// work-group gets.
+static int split_group_grid(const LinItem* items, int count, int64_t slots, int nb_cap,
+                            LinGroup& gp) {
+  int64_t nblk[kGroupMax], total = 0;
+  for (int l = 0; l < count; ++l) {
+    nblk[l] = (items[l].n + 15) / 16;
+    total += nblk[l];
+  }
+  int64_t grid_total = total < slots ? total : slots;
+  const int64_t need = (total + nb_cap - 1) / nb_cap;
+  grid_total = grid_total > need ? grid_total : need;
+  int start = 0, nb = 1;
+  for (int l = 0; l < count; ++l) {
+    int64_t gl = grid_total * nblk[l] / total;
+    const int64_t need_l = (nblk[l] + nb_cap - 1) / nb_cap;
+    gl = gl > need_l ? gl : need_l;
+    gl = gl < nblk[l] ? gl : nblk[l];
+    gl = gl > 0 ? gl : 1;
+    gp.x[l] = items[l].x;
+    gp.inv[l] = items[l].inv;
+    gp.qw[l] = items[l].qw;
+    gp.sc[l] = items[l].sc;
+    gp.qz[l] = items[l].qz;
+    gp.y[l] = items[l].y;
+    gp.n[l] = items[l].n;
+    gp.wg0[l] = start;
+    start += (int)gl;
+    const int nbl = (int)((nblk[l] + gl - 1) / gl);
+    nb = nb > nbl ? nb : nbl;
+  }
+  for (int l = count; l < kGroupMax; ++l) {
+    gp.x[l] = nullptr; gp.inv[l] = nullptr; gp.qw[l] = nullptr; gp.sc[l] = nullptr;
+    gp.qz[l] = nullptr; gp.y[l] = nullptr; gp.n[l] = 0;
+  }
+  for (int l = count; l <= kGroupMax; ++l) gp.wg0[l] = start;
+  gp.count = count;
+  return nb;
+}
+
+static bool scales_octets(const LinItem* items, int count, int64_t ng) {
+  if (ng % 8 != 0) return false;
+  for (int l = 0; l < count; ++l)
+    if (reinterpret_cast<uintptr_t>(items[l].sc) % 16 != 0) return false;
+  return true;
+}
+
 template <int G>
-static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
-                                  const uint16_t* scales, const uint32_t* qzeros,
-                                  const uint16_t* inv_s16, int64_t m, int64_t n, int64_t k,
-                                  uint16_t* y, void* scratch, hipStream_t stream) {
+static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, void* scratch,
+                                    hipStream_t stream) {
+  const uint16_t* x = it.x;
+  const uint32_t* qweight = it.qw;
+  const uint16_t* scales = it.sc;
+  const uint32_t* qzeros = it.qz;
+  const uint16_t* inv_s16 = it.inv;
+  uint16_t* y = it.y;
+  const int64_t n = it.n;
   if (m > 32) {
     const size_t lds = gemm_lds_bytes(k, G);
     const size_t lds_static = (size_t)2 * kGemmBM * kGemmBK * 2;
@@ -1403,106 +1518,6 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
                          tiles_n);
     }
     return hipGetLastError();
-  }
-  // the fused decode kernel: at most kGemvMaxBlk column blocks per
-  // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
-  // thread) and whose LDS plan fits 160 KiB; other shapes take the staged
-  // two-kernel path below
-  if (m == 1) {
-    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
-    const int64_t nblk = (n + 15) / 16;
-    auto plan = [&](int waves, int& nb_cap, int64_t& per_cu) {
-      nb_cap = kGemvMaxBlk;
-      while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * waves * 64 ||
-                            gemv_lds_bytes(k, G, nb_cap, waves) > 160 * 1024))
-        --nb_cap;
-      per_cu = nb_cap > 0 ? (int64_t)(160 * 1024) / (int64_t)gemv_lds_bytes(k, G, nb_cap, waves) : 0;
-      const int64_t wg_cap = 16 / waves;            // 16 waves per CU (4 per SIMD)
-      per_cu = per_cu < wg_cap ? per_cu : wg_cap;
-    };
-    int nb_cap = 0;
-    int64_t per_cu = 0;
-    plan(8, nb_cap, per_cu);
-    int waves = 8;
-    // LDS leaves room for one 8-wave work-group per CU: 16 waves put twice
-    // the weight bytes in flight
-    if (nb_cap > 0 && per_cu < 2) {
-      int nb16 = 0;
-      int64_t pc16 = 0;
-      plan(16, nb16, pc16);
-      if (nb16 > 0 && pc16 >= 1) { waves = 16; nb_cap = nb16; per_cu = pc16; }
-    }
-    if (nb_cap > 0 && per_cu >= 1) {
-      const int64_t slots = (int64_t)kGemvCUs * per_cu;
-      // fill the chip first, then give each work-group up to nb_cap blocks
-      int64_t grid = nblk < slots ? nblk : slots;
-      const int64_t need = (nblk + nb_cap - 1) / nb_cap;
-      grid = grid > need ? grid : need;
-      const int nb = (int)((nblk + grid - 1) / grid);
-      const size_t lds = gemv_lds_bytes(k, G, nb, waves);
-      const bool szv = (ng_all % 8 == 0) && (reinterpret_cast<uintptr_t>(scales) % 16 == 0);
-      const void* fn =
-          waves == 16 ? (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 16>)
-                             : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 16>))
-                      : (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 8>)
-                             : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 8>));
-      if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-      }
-      const dim3 gd((unsigned)grid), bd((unsigned)(waves * 64));
-      if (waves == 16) {
-        if (szv)
-          hipLaunchKernelGGL((linear_gemv_kernel<G, true, 16>), gd, bd, lds, stream, x, inv_s16,
-                             qweight, scales, qzeros, n, k, y);
-        else
-          hipLaunchKernelGGL((linear_gemv_kernel<G, false, 16>), gd, bd, lds, stream, x, inv_s16,
-                             qweight, scales, qzeros, n, k, y);
-      } else {
-        if (szv)
-          hipLaunchKernelGGL((linear_gemv_kernel<G, true, 8>), gd, bd, lds, stream, x, inv_s16,
-                             qweight, scales, qzeros, n, k, y);
-        else
-          hipLaunchKernelGGL((linear_gemv_kernel<G, false, 8>), gd, bd, lds, stream, x, inv_s16,
-                             qweight, scales, qzeros, n, k, y);
-      }
-      return hipGetLastError();
-    }
-  }
-  // skinny 2 <= m <= 16: one fused kernel when its LDS plan fits
-  if (m >= 2 && m <= 16) {
-    const int tcs = 1;
-    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
-    const int64_t nblk = (n + 15) / 16;
-    int nb_cap = kGemvMaxBlk;
-    while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * kSk16Threads ||
-                          skinny_fused_lds_bytes(k, G, nb_cap, tcs) > 160 * 1024))
-      --nb_cap;
-    if (nb_cap > 0) {
-      int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)skinny_fused_lds_bytes(k, G, nb_cap, tcs);
-      per_cu = per_cu < 2 ? per_cu : 2;
-      const int64_t slots = (int64_t)kGemvCUs * per_cu;
-      int64_t grid = nblk < slots ? nblk : slots;
-      const int64_t need = (nblk + nb_cap - 1) / nb_cap;
-      grid = grid > need ? grid : need;
-      const int nb = (int)((nblk + grid - 1) / grid);
-      const size_t lds = skinny_fused_lds_bytes(k, G, nb, tcs);
-      const bool szv = (ng_all % 8 == 0) && (reinterpret_cast<uintptr_t>(scales) % 16 == 0);
-      const dim3 gd((unsigned)grid), bd(kSk16Threads);
-#define AWQ_SKF(TCC, SZ, PFF)                                                                  \
-  {                                                                                            \
-    const void* fn_ = reinterpret_cast<const void*>(&linear_skinny_fused_kernel<G, TCC, SZ, PFF>); \
-    if (lds > 65536) {                                                                         \
-      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-      if (e_ != hipSuccess) return e_;                                                         \
-    }                                                                                          \
-    hipLaunchKernelGGL((linear_skinny_fused_kernel<G, TCC, SZ, PFF>), gd, bd, lds, stream, x,   \
-                       inv_s16, qweight, scales, qzeros, m, n, k, y);                          \
-  }
-      if (szv) AWQ_SKF(1, true, 2) else AWQ_SKF(1, false, 2)
-#undef AWQ_SKF
-      return hipGetLastError();
-    }
   }
   // 16 < m <= 32: prep16 + skinny16 when its LDS plan fits (with 32 tokens the
   // activation operand formed once per call beats forming it per item)
@@ -1546,6 +1561,7 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
       return hipGetLastError();
     }
   }
+  // the staged two-kernel decode path (any m <= 32 whose plans above do not fit)
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / G;
   char* sp = static_cast<char*>(scratch);
@@ -1577,17 +1593,121 @@ static hipError_t launch_linear_g(const uint16_t* x, const uint32_t* qweight,
   return hipGetLastError();
 }
 
+template <int G>
+static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t m, int64_t k,
+                                        void* scratch, hipStream_t stream) {
+  // the decode GEMV (m = 1): at most kGemvMaxBlk column blocks per
+  // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
+  // thread) and whose LDS plan fits 160 KiB
+  if (m == 1) {
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
+    auto plan = [&](int waves, int& nb_cap, int64_t& per_cu) {
+      nb_cap = kGemvMaxBlk;
+      while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * waves * 64 ||
+                            gemv_lds_bytes(k, G, nb_cap, waves) > 160 * 1024))
+        --nb_cap;
+      per_cu = nb_cap > 0 ? (int64_t)(160 * 1024) / (int64_t)gemv_lds_bytes(k, G, nb_cap, waves) : 0;
+      const int64_t wg_cap = 16 / waves;            // 16 waves per CU (4 per SIMD)
+      per_cu = per_cu < wg_cap ? per_cu : wg_cap;
+    };
+    int nb_cap = 0;
+    int64_t per_cu = 0;
+    plan(8, nb_cap, per_cu);
+    int waves = 8;
+    // LDS leaves room for one 8-wave work-group per CU: 16 waves put twice
+    // the weight bytes in flight
+    if (nb_cap > 0 && per_cu < 2) {
+      int nb16 = 0;
+      int64_t pc16 = 0;
+      plan(16, nb16, pc16);
+      if (nb16 > 0 && pc16 >= 1) { waves = 16; nb_cap = nb16; per_cu = pc16; }
+    }
+    if (nb_cap > 0 && per_cu >= 1) {
+      LinGroup gp;
+      const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
+      const size_t lds = gemv_lds_bytes(k, G, nb, waves);
+      const bool szv = scales_octets(items, count, ng_all);
+      const void* fn =
+          waves == 16 ? (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 16>)
+                             : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 16>))
+                      : (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 8>)
+                             : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 8>));
+      if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      const dim3 gd((unsigned)gp.wg0[count]), bd((unsigned)(waves * 64));
+      if (waves == 16) {
+        if (szv)
+          hipLaunchKernelGGL((linear_gemv_kernel<G, true, 16>), gd, bd, lds, stream, gp, k);
+        else
+          hipLaunchKernelGGL((linear_gemv_kernel<G, false, 16>), gd, bd, lds, stream, gp, k);
+      } else {
+        if (szv)
+          hipLaunchKernelGGL((linear_gemv_kernel<G, true, 8>), gd, bd, lds, stream, gp, k);
+        else
+          hipLaunchKernelGGL((linear_gemv_kernel<G, false, 8>), gd, bd, lds, stream, gp, k);
+      }
+      return hipGetLastError();
+    }
+  }
+  // skinny 2 <= m <= 16: one fused kernel when its LDS plan fits
+  if (m >= 2 && m <= 16) {
+    const int tcs = 1;
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
+    int nb_cap = kGemvMaxBlk;
+    while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * kSk16Threads ||
+                          skinny_fused_lds_bytes(k, G, nb_cap, tcs) > 160 * 1024))
+      --nb_cap;
+    if (nb_cap > 0) {
+      int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)skinny_fused_lds_bytes(k, G, nb_cap, tcs);
+      per_cu = per_cu < 2 ? per_cu : 2;
+      LinGroup gp;
+      const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
+      const size_t lds = skinny_fused_lds_bytes(k, G, nb, tcs);
+      const bool szv = scales_octets(items, count, ng_all);
+      const dim3 gd((unsigned)gp.wg0[count]), bd(kSk16Threads);
+#define AWQ_SKF(TCC, SZ, PFF)                                                                  \
+  {                                                                                            \
+    const void* fn_ = reinterpret_cast<const void*>(&linear_skinny_fused_kernel<G, TCC, SZ, PFF>); \
+    if (lds > 65536) {                                                                         \
+      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((linear_skinny_fused_kernel<G, TCC, SZ, PFF>), gd, bd, lds, stream, gp,  \
+                       m, k);                                                                  \
+  }
+      if (szv) AWQ_SKF(1, true, 2) else AWQ_SKF(1, false, 2)
+#undef AWQ_SKF
+      return hipGetLastError();
+    }
+  }
+  // every other case: one linear after another on the stream (the staged
+  // kernels share the scratch buffer, in stream order)
+  for (int l = 0; l < count; ++l) {
+    hipError_t e = launch_linear_one<G>(items[l], m, k, scratch, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
+                               void* scratch, hipStream_t stream) {
+  switch (g) {
+    case 32:
+      return launch_linear_group_g<32>(items, count, m, k, scratch, stream);
+    case 64:
+      return launch_linear_group_g<64>(items, count, m, k, scratch, stream);
+    default:
+      return launch_linear_group_g<128>(items, count, m, k, scratch, stream);
+  }
+}
+
 hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                          const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
                          int64_t k, int32_t g, uint16_t* y, void* scratch, hipStream_t stream) {
-  switch (g) {
-    case 32:
-      return launch_linear_g<32>(x, qweight, scales, qzeros, inv_s16, m, n, k, y, scratch, stream);
-    case 64:
-      return launch_linear_g<64>(x, qweight, scales, qzeros, inv_s16, m, n, k, y, scratch, stream);
-    default:
-      return launch_linear_g<128>(x, qweight, scales, qzeros, inv_s16, m, n, k, y, scratch, stream);
-  }
+  const LinItem it{x, inv_s16, qweight, scales, qzeros, y, n};
+  return launch_linear_group(&it, 1, m, k, g, scratch, stream);
 }
 
 }  // namespace awq
