@@ -10,7 +10,9 @@ One step is one pass of the whole path over one batch of synthetic input:
             awq_linear_w4a16_group call, o, gate and up in one group call,
             down; 128 calls, replayed as one HIP graph each) at M = 1, 8 and
             32 tokens with g = 128, and at M = 1 and 32 with g = 64;
-  prefill   the 7 linears of layer L at M = 2048 tokens (GEMM).
+  prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
+            in the decode (4 calls, each one activation-prep launch and one
+            GEMM launch over the tiles of its linears).
 
 Inputs are resident in HBM before the timed region.  The reported value is
 the M = 1 decode: algorithmic bytes of the 224 linears (packed nibbles +
@@ -221,10 +223,13 @@ def main():
 
     def prefill(layer):
         st = stacks[128]
-        for li, (nm, n, k) in enumerate(shapes):
-            qw, sc, qz, _ = st[layer][li]
-            P.awq_linear_w4a16(XP[S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2],
-                               g=128, out=YP[li])
+        for grp in groups:
+            items = []
+            for li in grp:
+                nm = shapes[li][0]
+                qw, sc, qz, _ = st[layer][li]
+                items.append((XP[S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2], YP[li]))
+            P.awq_linear_w4a16_group(items, g=128)
 
     phases = ["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["prefill"]
     acc = {p: 0.0 for p in phases}

@@ -375,21 +375,32 @@ def _check_group(P, items, meta, k, g, cols_per=None):
         assert ok, (n, worst, raw)
 
 
-@pytest.mark.parametrize("m", [1, 8, 24, 40])
+@pytest.mark.parametrize("m", [1, 8, 24, 40, 300])
 @pytest.mark.parametrize("g", [128, 64])
 def test_linear_group_matches_single_and_oracle(P, m, g):
-    # m = 1 and m = 8: one grouped launch; m = 24 and 40: one launch per linear
+    # m = 1 and 8: one grouped decode launch; m = 24: one launch per linear;
+    # m = 40 and 300 (two row tiles, the second ragged): one activation-prep
+    # launch and one GEMM launch over the tiles of every linear
     specs = [(1000, 0.5, 460), (256, 0.3, 470), (264, None, 480), (16, 0.4, 490)]
     items, meta = _group_case(P, m, 2048, g, specs, 461 + m)
     _check_group(P, items, meta, 2048, g)
     _check_group(P, items[1:3], meta[1:3], 2048, g)
 
 
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 8, 24, 2048])
 def test_linear_group_llama3_8b_full_size_sampled(P, m):
     qkv = [(4096, 0.5, 500), (1024, 0.4, 510), (1024, 0.45, 520)]
     items, meta = _group_case(P, m, 4096, 128, qkv, 530 + m)
     _check_group(P, items, meta, 4096, 128, cols_per=128)
     gate_up = [(14336, 0.5, 540), (14336, 0.35, 550)]
     items, meta = _group_case(P, m, 4096, 128, gate_up, 560 + m)
+    _check_group(P, items, meta, 4096, 128, cols_per=128)
+
+
+@pytest.mark.parametrize("m", [20, 32])
+def test_linear_group_mixed_plan(P, m):
+    # above 16 tokens a group of more than 16 MiB of packed weights runs linear
+    # by linear, and the small linear in it still takes its own (fused) plan
+    specs = [(14336, 0.5, 570), (1024, 0.4, 580), (264, None, 590)]
+    items, meta = _group_case(P, m, 4096, 128, specs, 600 + m)
     _check_group(P, items, meta, 4096, 128, cols_per=128)

@@ -181,7 +181,7 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const ui
                                      g, y);
   if (st0 != AWQ_OK) return st0;
   void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g), &scratch);
+  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g, 1), &scratch);
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, scratch,
                                     (hipStream_t)stream);
@@ -204,7 +204,7 @@ awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count, i
     li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
   }
   void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g), &scratch);
+  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g, count), &scratch);
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group launch");

@@ -46,8 +46,9 @@ struct LinItem {
   int64_t n;
 };
 
-// Scratch bytes the linear needs for the staged activations.
-size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g);
+// Scratch bytes a call of count linears (same m, k, g) needs for the staged
+// activations.
+size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g, int count);
 
 hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                          const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
@@ -55,7 +56,8 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint1
                          hipStream_t stream);
 
 // 1..kGroupMax independent linears of the same m, k and g: one launch for the
-// decode kernels that take groups, consecutive launches otherwise.  Each y
+// kernels that take groups (decode GEMV, fused skinny, prefill GEMM),
+// consecutive launches otherwise.  Each y
 // holds the bits launch_linear writes for that linear alone.
 hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
                                void* scratch, hipStream_t stream);

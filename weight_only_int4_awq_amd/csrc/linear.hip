@@ -35,8 +35,13 @@ constexpr int kSkinnyWaves = 8;        // waves per work-group
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g) {
-  if (m > 32) return align256((size_t)m * (size_t)k * 2);     // scaled, permuted activations
+static int64_t gemm_row_chunk(int64_t k);
+
+size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g, int count) {
+  if (m > 32) {                 // scaled, permuted activations: one slot per linear
+    const size_t slot = align256((size_t)m * (size_t)k * 2);
+    return m <= gemm_row_chunk(k) ? (size_t)count * slot : slot;
+  }
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / g;
   size_t a = (size_t)tc * (size_t)k * 16 * 2;          // [tc][ng][4][16][g/4] halves
@@ -225,8 +230,9 @@ struct LinPick {
   int64_t n;
   int bid, grid;
 };
-__device__ __forceinline__ LinPick pick_linear(const LinGroup& gp) {
-  const int b = (int)blockIdx.x;
+// the linear that work-group (or tile) b of a group launch belongs to, and
+// b's index within that linear's range
+__device__ __forceinline__ LinPick pick_linear_at(const LinGroup& gp, int b) {
   int li = 0;
 #pragma unroll
   for (int i = 1; i < kGroupMax; ++i)
@@ -242,6 +248,9 @@ __device__ __forceinline__ LinPick pick_linear(const LinGroup& gp) {
   L.bid = b - gp.wg0[li];
   L.grid = gp.wg0[li + 1] - gp.wg0[li];
   return L;
+}
+__device__ __forceinline__ LinPick pick_linear(const LinGroup& gp) {
+  return pick_linear_at(gp, (int)blockIdx.x);
 }
 
 // ---------------------------------------------------------------- decode GEMV (m = 1)
@@ -1196,6 +1205,12 @@ size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
 //    once.  The next K-step's global loads are in flight while the current
 //    one is multiplied.
 constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 64;
+
+// rows of one GEMM launch: its x_tilde stays below 2^31 bytes
+static int64_t gemm_row_chunk(int64_t k) {
+  const int64_t c = (((int64_t)1 << 31) / (k * 2)) / kGemmBM * kGemmBM;
+  return c > 0 ? c : kGemmBM;
+}
 #ifndef AWQ_GEMM_SWZ_SHIFT
 #define AWQ_GEMM_SWZ_SHIFT 1
 #endif
@@ -1207,10 +1222,17 @@ __device__ __forceinline__ uint32_t perm_bytes(uint32_t hi, uint32_t lo, uint32_
 // x_tilde = fp16_rn(x * inv_s), every 8-channel chunk permuted into the
 // nibble-unpack slot order (k0,k4) (k1,k5) (k2,k6) (k3,k7); one pass over the
 // activations per call, so the GEMM's activation staging is a plain copy.
-__global__ __launch_bounds__(256) void linear_xprep_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ inv_s,
-                                                           int64_t m, int64_t k,
-                                                           uint16_t* __restrict__ xt) {
+// Item blockIdx.y of the group: x = gp.x, inv_s = gp.inv, x_tilde written to
+// gp.y (the scratch slot of that item).
+__global__ __launch_bounds__(256) void linear_xprep_kernel(const LinGroup gp, int64_t m,
+                                                           int64_t k) {
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kGroupMax; ++i)
+    if (i == (int)blockIdx.y) li = i;
+  const uint16_t* __restrict__ x = gp.x[li];
+  const uint16_t* __restrict__ inv_s = gp.inv[li];
+  uint16_t* __restrict__ xt = gp.y[li];
   const int64_t chunks = m * (k / 8);
   const bool has_inv = inv_s != nullptr;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
@@ -1239,11 +1261,11 @@ size_t gemm_lds_bytes(int64_t k, int32_t g) {
   return s_bytes + (size_t)kGemmBN * nzw * 4;
 }
 
+// A launch covers the tiles of up to kGroupMax linears (same m and k): tiles
+// [wg0[l], wg0[l+1]) belong to linear l, whose x is its x_tilde.
 template <int G>
-__global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
-    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-    int64_t m, int64_t n, int64_t k, uint16_t* __restrict__ y, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, int64_t m,
+                                                             int64_t k, int tiles_m) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // two distinct stage objects: the compiler can see that the copies into one
   // stage never alias the fragment reads of the other, so it does not wait for
@@ -1260,12 +1282,19 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(
   const int wm = wave & 1, wn = wave >> 1;
   // XCD-aware tile order: each XCD gets a contiguous range of tiles, M fastest,
   // so the work-groups that share a weight tile share that XCD's L2
-  const int total = tiles_m * tiles_n;
+  const int total = gp.wg0[gp.count];
   const int bid = blockIdx.x;
   const int per = total / 8, rem = total % 8;
   const int xcd = bid % 8, slot = bid / 8;
   const int tile = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const LinPick L = pick_linear_at(gp, tile);
+  const uint16_t* __restrict__ x = L.x;
+  const uint32_t* __restrict__ qweight = L.qw;
+  const uint16_t* __restrict__ scales = L.sc;
+  const uint32_t* __restrict__ qzeros = L.qz;
+  uint16_t* __restrict__ y = L.y;
+  const int64_t n = L.n;
+  const int tm = L.bid % tiles_m, tn = L.bid / tiles_m;
   const int64_t m0 = (int64_t)tm * kGemmBM, n0 = (int64_t)tn * kGemmBN;
   const int64_t kw_row = k / 8;
   const int nk = (int)(k / kGemmBK);
@@ -1491,34 +1520,6 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   const uint16_t* inv_s16 = it.inv;
   uint16_t* y = it.y;
   const int64_t n = it.n;
-  if (m > 32) {
-    const size_t lds = gemm_lds_bytes(k, G);
-    const size_t lds_static = (size_t)2 * kGemmBM * kGemmBK * 2;
-    if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
-    if (lds + lds_static > 65536) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<G>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    uint16_t* xt = static_cast<uint16_t*>(scratch);
-    const int64_t chunks = m * (k / 8);
-    const int64_t pgrid = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
-    hipLaunchKernelGGL(linear_xprep_kernel, dim3((unsigned)pgrid), dim3(256), 0, stream, x, inv_s16,
-                       m, k, xt);
-    // the kernel addresses its activations with 32-bit byte offsets: launch
-    // in row chunks of fewer than 2^31 bytes of x_tilde
-    int64_t chunk = (((int64_t)1 << 31) / (k * 2)) / kGemmBM * kGemmBM;
-    chunk = chunk > 0 ? chunk : kGemmBM;
-    const int tiles_n = (int)((n + kGemmBN - 1) / kGemmBN);
-    for (int64_t r0 = 0; r0 < m; r0 += chunk) {
-      const int64_t mc = (m - r0) < chunk ? (m - r0) : chunk;
-      const int tiles_m = (int)((mc + kGemmBM - 1) / kGemmBM);
-      hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256), lds,
-                         stream, xt + r0 * k, qweight, scales, qzeros, mc, n, k, y + r0 * n, tiles_m,
-                         tiles_n);
-    }
-    return hipGetLastError();
-  }
   // 16 < m <= 32: prep16 + skinny16 when its LDS plan fits (with 32 tokens the
   // activation operand formed once per call beats forming it per item)
   if (m > 16 && m <= 32) {
@@ -1593,9 +1594,69 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   return hipGetLastError();
 }
 
+// The prefill GEMM of a group (m > 32): x_tilde of every linear into a
+// scratch slot of its own (one launch for all), then one GEMM launch over
+// the tiles of all linears.  The kernel addresses its activations with 32-bit
+// byte offsets: an m whose x_tilde reaches 2^31 bytes runs linear after
+// linear, in row chunks, through scratch slot 0.
+template <int G>
+static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, int64_t k,
+                                    void* scratch, hipStream_t stream) {
+  const size_t lds = gemm_lds_bytes(k, G);
+  const size_t lds_static = (size_t)2 * kGemmBM * kGemmBK * 2;
+  if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
+  if (lds + lds_static > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<G>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const size_t slot_bytes = align256((size_t)m * (size_t)k * 2);
+  const int64_t chunk = gemm_row_chunk(k);
+  const bool whole = m <= chunk;
+  const int n_batch = whole ? 1 : count;
+  for (int bt = 0; bt < n_batch; ++bt) {
+    const LinItem* its = whole ? items : items + bt;
+    const int cnt = whole ? count : 1;
+    LinGroup xg = {};
+    for (int l = 0; l < cnt; ++l) {
+      xg.x[l] = its[l].x;
+      xg.inv[l] = its[l].inv;
+      xg.y[l] = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + (size_t)l * slot_bytes);
+    }
+    xg.count = cnt;
+    const int64_t chunks = m * (k / 8);
+    const int64_t pgrid = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
+    hipLaunchKernelGGL(linear_xprep_kernel, dim3((unsigned)pgrid, (unsigned)cnt), dim3(256), 0,
+                       stream, xg, m, k);
+    for (int64_t r0 = 0; r0 < m; r0 += chunk) {
+      const int64_t mc = (m - r0) < chunk ? (m - r0) : chunk;
+      const int tiles_m = (int)((mc + kGemmBM - 1) / kGemmBM);
+      LinGroup gg = {};
+      int total = 0;
+      for (int l = 0; l < cnt; ++l) {
+        const int64_t n = its[l].n;
+        gg.x[l] = xg.y[l] + r0 * k;
+        gg.qw[l] = its[l].qw;
+        gg.sc[l] = its[l].sc;
+        gg.qz[l] = its[l].qz;
+        gg.y[l] = its[l].y + r0 * n;
+        gg.n[l] = n;
+        gg.wg0[l] = total;
+        total += tiles_m * (int)((n + kGemmBN - 1) / kGemmBN);
+      }
+      for (int l = cnt; l <= kGroupMax; ++l) gg.wg0[l] = total;
+      gg.count = cnt;
+      hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)total), dim3(256), lds, stream, gg,
+                         mc, k, tiles_m);
+    }
+  }
+  return hipGetLastError();
+}
+
 template <int G>
 static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t m, int64_t k,
                                         void* scratch, hipStream_t stream) {
+  if (m > 32) return launch_gemm_group<G>(items, count, m, k, scratch, stream);
   // the decode GEMV (m = 1): at most kGemvMaxBlk column blocks per
   // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
   // thread) and whose LDS plan fits 160 KiB
@@ -1651,9 +1712,16 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
       return hipGetLastError();
     }
   }
-  // skinny 2 <= m <= 16: one fused kernel when its LDS plan fits
-  if (m >= 2 && m <= 16) {
-    const int tcs = 1;
+  // skinny 2 <= m <= 32: one fused kernel when its LDS plan fits (16-token
+  // chunks: one for m <= 16, two above).  Above 16 tokens the fused kernel
+  // reads every activation row once per 16-column block, which costs more than
+  // a separate activation-prep launch per linear once the group holds more
+  // than 16 MiB of packed weights (measured: q/k/v and o faster fused,
+  // gate/up, down and the 70B-shaped linears faster staged).
+  int64_t packed_bytes = 0;
+  for (int l = 0; l < count; ++l) packed_bytes += items[l].n * k / 2;
+  if (m >= 2 && (m <= 16 || (m <= 32 && packed_bytes <= ((int64_t)16 << 20)))) {
+    const int tcs = m <= 16 ? 1 : 2;
     const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
     int nb_cap = kGemvMaxBlk;
     while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * kSk16Threads ||
@@ -1677,15 +1745,21 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
     hipLaunchKernelGGL((linear_skinny_fused_kernel<G, TCC, SZ, PFF>), gd, bd, lds, stream, gp,  \
                        m, k);                                                                  \
   }
-      if (szv) AWQ_SKF(1, true, 2) else AWQ_SKF(1, false, 2)
+      if (tcs == 1) {
+        if (szv) AWQ_SKF(1, true, 2) else AWQ_SKF(1, false, 2)
+      } else {
+        if (szv) AWQ_SKF(2, true, 1) else AWQ_SKF(2, false, 1)
+      }
 #undef AWQ_SKF
       return hipGetLastError();
     }
   }
-  // every other case: one linear after another on the stream (the staged
-  // kernels share the scratch buffer, in stream order)
+  // every other case: one linear after another on the stream, each planned as
+  // a call of it alone (the staged kernels share the scratch buffer, in
+  // stream order)
+  if (count == 1) return launch_linear_one<G>(items[0], m, k, scratch, stream);
   for (int l = 0; l < count; ++l) {
-    hipError_t e = launch_linear_one<G>(items[l], m, k, scratch, stream);
+    hipError_t e = launch_linear_group_g<G>(items + l, 1, m, k, scratch, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
