@@ -397,10 +397,12 @@ def test_linear_group_llama3_8b_full_size_sampled(P, m):
     _check_group(P, items, meta, 4096, 128, cols_per=128)
 
 
-@pytest.mark.parametrize("m", [20, 32])
+@pytest.mark.parametrize("m", [8, 20, 32])
 def test_linear_group_mixed_plan(P, m):
-    # above 16 tokens a group of more than 16 MiB of packed weights runs linear
-    # by linear, and the small linear in it still takes its own (fused) plan
+    # m = 8: the group takes two column blocks per work-group (group-major
+    # kernel), the small linears alone take one (block-major kernel); above 16
+    # tokens a group of more than 16 MiB of packed weights runs linear by
+    # linear, and the small linear in it still takes its own (fused) plan
     specs = [(14336, 0.5, 570), (1024, 0.4, 580), (264, None, 590)]
     items, meta = _group_case(P, m, 4096, 128, specs, 600 + m)
     _check_group(P, items, meta, 4096, 128, cols_per=128)

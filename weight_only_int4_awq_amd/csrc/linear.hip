@@ -762,13 +762,15 @@ __global__ __launch_bounds__(kSk16Threads, 4) void linear_skinny16_kernel(
   uint4 aq[2 * PF][TC][WPL];          // raw bits, like the weight words
   const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(qweight, (uint32_t)((uint64_t)n * (uint64_t)k / 2));
   const __amdgpu_buffer_rsrc_t rs_a = buf_rsrc(a16, (uint32_t)((uint64_t)TC * (uint64_t)k * 32));
+  // the row (which decides whether a load is past the end) is in the VGPR
+  // offset, the group along K in the scalar one
   const uint32_t w_voff = ((uint32_t)r * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
   const uint32_t a_voff = (uint32_t)((c * 16 + r) * HPL) * 2u;
   int i_blk = (int)blockIdx.x, i_j = jb, i_left = total;
   auto issue = [&](int slot) {
     const int jj = i_j < ng ? i_j : ng - 1;
-    const uint32_t wso = ((uint32_t)i_blk * 16u * (uint32_t)kw_row + (uint32_t)(jj * LPG)) * 4u;
-    buf_words<WPL>(rs_w, w_voff, wso, wq[slot]);
+    const uint32_t wvo = w_voff + (uint32_t)i_blk * 16u * (uint32_t)kw_row * 4u;
+    buf_words<WPL>(rs_w, wvo, (uint32_t)(jj * LPG) * 4u, wq[slot]);
 #pragma unroll
     for (int tc = 0; tc < TC; ++tc) {
       const uint32_t aso = (uint32_t)((tc * ng + jj) * 64 * HPL) * 2u;
@@ -1003,20 +1005,25 @@ __device__ __forceinline__ void skinny_fused_body(
   uint4 xq[2 * PF][TC][WPL];
   const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(qweight, (uint32_t)((uint64_t)n * (uint64_t)k / 2));
   const __amdgpu_buffer_rsrc_t rs_x = buf_rsrc(x, (uint32_t)((uint64_t)m * (uint64_t)k * 2));
+  // the row or token (which decides whether a load is past the end) is in the
+  // VGPR offset, the group along K in the scalar one
   const uint32_t w_voff = ((uint32_t)r * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
-  const uint32_t x_voff = ((uint32_t)r * (uint32_t)k + (uint32_t)(8 * WPL * c)) * 2u;
+  uint32_t x_voff[TC];
+#pragma unroll
+  for (int tc = 0; tc < TC; ++tc)
+    x_voff[tc] = ((uint32_t)(tc * 16 + r) * (uint32_t)k + (uint32_t)(8 * WPL * c)) * 2u;
   int i_blk = bid, i_j = jb, i_left = total;
   auto issue = [&](int slot) {
     const int jj = i_j < ng ? i_j : ng - 1;
-    const uint32_t wso = ((uint32_t)i_blk * 16u * (uint32_t)kw_row + (uint32_t)(jj * LPG)) * 4u;
-    buf_words<WPL>(rs_w, w_voff, wso, wq[slot]);
+    const uint32_t wvo = w_voff + (uint32_t)i_blk * 16u * (uint32_t)kw_row * 4u;
+    buf_words<WPL>(rs_w, wvo, (uint32_t)(jj * LPG) * 4u, wq[slot]);
 #pragma unroll
     for (int tc = 0; tc < TC; ++tc) {
-      const uint32_t xso = ((uint32_t)tc * 16u * (uint32_t)k + (uint32_t)(jj * G)) * 2u;
+      const uint32_t xso = (uint32_t)(jj * G) * 2u;
 #pragma unroll
       for (int i = 0; i < WPL; ++i)
         xq[slot][tc][i] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, x_voff + 16u * i, xso, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, x_voff[tc] + 16u * i, xso, 0));
     }
     if (i_left > 1) {
       --i_left;
@@ -1163,6 +1170,260 @@ __device__ __forceinline__ void skinny_fused_body(
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- skinny, group-major
+// linear_skinny_gm: the fused skinny kernel with a work-group's (block, group)
+// items walked group-major.  One unit of a wave is group j of all NB column
+// blocks of its work-group, so the 16 activation rows of group j are loaded,
+// scaled and permuted into the MFMA A operand once for NB blocks (block-major
+// does that once per block, which at 16 tokens moves four times the weight
+// bytes through the caches).  The NB accumulators stay in registers over the
+// wave's K range, so the main loop has no barrier; after it the waves meet
+// once per block to sum their partial rows, and the reducing wave stores the
+// outputs.  Block slots past the linear's last block point one block past its
+// end: their weight loads read zeros, and they are not stored.
+template <int G, bool SZV, int NB, int PF>
+__device__ __forceinline__ void skinny_gm_body(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
+    const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
+    uint16_t* __restrict__ y, int bid, int grid) {
+  constexpr int WPL = G / 32, LPG = G / 8;
+  constexpr int W = kSk16Waves;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int ng = (int)(k / G);
+  const int nblk = (int)((n + 15) / 16);
+  const int my_blocks = (nblk - bid + grid - 1) / grid;   // 1 .. NB
+  const size_t inv_bytes = ((size_t)k * 2 + 1023) & ~(size_t)1023;
+  unsigned char* sp = smem;
+  uint16_t* inv_l = reinterpret_cast<uint16_t*>(sp);  sp += inv_bytes;
+  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);    sp += (size_t)NB * ng * 16 * 4;
+  floatx4_t* red = reinterpret_cast<floatx4_t*>(sp);  // [2][W][64]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int jb = ng * wave / W, je = ng * (wave + 1) / W;
+  const int cnt = je - jb;
+  const int nzw = (ng + 7) / 8, kw_row = (int)(k / 8);
+  const bool has_inv = inv_s != nullptr;
+
+  // ---- 1. inv_s into LDS (straight global -> LDS copies, as the fused kernel)
+  if (has_inv) {
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    const int64_t src_bytes = k * 2;
+    const char* srcb = reinterpret_cast<const char*>(inv_s);
+    const int n_copy = (int)(inv_bytes / 1024);
+    for (int i = wave; i < n_copy; i += W) {
+      int64_t off = (int64_t)i * 1024 + lane * 16;
+      off = off + 16 <= src_bytes ? off : src_bytes - 16;
+      __builtin_amdgcn_global_load_lds((const void*)(srcb + off),
+                                       (lds_void_t*)(reinterpret_cast<char*>(inv_l) + i * 1024),
+                                       16, 0, 0);
+    }
+  }
+  // ---- 2. scale and zero words of the work-group's blocks
+  const int n_oct = my_blocks * 16 * nzw;
+  uint4 sz_s[kGemvSzRounds];
+  uint32_t sz_z[kGemvSzRounds];
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    sz_s[i] = make_uint4(0, 0, 0, 0);
+    sz_z[i] = 0;
+    const int o = tid + i * kSk16Threads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      int col = (bid + bs * grid) * 16 + row;
+      col = col < (int)n ? col : (int)n - 1;
+      const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
+      if constexpr (SZV) {
+        sz_s[i] = *reinterpret_cast<const uint4*>(srow);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (oct * 8 + e < ng) ? srow[e] : (uint16_t)0;
+        sz_s[i] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                             h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+      }
+      sz_z[i] = qzeros[(int64_t)col * nzw + oct];
+    }
+  }
+
+  // ---- 3. first units (unconditional buffer loads: rows past n, block slots
+  // past the last block and tokens past m read zeros; the row or token is in
+  // the VGPR offset, the group along K in the scalar one)
+  uint32_t wq[2 * PF][NB][WPL];
+  uint4 xq[2 * PF][WPL];
+  const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(qweight, (uint32_t)((uint64_t)n * (uint64_t)k / 2));
+  const __amdgpu_buffer_rsrc_t rs_x = buf_rsrc(x, (uint32_t)((uint64_t)m * (uint64_t)k * 2));
+  uint32_t w_voff[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    int blk = bid + bb * grid;
+    blk = blk < nblk ? blk : nblk;
+    w_voff[bb] = ((uint32_t)(blk * 16 + r) * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
+  }
+  const uint32_t x_voff = ((uint32_t)r * (uint32_t)k + (uint32_t)(8 * WPL * c)) * 2u;
+  int i_j = jb, i_left = cnt;
+  auto issue = [&](int slot) {
+    const int jj = i_j < ng ? i_j : ng - 1;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+      buf_words<WPL>(rs_w, w_voff[bb], (uint32_t)(jj * LPG) * 4u, wq[slot][bb]);
+#pragma unroll
+    for (int i = 0; i < WPL; ++i)
+      xq[slot][i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, x_voff + 16u * i, (uint32_t)(jj * G) * 2u, 0));
+    if (i_left > 1) {
+      --i_left;
+      ++i_j;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(p);
+
+  // ---- 4. scale|zero words into LDS as [block][group][column]
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    const int o = tid + i * kSk16Threads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      const uint32_t sw[4] = {sz_s[i].x, sz_s[i].y, sz_s[i].z, sz_s[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = oct * 8 + e;
+        if (j < ng)
+          szw[((size_t)bs * ng + j) * 16 + row] =
+              ((sw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) | (((sz_z[i] >> (4 * e)) & 0xFu) << 16);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);      // the inv_s copies have landed
+  __syncthreads();
+
+  const UnpackConsts uc = unpack_consts();
+  floatx4_t acc[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) acc[bb] = floatx4_t{};
+  int c_j = jb, c_left = cnt;
+  auto consume = [&](int p, bool guarded) {   // guarded only in the tail
+    if (!guarded || c_left > 0) {
+      const int j = c_j;
+      // A: x_tilde = fp16_rn(x inv_s) of the 16 token rows, channels permuted
+      // into the unpack order (k0, k4, k1, k5, k2, k6, k3, k7)
+      half8_t av[WPL];
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        const uint4 sv = has_inv ? *reinterpret_cast<const uint4*>(inv_l + j * G + 8 * (WPL * c + i))
+                                 : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+        const uint4 xv = xq[p][i];
+        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, sv.x));
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
+        const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
+        const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.w) * __builtin_bit_cast(half2_t, sv.w));
+        av[i] = __builtin_bit_cast(half8_t, make_uint4(__builtin_amdgcn_perm(p2, p0, 0x05040100u),
+                                                       __builtin_amdgcn_perm(p2, p0, 0x07060302u),
+                                                       __builtin_amdgcn_perm(p3, p1, 0x05040100u),
+                                                       __builtin_amdgcn_perm(p3, p1, 0x07060302u)));
+      }
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        // B: the 8 weights of word i of block bb, fp16_rn((q - z) D) in unpack order
+        const uint32_t szv = szw[((size_t)bb * ng + j) * 16 + r];
+        const float d = h2f((uint16_t)szv), z = (float)(szv >> 16);
+        const half2_t dd = {(half_t)d, (half_t)d};
+        const half2_t o1024 = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};
+        const half2_t o64 = {(half_t)(-64.0f - z), (half_t)(-64.0f - z)};
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+          uint32_t u[4];
+          unpack_word(wq[p][bb][i], u, uc);
+          const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024) * dd;
+          const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64) * dd;
+          const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024) * dd;
+          const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + o64) * dd;
+          const half8_t bop = __builtin_bit_cast(
+              half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+                                  __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)));
+          acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], bop, acc[bb], 0, 0, 0);
+        }
+      }
+      --c_left;
+      ++c_j;
+    }
+  };
+  if (cnt > 0) {
+    int left = cnt;
+    while (true) {
+      if (left > PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(PF + p);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(p, false);
+        left -= PF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(p, true);
+        break;
+      }
+      if (left > PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) issue(p);
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(PF + p, false);
+        left -= PF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) consume(PF + p, true);
+        break;
+      }
+    }
+  }
+
+  // ---- 5. per block: the W partial rows summed in wave order by the last
+  // wave, which stores the block (lane (c, r) holds tokens 4c + e of column r)
+  const int reducer = W - 1;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    if (bb < my_blocks) {
+      floatx4_t* rb = red + (size_t)(bb & 1) * W * 64;
+      rb[wave * 64 + lane] = acc[bb];
+      __syncthreads();
+      if (wave == reducer) {
+        floatx4_t sacc = rb[lane];
+#pragma unroll
+        for (int wv = 1; wv < W; ++wv) sacc += rb[wv * 64 + lane];
+        const int64_t col = ((int64_t)bid + (int64_t)bb * grid) * 16 + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = sacc[e];
+          const int64_t t = 4 * c + e;
+          if (t < m && col < n) y[t * n + col] = f2h_rn(v);
+        }
+      }
+    }
+  }
+}
+
+#ifndef AWQ_SKINNY_GM_MINW
+#define AWQ_SKINNY_GM_MINW 2
+#endif
+template <int G, bool SZV, int NB, int PF>
+__global__ __launch_bounds__(kSk16Threads, AWQ_SKINNY_GM_MINW) void linear_skinny_gm_kernel(const LinGroup gp,
+                                                                           int64_t m, int64_t k) {
+  const LinPick L = pick_linear(gp);
+  skinny_gm_body<G, SZV, NB, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid);
+}
+
+// LDS of the group-major skinny kernel: inv_s (whole 1 KiB copies), scale|zero
+// words [NB][ng][16], reduction rows [2][8][64] float4.
+size_t skinny_gm_lds_bytes(int64_t k, int32_t g, int nb) {
+  const size_t ng = (size_t)(k / g);
+  const size_t inv = ((size_t)k * 2 + 1023) & ~(size_t)1023;
+  return inv + (size_t)nb * ng * 16 * 4 + (size_t)2 * kSk16Waves * 64 * 16;
 }
 
 // LDS of the fused skinny kernel: inv_s (rounded up to whole 1 KiB copies),
@@ -1503,6 +1764,19 @@ static int split_group_grid(const LinItem* items, int count, int64_t slots, int 
   return nb;
 }
 
+// The decode kernels address the packed weights with 32-bit byte offsets
+// (including the up to 16 rows past n of the last column block, and one block
+// past the end), the activations of up to 32 tokens likewise.
+static bool offsets32_ok(const LinItem* items, int count, int64_t k) {
+  const uint64_t lim = (uint64_t)1 << 32;
+  if ((uint64_t)32 * (uint64_t)k * 2 >= lim) return false;
+  for (int l = 0; l < count; ++l) {
+    const uint64_t rows = (uint64_t)((items[l].n + 15) / 16) * 16 + 16;
+    if (rows * (uint64_t)k / 2 >= lim) return false;
+  }
+  return true;
+}
+
 static bool scales_octets(const LinItem* items, int count, int64_t ng) {
   if (ng % 8 != 0) return false;
   for (int l = 0; l < count; ++l)
@@ -1522,7 +1796,7 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   const int64_t n = it.n;
   // 16 < m <= 32: prep16 + skinny16 when its LDS plan fits (with 32 tokens the
   // activation operand formed once per call beats forming it per item)
-  if (m > 16 && m <= 32) {
+  if (m > 16 && m <= 32 && offsets32_ok(&it, 1, k)) {
     const int tcs = 2;
     const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
     const int64_t nblk = (n + 15) / 16;
@@ -1660,7 +1934,8 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
   // the decode GEMV (m = 1): at most kGemvMaxBlk column blocks per
   // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
   // thread) and whose LDS plan fits 160 KiB
-  if (m == 1) {
+  const bool off32 = offsets32_ok(items, count, k);
+  if (m == 1 && off32) {
     const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
     auto plan = [&](int waves, int& nb_cap, int64_t& per_cu) {
       nb_cap = kGemvMaxBlk;
@@ -1720,7 +1995,7 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
   // gate/up, down and the 70B-shaped linears faster staged).
   int64_t packed_bytes = 0;
   for (int l = 0; l < count; ++l) packed_bytes += items[l].n * k / 2;
-  if (m >= 2 && (m <= 16 || (m <= 32 && packed_bytes <= ((int64_t)16 << 20)))) {
+  if (off32 && m >= 2 && (m <= 16 || (m <= 32 && packed_bytes <= ((int64_t)16 << 20)))) {
     const int tcs = m <= 16 ? 1 : 2;
     const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
     int nb_cap = kGemvMaxBlk;
@@ -1745,12 +2020,37 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
     hipLaunchKernelGGL((linear_skinny_fused_kernel<G, TCC, SZ, PFF>), gd, bd, lds, stream, gp,  \
                        m, k);                                                                  \
   }
-      if (tcs == 1) {
+#ifndef AWQ_SKINNY_GM_PF
+#define AWQ_SKINNY_GM_PF 1
+#endif
+#define AWQ_SKG(SZ, NBB)                                                                       \
+  {                                                                                            \
+    const size_t lg_ = skinny_gm_lds_bytes(k, G, NBB);                                         \
+    const void* fn_ = reinterpret_cast<const void*>(&linear_skinny_gm_kernel<G, SZ, NBB, AWQ_SKINNY_GM_PF>); \
+    if (lg_ > 65536) {                                                                         \
+      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg_); \
+      if (e_ != hipSuccess) return e_;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((linear_skinny_gm_kernel<G, SZ, NBB, AWQ_SKINNY_GM_PF>), gd, bd, lg_, stream, gp, \
+                       m, k);                                                                  \
+  }
+      // several blocks per work-group: group-major (the same sums in the same
+      // order, so the same bits as the block-major kernel)
+      if (tcs == 1 && nb >= 2) {
+        if (nb == 2) {
+          if (szv) AWQ_SKG(true, 2) else AWQ_SKG(false, 2)
+        } else if (nb == 3) {
+          if (szv) AWQ_SKG(true, 3) else AWQ_SKG(false, 3)
+        } else {
+          if (szv) AWQ_SKG(true, 4) else AWQ_SKG(false, 4)
+        }
+      } else if (tcs == 1) {
         if (szv) AWQ_SKF(1, true, 2) else AWQ_SKF(1, false, 2)
       } else {
         if (szv) AWQ_SKF(2, true, 1) else AWQ_SKF(2, false, 1)
       }
 #undef AWQ_SKF
+#undef AWQ_SKG
       return hipGetLastError();
     }
   }
