@@ -330,6 +330,35 @@ def test_linear_decode_multiblock(P, n, k, g):
     _check_linear(P, w, x, s16, g)
 
 
+def test_linear_packed_weights_at_4gib(P):
+    # the largest packed weights a call takes (n k / 2 just below 4 GiB): the
+    # decode kernels' 32-bit byte offsets, which run up to a block past the
+    # last one, do not reach, so every m <= 32 takes the 64-bit staged path
+    # (and the prefill GEMM addresses weights with 64-bit pointers).  Packed
+    # tensors are drawn directly (random nibbles, steps and zeros); outputs are
+    # checked on sampled columns, the ragged end among them.
+    n, k, g = (1 << 20) - 5, 8192, 128
+    gen = torch.Generator(device=DEV).manual_seed(620)
+    qw = torch.randint(-2**31, 2**31 - 1, (n, k // 8), dtype=torch.int32, device=DEV, generator=gen)
+    sc = (torch.rand((n, k // g), device=DEV, generator=gen) * 0.01 + 0.001).half()
+    qz = torch.randint(-2**31, 2**31 - 1, (n, k // (8 * g)), dtype=torch.int32, device=DEV, generator=gen)
+    xc = S.activations(64, k, 621, S.outlier_channels(k, 0.01, 622), 20.0)
+    inv = O.fp16_rn(1.0 / O.scale_candidate(O.calib_stats(xc), 0.4).astype(np.float64))
+    rng = np.random.Generator(np.random.PCG64(623))
+    cols = np.unique(np.concatenate([rng.choice(n, 96, replace=False), np.arange(n - 21, n),
+                                     np.arange((1 << 20) - 40, (1 << 20) - 30)]))
+    ci = torch.from_numpy(cols).to(DEV)
+    hq, hs, hz = host_u32(qw[ci]), sc[ci].cpu().numpy(), host_u32(qz[ci])
+    for m in (1, 8, 24, 40):
+        x = S.activations(m, k, 624 + m, S.outlier_channels(k, 0.01, 622), 20.0)
+        y = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=g)
+        torch.cuda.synchronize()
+        yr = O.linear_ref(x, hq, hs, hz, inv, k, g)
+        ok, worst, raw = O.check_linear(host16(y[:, ci]), yr)
+        assert ok, (m, worst, raw)
+        del y
+
+
 # ----------------------------------------------------------------- linear groups
 
 
