@@ -12,7 +12,11 @@ One step is one pass of the whole path over one batch of synthetic input:
             32 tokens with g = 128, and at M = 1 and 32 with g = 64;
   prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
             in the decode (4 calls, each one activation-prep launch and one
-            GEMM launch over the tiles of its linears).
+            GEMM launch over the tiles of its linears);
+  70B rows  the four Llama-3-70B-shaped linears (8192<-8192, 1024<-8192,
+            28672<-8192, 8192<-28672) at M = 1 and 16, each call on its own
+            copy of the packed weights (>= 512 MB of copies per shape), so
+            every call streams its weights from HBM.
 
 Inputs are resident in HBM before the timed region.  The reported value is
 the M = 1 decode: algorithmic bytes of the 224 linears (packed nibbles +
@@ -231,7 +235,46 @@ def main():
                 items.append((XP[S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2], YP[li]))
             P.awq_linear_w4a16_group(items, g=128)
 
-    phases = ["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["prefill"]
+    # Llama-3-70B-shaped single linears at M = 1 and 16, searched and packed
+    # like the stack (128 calibration tokens); timed cold: every call reads its
+    # own copy of the packed weights, the copies of one shape >= 512 MB, all
+    # calls of one (shape, M) replayed as one HIP graph
+    big = []
+    for nm, n, k in S.LLAMA3_70B_LINEARS:
+        slot = S.SLOTS[nm]
+        ch = S.outlier_channels(k, 0.005, S.seed_of(4, 0, slot, 3))
+        w = S.torch_weights(n, k, 0.015, S.seed_of(4, 0, slot, 0), dev)
+        xc = S.torch_activations(128, k, S.seed_of(4, 0, slot, 1), ch, 30.0, dev)
+        ws = torch.empty(P.awq_search_workspace_size(n, k, 128, 128, n_grid), dtype=torch.uint8, device=dev)
+        _, s16, inv, _ = P.awq_search_scale(w, xc, P.awq_calib_stats(xc), g=128, n_grid=n_grid, workspace=ws)
+        qw, sc, qz, _ = P.awq_pack_int4(w, s16, g=128)
+        del w, ws
+        copies = max(2, -(-(512 << 20) // (n * k // 2)))
+        packs = [(qw, sc, qz)] + [(qw.clone(), sc.clone(), qz.clone()) for _ in range(copies - 1)]
+        xr = {m: S.torch_activations(m, k, S.seed_of(4, 0, slot, 2) + m, ch, 30.0, dev) for m in (1, 16)}
+        yb = {m: torch.empty((m, n), dtype=torch.float16, device=dev) for m in (1, 16)}
+        big.append((nm, n, k, packs, inv, xr, yb))
+    big_cases = [(bi, m) for bi in range(len(big)) for m in (1, 16)]
+
+    def big_calls(bi, m):
+        nm, n, k, packs, inv, xr, yb = big[bi]
+        for qw, sc, qz in packs:
+            P.awq_linear_w4a16(xr[m], qw, sc, qz, inv, g=128, out=yb[m])
+
+    for bi, m in big_cases:
+        big_calls(bi, m)
+    torch.cuda.synchronize()
+    big_graphs = {}
+    for bi, m in big_cases:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            big_calls(bi, m)
+        big_graphs[(bi, m)] = gr
+    torch.cuda.synchronize()
+    log("packed and captured the 70B-shaped linears")
+
+    phases = (["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["prefill"] +
+              [f"big_{big[bi][0]}_m{m}" for bi, m in big_cases])
     acc = {p: 0.0 for p in phases}
 
     def step(i, timed):
@@ -244,7 +287,10 @@ def main():
             graphs[(g, m)].replay()
             ev[2 + pi].record(stream)
         prefill(layer)
-        ev[-1].record(stream)
+        ev[2 + len(decode_cases)].record(stream)
+        for ci, key in enumerate(big_cases):
+            big_graphs[key].replay()
+            ev[3 + len(decode_cases) + ci].record(stream)
         if timed:
             return ev
         return None
@@ -286,6 +332,20 @@ def main():
     rows["producer_m512"] = {"us_per_layer": t_pr * 1e6,
                              "search_TFLOPs_algorithmic": search_flops / t_pr / 1e12}
 
+    for bi, m in big_cases:
+        nm, n, k, packs, inv, xr, yb = big[bi]
+        t = acc[f"big_{nm}_m{m}"] / K / len(packs)
+        by = gemv_bytes(m, n, k, 128)
+        rows[f"llama3_70b_{nm}_m{m}"] = {"us_per_call": t * 1e6, "GBps": by / t / 1e9,
+                                         "frac_hbm_peak": by / t / 1e9 / HBM_PEAK_GBS,
+                                         "n": n, "k": k, "cold_copies": len(packs)}
+    # the two 122 MB shapes (28672<-8192, 8192<-28672) at M = 1 together
+    bp = [rows[f"llama3_70b_{nm}_m1"] for nm in ("gate_up", "down")]
+    bp_bytes = sum(gemv_bytes(1, r["n"], r["k"], 128) for r in bp)
+    bp_us = sum(r["us_per_call"] for r in bp)
+    big_pair = {"GBps": round(bp_bytes / bp_us / 1e3, 2),
+                "frac_hbm_peak": round(bp_bytes / bp_us / 1e3 / HBM_PEAK_GBS, 4),
+                "us_per_call": [round(r["us_per_call"], 2) for r in bp]}
     value = rows["decode_g128_m1"]["GBps"]
     t1 = acc["decode_g128_m1"] / K
     n_launch = L * len(groups)               # one decode-GEMV launch per group call at M = 1
@@ -306,10 +366,12 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% x20 outlier channels)",
         "config": {"workload": "llama3-8b-shaped linear stack: producer (calib 512 tok, 20-pt alpha "
                                "search, int4 g128 pack) on one layer + 32-layer decode at M=1/8/32 "
-                               "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048",
+                               "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048 + llama3-70b-"
+                               "shaped linears at M=1/16 (cold copies)",
                    "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32],
                    "m_prefill": 2048, "m_calib": m_cal, "n_grid": n_grid, "group_size": [128, 64]},
         "gemm_tflops_m2048": round(rows["prefill_m2048"]["TFLOPs"], 2),
+        "gemv_70b_big_pair_m1": big_pair,
         "roofline": {"bound": "hbm", "achieved": round(bytes_per_launch / avg_launch / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(bytes_per_launch / avg_launch / 1e9 / HBM_PEAK_GBS, 4),
