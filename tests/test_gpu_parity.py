@@ -359,6 +359,62 @@ def test_linear_packed_weights_at_4gib(P):
         del y
 
 
+@pytest.mark.parametrize("m", [33, 64, 256, 300])
+def test_linear_split_k_full_size_sampled(P, m):
+    # between the skinny kernels and a full prefill the GEMM's tiles alone
+    # leave CUs idle: 64-row tiles up to 64 tokens, and each tile's K-steps
+    # split over several work-groups (fp32 partial tiles in scratch, summed in
+    # slice order by a second launch).  Full Llama-3-8B shapes, sampled
+    # columns against the oracle, and a second call bit for bit equal.
+    rng = np.random.Generator(np.random.PCG64(700 + m))
+    for n, k, alpha in ((4096, 4096, 0.5), (1024, 4096, 0.3), (4096, 14336, 0.45)):
+        w = S.weights(n, k, 0.02, 701 + n + k)
+        xc = S.activations(64, k, 702 + k, S.outlier_channels(k, 0.01, 703), 20.0)
+        s16 = O.scale_candidate(O.calib_stats(xc), alpha)
+        inv = O.fp16_rn(1.0 / s16.astype(np.float64))
+        qw, sc, qz, _ = P.awq_pack_int4(dev(w), dev(s16), g=128)
+        del w
+        x = S.activations(m, k, 704 + m + k, S.outlier_channels(k, 0.01, 703), 20.0)
+        y = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=128)
+        y2 = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=128)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        cols = np.unique(np.concatenate([rng.choice(n, 96, replace=False), np.arange(n - 8, n)]))
+        yr = O.linear_ref_rows(x, host_u32(qw), sc.cpu().numpy(), host_u32(qz), inv, k, 128, cols)
+        ok, worst, raw = O.check_linear(host16(y)[:, cols], yr)
+        assert ok, (m, n, k, worst, raw)
+
+
+def test_linear_split_k_graph_replays(P):
+    # a captured split-K call (GEMM launch + slice-sum launch over scratch
+    # partials) replayed several times, with eager calls of other sizes in
+    # between that reuse the same scratch: every replay matches the eager result
+    k, n, m = 4096, 1024, 64
+    w = S.weights(n, k, 0.02, 710)
+    qw, sc, qz, _ = P.awq_pack_int4(dev(w), None, g=128)
+    x = dev(S.activations(m, k, 711, S.outlier_channels(k, 0.01, 712), 20.0))
+    x_other = dev(S.activations(40, k, 713, S.outlier_channels(k, 0.01, 712), 20.0))
+    y_eager = P.awq_linear_w4a16(x, qw, sc, qz, None, g=128)
+    torch.cuda.synchronize()
+    out = torch.empty_like(y_eager)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gr, stream=stream):
+            P.awq_linear_w4a16(x, qw, sc, qz, None, g=128, out=out)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(float("nan"))
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), y_eager.view(torch.int16)), i
+        y_mid = P.awq_linear_w4a16(x_other, qw, sc, qz, None, g=128)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(y_mid).all())
+
+
 # ----------------------------------------------------------------- linear groups
 
 

@@ -180,11 +180,11 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const ui
   awq_status st0 = check_linear_args("awq_linear_w4a16", x, qweight, scales, qzeros, inv_s16, m, n, k,
                                      g, y);
   if (st0 != AWQ_OK) return st0;
+  const awq::LinItem it{x, inv_s16, qweight, scales, qzeros, y, n};
   void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g, 1), &scratch);
+  awq_status st = get_scratch(awq::linear_group_scratch_bytes(&it, 1, m, k, g), &scratch);
   if (st != AWQ_OK) return st;
-  hipError_t e = awq::launch_linear(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, scratch,
-                                    (hipStream_t)stream);
+  hipError_t e = awq::launch_linear_group(&it, 1, m, k, g, scratch, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16 launch");
   return AWQ_OK;
 }
@@ -204,7 +204,7 @@ awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count, i
     li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
   }
   void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_scratch_bytes(m, k, g, count), &scratch);
+  awq_status st = get_scratch(awq::linear_group_scratch_bytes(li, count, m, k, g), &scratch);
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group launch");

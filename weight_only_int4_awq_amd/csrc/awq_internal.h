@@ -47,13 +47,11 @@ struct LinItem {
 };
 
 // Scratch bytes a call of count linears (same m, k, g) needs for the staged
-// activations.
+// activations (and, for m > 32, the scaled activations of every linear and the
+// fp32 partial tiles of the linears split along K).
 size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g, int count);
-
-hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
-                         const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
-                         int64_t n, int64_t k, int32_t g, uint16_t* y, void* scratch,
-                         hipStream_t stream);
+size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k,
+                                  int32_t g);
 
 // 1..kGroupMax independent linears of the same m, k and g: one launch for the
 // kernels that take groups (decode GEMV, fused skinny, prefill GEMM),

@@ -37,6 +37,16 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static int64_t gemm_row_chunk(int64_t k);
 
+static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k);
+
+size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k,
+                                  int32_t g) {
+  size_t total = linear_scratch_bytes(m, k, g, count);
+  if (m > 32)
+    for (int l = 0; l < count; ++l) total += gemm_part_bytes(m, items[l].n, k);
+  return total;
+}
+
 size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g, int count) {
   if (m > 32) {                 // scaled, permuted activations: one slot per linear
     const size_t slot = align256((size_t)m * (size_t)k * 2);
@@ -219,6 +229,10 @@ struct LinGroup {
   int64_t n[kGroupMax];
   int32_t wg0[kGroupMax + 1];
   int32_t count;
+  // prefill GEMM only: slices of K per tile and fp32 partial tiles of the
+  // linears split along K (ks = 1: not split)
+  int32_t ks[kGroupMax];
+  float* part[kGroupMax];
 };
 struct LinPick {
   const uint16_t* x;
@@ -229,6 +243,8 @@ struct LinPick {
   uint16_t* y;
   int64_t n;
   int bid, grid;
+  int ks;
+  float* part;
 };
 // the linear that work-group (or tile) b of a group launch belongs to, and
 // b's index within that linear's range
@@ -247,6 +263,8 @@ __device__ __forceinline__ LinPick pick_linear_at(const LinGroup& gp, int b) {
   L.n = gp.n[li];
   L.bid = b - gp.wg0[li];
   L.grid = gp.wg0[li + 1] - gp.wg0[li];
+  L.ks = gp.ks[li];
+  L.part = gp.part[li];
   return L;
 }
 __device__ __forceinline__ LinPick pick_linear(const LinGroup& gp) {
@@ -1447,7 +1465,8 @@ size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
 // ---------------------------------------------------------------- prefill GEMM
 // Work-group tile 256 tokens x 128 output columns, K-step 64, 4 waves in a
 // 2 x 2 arrangement, each wave 128 x 64 = 4 x 2 blocks of
-// v_mfma_f32_32x32x16_f16 (fp32 accumulators).
+// v_mfma_f32_32x32x16_f16 (fp32 accumulators); for few tokens a 64 x 128
+// tile, 4 waves side by side along N, each 64 x 32 = 2 x 1 blocks.
 //  * A (activations): linear_xprep first writes x_tilde = fp16(x * inv_s)
 //    once per call, every 8-channel chunk permuted into the nibble-unpack
 //    slot order.  Each K-step the work-group copies its 256 x 64 tile straight
@@ -1471,6 +1490,45 @@ constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 64;
 static int64_t gemm_row_chunk(int64_t k) {
   const int64_t c = (((int64_t)1 << 31) / (k * 2)) / kGemmBM * kGemmBM;
   return c > 0 ? c : kGemmBM;
+}
+
+#ifndef AWQ_GEMM_SMALL_M
+#define AWQ_GEMM_SMALL_M 128
+#endif
+#ifndef AWQ_GEMM_SPLIT_TARGET
+#define AWQ_GEMM_SPLIT_TARGET 256
+#endif
+// tile rows: 64 for few tokens (the 256-row tile would be mostly padding)
+static int gemm_bm(int64_t m) { return m <= AWQ_GEMM_SMALL_M ? 64 : kGemmBM; }
+
+// Slices of K per tile for a linear whose tiles alone leave CUs idle: enough
+// slices for one work-group per CU, at least two K-steps each, at most 16.
+// With 64-row tiles (m <= 128) whenever the linear has fewer tiles than CUs;
+// with 256-row tiles up to 512 tokens and 64 tiles, or 128 tiles where K >=
+// 8192 makes a tile's K loop long (beyond that the partial tiles' round trip
+// costs more than the idle CUs: measured on the Llama-shaped linears).  A
+// property of the linear alone, so a group call computes every linear exactly
+// as a call of it alone.
+static int gemm_split(int64_t m, int64_t n, int64_t k) {
+  const int bm = gemm_bm(m);
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + kGemmBN - 1) / kGemmBN);
+  if (m > gemm_row_chunk(k) || tiles >= AWQ_GEMM_SPLIT_TARGET) return 1;
+  if (bm != 64 && (m > 512 || tiles > 128 || (tiles > 64 && k < 8192))) return 1;
+  const int64_t nk = k / kGemmBK;
+  int64_t sk = (AWQ_GEMM_SPLIT_TARGET + tiles - 1) / tiles;
+  const int64_t smax = nk / 2 < 16 ? nk / 2 : 16;
+  sk = sk < smax ? sk : smax;
+  return sk > 1 ? (int)sk : 1;
+}
+
+// fp32 partial tiles of a split linear: [tile][slice][min(m, 256) rows][128]
+static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k) {
+  const int sk = gemm_split(m, n, k);
+  if (sk == 1) return 0;
+  const int bm = gemm_bm(m);
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + kGemmBN - 1) / kGemmBN);
+  const int64_t rows_t = m < bm ? m : bm;
+  return align256((size_t)sk * (size_t)tiles * (size_t)rows_t * kGemmBN * 4);
 }
 #ifndef AWQ_GEMM_SWZ_SHIFT
 #define AWQ_GEMM_SWZ_SHIFT 1
@@ -1524,15 +1582,23 @@ size_t gemm_lds_bytes(int64_t k, int32_t g) {
 
 // A launch covers the tiles of up to kGroupMax linears (same m and k): tiles
 // [wg0[l], wg0[l+1]) belong to linear l, whose x is its x_tilde.
-template <int G>
+template <int G, int BM>
 __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, int64_t m,
                                                              int64_t k, int tiles_m) {
+  // BM = 256: waves 2 (M) x 2 (N), each 128 x 64 = 4 x 2 blocks of 32 x 32;
+  // BM = 64 (few tokens): waves 1 x 4, each 64 x 32 = 2 x 1 blocks
+  constexpr int WM = BM == 256 ? 2 : 1;
+  constexpr int WN = 4 / WM;
+  constexpr int RW = BM / WM, CW = kGemmBN / WN;    // rows and columns per wave
+  constexpr int BMB = RW / 32, BNB = CW / 32;       // 32 x 32 blocks per wave
+  constexpr int AR = BM / 32;                       // A copy instructions per wave (8 rows each)
+  static_assert(BM == 256 || BM == 64, "tile rows");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // two distinct stage objects: the compiler can see that the copies into one
   // stage never alias the fragment reads of the other, so it does not wait for
   // the copies before reading
-  __shared__ __attribute__((aligned(16))) uint16_t a_st0[kGemmBM * kGemmBK];
-  __shared__ __attribute__((aligned(16))) uint16_t a_st1[kGemmBM * kGemmBK];
+  __shared__ __attribute__((aligned(16))) uint16_t a_st0[BM * kGemmBK];
+  __shared__ __attribute__((aligned(16))) uint16_t a_st1[BM * kGemmBK];
   const int ng = (int)(k / G), nzw = (ng + 7) / 8;
   uint16_t* s_l = reinterpret_cast<uint16_t*>(smem);                          // [128][ng]
   const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
@@ -1540,7 +1606,7 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   // XCD-aware tile order: each XCD gets a contiguous range of tiles, M fastest,
   // so the work-groups that share a weight tile share that XCD's L2
   const int total = gp.wg0[gp.count];
@@ -1555,10 +1621,14 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
   const uint32_t* __restrict__ qzeros = L.qz;
   uint16_t* __restrict__ y = L.y;
   const int64_t n = L.n;
-  const int tm = L.bid % tiles_m, tn = L.bid / tiles_m;
-  const int64_t m0 = (int64_t)tm * kGemmBM, n0 = (int64_t)tn * kGemmBN;
+  // work-group L.bid of the linear: tile L.bid / ks, slice L.bid % ks of its K-steps
+  const int ks = L.ks;
+  const int tl = L.bid / ks, sl = L.bid - tl * ks;
+  const int tm = tl % tiles_m, tn = tl / tiles_m;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * kGemmBN;
   const int64_t kw_row = k / 8;
   const int nk = (int)(k / kGemmBK);
+  const int kt0 = (int)((int64_t)sl * nk / ks), kt1 = (int)((int64_t)(sl + 1) * nk / ks);
 
   // ---- scales and zero words of this tile's columns (rows of W)
   for (int i = tid; i < kGemmBN * ng; i += 256) {
@@ -1578,17 +1648,17 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
   // wave instruction fills 64 consecutive 16-byte LDS slots (8 rows x 8
   // chunks); lane i writes slot i, so the XOR swizzle of the chunk position is
   // applied on the global side: lane (row r, slot p) fetches logical chunk
-  // p ^ ((r >> S) & 7).  Wave w fills rows 64 w .. 64 w + 63 of the stage.
+  // p ^ ((r >> S) & 7).  Wave w fills rows BM/4 w .. BM/4 (w + 1) - 1 of the stage.
   // The activations arrive already scaled and slot-permuted (linear_xprep).
   typedef __attribute__((address_space(3))) void lds_void_t;
   const int a_lr = lane >> 3, a_p = lane & 7;
   // 32-bit byte offsets from the activation base (one launch covers fewer
   // than 2^31 bytes of x_tilde; the host splits larger M)
   const char* xbytes = reinterpret_cast<const char*>(x);
-  uint32_t a_off[8];
+  uint32_t a_off[AR];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int lrow = wave * 64 + 8 * i + a_lr;
+  for (int i = 0; i < AR; ++i) {
+    const int lrow = wave * (BM / 4) + 8 * i + a_lr;
     int64_t row = m0 + lrow;
     row = row < m ? row : m - 1;
     a_off[i] = (uint32_t)((row * k + (a_p ^ ((lrow >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 8) * 2);
@@ -1596,47 +1666,47 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
 #define AWQ_GEMM_LOAD_A(KT, STAGE_PTR)                                                  \
   {                                                                                     \
     const char* xk_ = xbytes + (int64_t)(KT) * kGemmBK * 2;                             \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                       \
+    _Pragma("unroll") for (int i = 0; i < AR; ++i)                                      \
       __builtin_amdgcn_global_load_lds(                                                 \
           (const void*)(xk_ + a_off[i]),                                                \
-          (lds_void_t*)((STAGE_PTR) + (wave * 64 + 8 * i) * 64), 16, 0, 0);             \
+          (lds_void_t*)((STAGE_PTR) + (wave * (BM / 4) + 8 * i) * 64), 16, 0, 0);       \
   }
 
   // ---- B loader: lane (j = lane % 32, c = lane / 32) of block bn loads words 4c..4c+3
   const int bj = lane & 31, bc = lane >> 5;
-  const uint32_t* b_src[2];
+  const uint32_t* b_src[BNB];
 #pragma unroll
-  for (int bn = 0; bn < 2; ++bn) {
-    int64_t col = n0 + wn * 64 + bn * 32 + bj;
+  for (int bn = 0; bn < BNB; ++bn) {
+    int64_t col = n0 + wn * CW + bn * 32 + bj;
     col = col < n ? col : n - 1;
     b_src[bn] = qweight + col * kw_row + 4 * bc;
   }
-  uint4 wb0, wb1;
+  uint4 wb[BNB];
 #define AWQ_GEMM_LOAD_B(KT)                                                        \
   {                                                                                \
-    wb0 = *reinterpret_cast<const uint4*>(b_src[0] + (int64_t)(KT) * 8);           \
-    wb1 = *reinterpret_cast<const uint4*>(b_src[1] + (int64_t)(KT) * 8);           \
+    _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn)                             \
+      wb[bn] = *reinterpret_cast<const uint4*>(b_src[bn] + (int64_t)(KT) * 8);     \
   }
 
-  floatx16_t acc[4][2];
+  floatx16_t acc[BMB][BNB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BMB; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = floatx16_t{};
+    for (int jj = 0; jj < BNB; ++jj) acc[i][jj] = floatx16_t{};
 
-  AWQ_GEMM_LOAD_A(0, a_st0);
-  AWQ_GEMM_LOAD_B(0);
+  AWQ_GEMM_LOAD_A(kt0, a_st0);
+  AWQ_GEMM_LOAD_B(kt0);
   __builtin_amdgcn_s_waitcnt(0);       // the direct-to-LDS copies have landed
   __syncthreads();
   const UnpackConsts uc = unpack_consts();
   // byte offset of this lane's A fragment of row block bm at sub-step 0: row
-  // r = wm 128 + bm 32 + lane % 32 holds logical chunk ch = 4 (lane / 32) + s
+  // r = wm RW + bm 32 + lane % 32 holds logical chunk ch = 4 (lane / 32) + s
   // at physical chunk ch ^ ((r >> S) & 7); s only flips chunk bits 0-1, so
   // sub-step s reads a_base[bm] ^ (16 s)
-  uint32_t a_base[4];
+  uint32_t a_base[BMB];
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
-    const int row = wm * 128 + bm * 32 + (lane & 31);
+  for (int bm = 0; bm < BMB; ++bm) {
+    const int row = wm * RW + bm * 32 + (lane & 31);
     a_base[bm] = (uint32_t)(row * 128 + ((4 * bc) ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 16);
   }
 
@@ -1647,36 +1717,36 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
   // copies and meet at the barrier.
 #define AWQ_GEMM_A_READ(CUR, S, DST)                                                    \
   {                                                                                     \
-    _Pragma("unroll") for (int bm = 0; bm < 4; ++bm)                                    \
+    _Pragma("unroll") for (int bm = 0; bm < BMB; ++bm)                                  \
       DST[bm] = *reinterpret_cast<const half8_t*>(                                      \
           reinterpret_cast<const char*>(CUR) + (a_base[bm] ^ (uint32_t)(16 * (S))));     \
   }
 #define AWQ_GEMM_STEP(KT, CUR, NXT)                                                     \
   {                                                                                     \
-    const uint4 wc0 = wb0, wc1 = wb1;                                                   \
-    const int ktn_ = (KT) + 1 < nk ? (KT) + 1 : (KT);                                  \
+    uint4 wc[BNB];                                                                      \
+    _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) wc[bn] = wb[bn];                 \
+    const int ktn_ = (KT) + 1 < kt1 ? (KT) + 1 : (KT);                                 \
     AWQ_GEMM_LOAD_A(ktn_, NXT);                                                         \
     AWQ_GEMM_LOAD_B(ktn_);                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     const int grp = ((KT) * kGemmBK + 32 * bc) / G;                                     \
-    half2_t dd[2], o1024[2], o64[2];                                                    \
-    _Pragma("unroll") for (int bn = 0; bn < 2; ++bn) {                                  \
-      const int r = wn * 64 + bn * 32 + bj;                                             \
+    half2_t dd[BNB], o1024[BNB], o64[BNB];                                              \
+    _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) {                                \
+      const int r = wn * CW + bn * 32 + bj;                                             \
       const float d = h2f(s_l[r * ng + grp]);                                           \
       const float z = (float)((z_l[r * nzw + (grp >> 3)] >> (4 * (grp & 7))) & 0xFu);   \
       dd[bn] = half2_t{(half_t)d, (half_t)d};                                           \
       o1024[bn] = half2_t{(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};             \
       o64[bn] = half2_t{(half_t)(-64.0f - z), (half_t)(-64.0f - z)};                    \
     }                                                                                   \
-    const uint32_t ww0[4] = {wc0.x, wc0.y, wc0.z, wc0.w};                               \
-    const uint32_t ww1[4] = {wc1.x, wc1.y, wc1.z, wc1.w};                               \
-    half8_t af[4];                                                                      \
+    half8_t af[BMB];                                                                    \
     AWQ_GEMM_A_READ(CUR, 0, af)                                                         \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                     \
-      half8_t bq[2];                                                                    \
-      _Pragma("unroll") for (int bn = 0; bn < 2; ++bn) {                                \
+      half8_t bq[BNB];                                                                  \
+      _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) {                              \
+        const uint32_t wsel = s == 0 ? wc[bn].x : s == 1 ? wc[bn].y : s == 2 ? wc[bn].z : wc[bn].w; \
         uint32_t u[4];                                                                  \
-        unpack_word(bn == 0 ? ww0[s] : ww1[s], u, uc);                                  \
+        unpack_word(wsel, u, uc);                                                       \
         const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + o1024[bn]) * dd[bn];    \
         const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + o64[bn]) * dd[bn];      \
         const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + o1024[bn]) * dd[bn];    \
@@ -1686,8 +1756,8 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
                                 __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3))); \
       }                                                                                 \
       /* each A fragment is reloaded for the next sub-step right after its last use */  \
-      _Pragma("unroll") for (int bm = 0; bm < 4; ++bm) {                                \
-        _Pragma("unroll") for (int bn = 0; bn < 2; ++bn)                                \
+      _Pragma("unroll") for (int bm = 0; bm < BMB; ++bm) {                              \
+        _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn)                              \
           acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bm], bq[bn], acc[bm][bn], 0, 0, 0); \
         if (s + 1 < 4)                                                                  \
           af[bm] = *reinterpret_cast<const half8_t*>(                                   \
@@ -1697,28 +1767,99 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
     __builtin_amdgcn_s_waitcnt(0);                                                      \
     __syncthreads();                                                                    \
   }
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
+  int kt = kt0;
+  for (; kt + 1 < kt1; kt += 2) {
     AWQ_GEMM_STEP(kt, a_st0, a_st1);
     AWQ_GEMM_STEP(kt + 1, a_st1, a_st0);
   }
-  if (kt < nk) AWQ_GEMM_STEP(kt, a_st0, a_st1);
+  if (kt < kt1) AWQ_GEMM_STEP(kt, a_st0, a_st1);
 #undef AWQ_GEMM_STEP
 #undef AWQ_GEMM_A_READ
 #undef AWQ_GEMM_LOAD_A
 #undef AWQ_GEMM_LOAD_B
 
   // ---- epilogue: value e of lane l in block (bm, bn) is row 8(e/4) + 4(l/32) + e%4, column l%32
+  if (ks == 1) {
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < BMB; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 2; ++bn)
+      for (int bn = 0; bn < BNB; ++bn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t t = m0 + wm * RW + bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+          const int64_t cidx = n0 + wn * CW + bn * 32 + (lane & 31);
+          if (t < m && cidx < n) y[t * n + cidx] = f2h_rn(acc[bm][bn][e]);
+        }
+    return;
+  }
+  // split along K: the fp32 partial tile (its valid rows) goes to slice sl of
+  // the tile's partials; linear_gemm_reduce_kernel, the next launch, sums the
+  // slices in slice order
+  const int rows_t = m < BM ? (int)m : BM;                   // partial rows per tile
+  const int mrow = (m - m0) < rows_t ? (int)(m - m0) : rows_t;
+  float* __restrict__ part = L.part + ((size_t)tl * ks + sl) * rows_t * kGemmBN;
+#pragma unroll
+  for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < BNB; ++bn)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t t = m0 + wm * 128 + bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
-        const int64_t cidx = n0 + wn * 64 + bn * 32 + (lane & 31);
-        if (t < m && cidx < n) y[t * n + cidx] = f2h_rn(acc[bm][bn][e]);
+        const int row = wm * RW + bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+        const int col = wn * CW + bn * 32 + (lane & 31);
+        // the element goes through a scalar first (a bit cast of an element of
+        // a vector value reads the vector's first element on this compiler)
+        const float v = acc[bm][bn][e];
+        if (row < mrow) part[row * kGemmBN + col] = v;
       }
+}
+
+// Sums the K slices of the split linears of a GEMM launch (linear
+// blockIdx.y; a linear that was not split has no work here): every thread
+// takes 4 adjacent columns of one row of one tile and adds the slices in
+// slice order, all slice loads of a batch of 8 in flight together.
+template <int BM>
+__global__ __launch_bounds__(256) void linear_gemm_reduce_kernel(const LinGroup gp, int64_t m,
+                                                                 int tiles_m) {
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < kGroupMax; ++i)
+    if (i == (int)blockIdx.y) li = i;
+  const int ks = gp.ks[li];
+  if (ks == 1) return;
+  const int64_t n = gp.n[li];
+  const float* __restrict__ part = gp.part[li];
+  uint16_t* __restrict__ y = gp.y[li];
+  const int rows_t = m < BM ? (int)m : BM;
+  const int tiles = tiles_m * (int)((n + kGemmBN - 1) / kGemmBN);
+  const int64_t chunks = (int64_t)tiles * rows_t * (kGemmBN / 4);
+  const size_t slice_floats = (size_t)rows_t * kGemmBN;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
+    const int tl = (int)(c / ((int64_t)rows_t * (kGemmBN / 4)));
+    const int w = (int)(c - (int64_t)tl * rows_t * (kGemmBN / 4));
+    const int row = w / (kGemmBN / 4), c4 = (w - row * (kGemmBN / 4)) * 4;
+    const int tm = tl % tiles_m, tn = tl / tiles_m;
+    const int64_t t = (int64_t)tm * BM + row, col = (int64_t)tn * kGemmBN + c4;
+    if (t >= m) continue;
+    const float* src = part + (size_t)tl * ks * slice_floats + (size_t)row * kGemmBN + c4;
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ks; s0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ks) v[j] = *reinterpret_cast<const float4*>(src + (size_t)(s0 + j) * slice_floats);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < ks) {
+          sum[0] += v[j].x;
+          sum[1] += v[j].y;
+          sum[2] += v[j].z;
+          sum[3] += v[j].w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (col + i < n) y[t * n + col + i] = f2h_rn(sum[i]);
+  }
 }
 
 // Work-groups of a group launch: the grid one launch of all the column blocks
@@ -1877,11 +2018,13 @@ template <int G>
 static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, int64_t k,
                                     void* scratch, hipStream_t stream) {
   const size_t lds = gemm_lds_bytes(k, G);
-  const size_t lds_static = (size_t)2 * kGemmBM * kGemmBK * 2;
+  const int bm = gemm_bm(m);
+  const size_t lds_static = (size_t)2 * bm * kGemmBK * 2;
+  const void* fn = bm == 64 ? reinterpret_cast<const void*>(&linear_gemm_kernel<G, 64>)
+                            : reinterpret_cast<const void*>(&linear_gemm_kernel<G, kGemmBM>);
   if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
   if (lds + lds_static > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_gemm_kernel<G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const size_t slot_bytes = align256((size_t)m * (size_t)k * 2);
@@ -1904,9 +2047,11 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
                        stream, xg, m, k);
     for (int64_t r0 = 0; r0 < m; r0 += chunk) {
       const int64_t mc = (m - r0) < chunk ? (m - r0) : chunk;
-      const int tiles_m = (int)((mc + kGemmBM - 1) / kGemmBM);
+      const int tiles_m = (int)((mc + bm - 1) / bm);
       LinGroup gg = {};
       int total = 0;
+      bool split = false;
+      char* part = static_cast<char*>(scratch) + (size_t)cnt * slot_bytes;
       for (int l = 0; l < cnt; ++l) {
         const int64_t n = its[l].n;
         gg.x[l] = xg.y[l] + r0 * k;
@@ -1916,12 +2061,34 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
         gg.y[l] = its[l].y + r0 * n;
         gg.n[l] = n;
         gg.wg0[l] = total;
-        total += tiles_m * (int)((n + kGemmBN - 1) / kGemmBN);
+        // split along K only where the whole m is one launch (mc == m)
+        const int sk = whole ? gemm_split(m, n, k) : 1;
+        gg.ks[l] = sk;
+        if (sk > 1) {
+          gg.part[l] = reinterpret_cast<float*>(part);
+          part += gemm_part_bytes(m, n, k);
+          split = true;
+        }
+        total += tiles_m * (int)((n + kGemmBN - 1) / kGemmBN) * sk;
       }
       for (int l = cnt; l <= kGroupMax; ++l) gg.wg0[l] = total;
       gg.count = cnt;
-      hipLaunchKernelGGL(linear_gemm_kernel<G>, dim3((unsigned)total), dim3(256), lds, stream, gg,
-                         mc, k, tiles_m);
+      if (bm == 64)
+        hipLaunchKernelGGL((linear_gemm_kernel<G, 64>), dim3((unsigned)total), dim3(256), lds, stream,
+                           gg, mc, k, tiles_m);
+      else
+        hipLaunchKernelGGL((linear_gemm_kernel<G, kGemmBM>), dim3((unsigned)total), dim3(256), lds,
+                           stream, gg, mc, k, tiles_m);
+      if (split) {
+        // the slices of every split linear (a few MB of fp32 partials, still
+        // in the caches): a grid over the chip per linear
+        const dim3 rg(256u, (unsigned)cnt);
+        if (bm == 64)
+          hipLaunchKernelGGL((linear_gemm_reduce_kernel<64>), rg, dim3(256), 0, stream, gg, mc, tiles_m);
+        else
+          hipLaunchKernelGGL((linear_gemm_reduce_kernel<kGemmBM>), rg, dim3(256), 0, stream, gg, mc,
+                             tiles_m);
+      }
     }
   }
   return hipGetLastError();
@@ -1959,7 +2126,7 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
       if (nb16 > 0 && pc16 >= 1) { waves = 16; nb_cap = nb16; per_cu = pc16; }
     }
     if (nb_cap > 0 && per_cu >= 1) {
-      LinGroup gp;
+      LinGroup gp = {};
       const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
       const size_t lds = gemv_lds_bytes(k, G, nb, waves);
       const bool szv = scales_octets(items, count, ng_all);
@@ -2005,7 +2172,7 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
     if (nb_cap > 0) {
       int64_t per_cu = (int64_t)(160 * 1024) / (int64_t)skinny_fused_lds_bytes(k, G, nb_cap, tcs);
       per_cu = per_cu < 2 ? per_cu : 2;
-      LinGroup gp;
+      LinGroup gp = {};
       const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
       const size_t lds = skinny_fused_lds_bytes(k, G, nb, tcs);
       const bool szv = scales_octets(items, count, ng_all);
@@ -2075,13 +2242,6 @@ hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64
     default:
       return launch_linear_group_g<128>(items, count, m, k, scratch, stream);
   }
-}
-
-hipError_t launch_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
-                         const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
-                         int64_t k, int32_t g, uint16_t* y, void* scratch, hipStream_t stream) {
-  const LinItem it{x, inv_s16, qweight, scales, qzeros, y, n};
-  return launch_linear_group(&it, 1, m, k, g, scratch, stream);
 }
 
 }  // namespace awq
