@@ -7,9 +7,9 @@ One step is one pass of the whole path over one batch of synthetic input:
             tokens each), awq_search_scale (20-point alpha grid, g = 128) and
             awq_pack_int4 for its 7 linears, written back into the stack;
   decode    the whole 32-layer stack (7 linears per layer: q, k and v in one
-            awq_linear_w4a16_group call, o, gate and up in one group call,
-            down; 128 calls, replayed as one HIP graph each) at M = 1, 8 and
-            32 tokens with g = 128, and at M = 1 and 32 with g = 64;
+            awq_linear_w4a16_group call; o; gate and up in one group call;
+            down; 128 calls, replayed as one HIP graph each) at M = 1, 8, 32
+            and 128 tokens with g = 128, and at M = 1 and 32 with g = 64;
   prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
             in the decode (4 calls, each one activation-prep launch and one
             GEMM launch over the tiles of its linears);
@@ -171,7 +171,7 @@ def main():
 
     # decode inputs: one token batch per distinct input per layer
     XR = {}
-    for m in (1, 8, 32):
+    for m in (1, 8, 32, 128):
         XR[m] = []
         for layer in range(L):
             d = {}
@@ -181,7 +181,7 @@ def main():
                 d[inp] = S.torch_activations(m, kin[inp], S.seed_of(5, layer, slot, 2) + 7 * m, ch, 20.0, dev)
             XR[m].append(d)
     YR = {m: [[torch.empty((m, n), dtype=torch.float16, device=dev) for nm, n, k in shapes]
-              for _ in range(L)] for m in (1, 8, 32)}
+              for _ in range(L)] for m in (1, 8, 32, 128)}
 
     # a decode step: the linears that read the same input (q, k, v; gate,
     # up) are independent and run as one group call; o and down alone
@@ -204,7 +204,7 @@ def main():
                                   st[layer][li + len(shapes)][2], YR[m][layer][li]))
                 P.awq_linear_w4a16_group(items, g=g)
 
-    decode_cases = [(128, 1), (128, 8), (128, 32), (64, 1), (64, 32)]
+    decode_cases = [(128, 1), (128, 8), (128, 32), (128, 128), (64, 1), (64, 32)]
     for g, m in decode_cases:        # eager run first: allocates the library scratch
         decode(g, m)
     torch.cuda.synchronize()
@@ -365,10 +365,10 @@ def main():
         "dtype": "f16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations with 1% x20 outlier channels)",
         "config": {"workload": "llama3-8b-shaped linear stack: producer (calib 512 tok, 20-pt alpha "
-                               "search, int4 g128 pack) on one layer + 32-layer decode at M=1/8/32 "
+                               "search, int4 g128 pack) on one layer + 32-layer decode at M=1/8/32/128 "
                                "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048 + llama3-70b-"
                                "shaped linears at M=1/16 (cold copies)",
-                   "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32],
+                   "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32, 128],
                    "m_prefill": 2048, "m_calib": m_cal, "n_grid": n_grid, "group_size": [128, 64]},
         "gemm_tflops_m2048": round(rows["prefill_m2048"]["TFLOPs"], 2),
         "gemv_70b_big_pair_m1": big_pair,
