@@ -39,11 +39,25 @@ static int64_t gemm_row_chunk(int64_t k);
 
 static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k);
 
+static bool skinny_wide(const LinItem& it, int64_t m, int64_t k);
+
 size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k,
                                   int32_t g) {
   size_t total = linear_scratch_bytes(m, k, g, count);
-  if (m > 32)
+  if (m > 32) {
     for (int l = 0; l < count; ++l) total += gemm_part_bytes(m, items[l].n, k);
+  } else if (m > 16) {
+    // wide linears run the GEMM: x_tilde slots and partial tiles
+    size_t gemm = 0;
+    int nw = 0;
+    for (int l = 0; l < count; ++l)
+      if (skinny_wide(items[l], m, k)) {
+        gemm += gemm_part_bytes(m, items[l].n, k);
+        ++nw;
+      }
+    gemm += (size_t)nw * align256((size_t)m * (size_t)k * 2);
+    total = total > gemm ? total : gemm;
+  }
   return total;
 }
 
@@ -2009,6 +2023,13 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   return hipGetLastError();
 }
 
+// 17 <= m <= 32: a linear that a call of it alone would not run fused (more
+// than 16 MiB of packed weights) and that is wide (at least 12288 columns)
+// takes the GEMM.  A property of the linear alone, as every plan choice.
+static bool skinny_wide(const LinItem& it, int64_t m, int64_t k) {
+  return m > 16 && m <= 32 && it.n >= 12288 && it.n * k / 2 > ((int64_t)16 << 20);
+}
+
 // The prefill GEMM of a group (m > 32): x_tilde of every linear into a
 // scratch slot of its own (one launch for all), then one GEMM launch over
 // the tiles of all linears.  The kernel addresses its activations with 32-bit
@@ -2097,6 +2118,8 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
 template <int G>
 static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t m, int64_t k,
                                         void* scratch, hipStream_t stream) {
+  // fused skinny plan above 16 tokens: groups of at most this many packed bytes
+  constexpr int64_t kFusedMax = (int64_t)16 << 20;
   if (m > 32) return launch_gemm_group<G>(items, count, m, k, scratch, stream);
   // the decode GEMV (m = 1): at most kGemvMaxBlk column blocks per
   // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
@@ -2162,7 +2185,7 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
   // gate/up, down and the 70B-shaped linears faster staged).
   int64_t packed_bytes = 0;
   for (int l = 0; l < count; ++l) packed_bytes += items[l].n * k / 2;
-  if (off32 && m >= 2 && (m <= 16 || (m <= 32 && packed_bytes <= ((int64_t)16 << 20)))) {
+  if (off32 && m >= 2 && (m <= 16 || (m <= 32 && packed_bytes <= kFusedMax))) {
     const int tcs = m <= 16 ? 1 : 2;
     const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
     int nb_cap = kGemvMaxBlk;
@@ -2219,6 +2242,27 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
 #undef AWQ_SKF
 #undef AWQ_SKG
       return hipGetLastError();
+    }
+  }
+  // 17 <= m <= 32: wide linears that do not take the fused kernel run as one
+  // grouped GEMM launch (64-row tiles, split along K), which streams their
+  // weights faster than the staged skinny pair (measured: gate/up 67 -> 40 us,
+  // 70B-shaped gate/up 93 -> 70 us at 32 tokens); the others as calls alone
+  if (m > 16 && m <= 32) {
+    LinItem wide[kGroupMax], rest[kGroupMax];
+    int nw = 0, nr = 0;
+    for (int l = 0; l < count; ++l) {
+      if (skinny_wide(items[l], m, k)) wide[nw++] = items[l];
+      else rest[nr++] = items[l];
+    }
+    if (nw > 0) {
+      hipError_t e = launch_gemm_group<G>(wide, nw, m, k, scratch, stream);
+      if (e != hipSuccess) return e;
+      for (int l = 0; l < nr; ++l) {
+        e = launch_linear_group_g<G>(rest + l, 1, m, k, scratch, stream);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
   }
   // every other case: one linear after another on the stream, each planned as
