@@ -1614,9 +1614,11 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
   __shared__ __attribute__((aligned(16))) uint16_t a_st0[BM * kGemmBK];
   __shared__ __attribute__((aligned(16))) uint16_t a_st1[BM * kGemmBK];
   const int ng = (int)(k / G), nzw = (ng + 7) / 8;
-  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem);                          // [128][ng]
+  // scales and zero words of the tile's columns, column fastest: the lanes of
+  // a wave read 32 consecutive columns of one group (no bank conflicts)
+  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem);                          // [ng][128]
   const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
-  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + s_bytes);                // [128][nzw]
+  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + s_bytes);                // [nzw][128]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1649,13 +1651,13 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
     const int r = i / ng, gg = i % ng;
     int64_t col = n0 + r;
     col = col < n ? col : n - 1;
-    s_l[i] = scales[col * ng + gg];
+    s_l[gg * kGemmBN + r] = scales[col * ng + gg];
   }
   for (int i = tid; i < kGemmBN * nzw; i += 256) {
     const int r = i / nzw, w = i % nzw;
     int64_t col = n0 + r;
     col = col < n ? col : n - 1;
-    z_l[i] = qzeros[col * nzw + w];
+    z_l[w * kGemmBN + r] = qzeros[col * nzw + w];
   }
 
   // ---- A loader: direct global -> LDS copies (global_load_lds_dwordx4).  One
@@ -1747,8 +1749,8 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
     half2_t dd[BNB], o1024[BNB], o64[BNB];                                              \
     _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) {                                \
       const int r = wn * CW + bn * 32 + bj;                                             \
-      const float d = h2f(s_l[r * ng + grp]);                                           \
-      const float z = (float)((z_l[r * nzw + (grp >> 3)] >> (4 * (grp & 7))) & 0xFu);   \
+      const float d = h2f(s_l[grp * kGemmBN + r]);                                      \
+      const float z = (float)((z_l[(grp >> 3) * kGemmBN + r] >> (4 * (grp & 7))) & 0xFu); \
       dd[bn] = half2_t{(half_t)d, (half_t)d};                                           \
       o1024[bn] = half2_t{(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};             \
       o64[bn] = half2_t{(half_t)(-64.0f - z), (half_t)(-64.0f - z)};                    \
