@@ -385,6 +385,19 @@ def test_linear_split_k_full_size_sampled(P, m):
         assert ok, (m, n, k, worst, raw)
 
 
+@pytest.mark.parametrize("m,k,g", [(40, 14336, 32), (300, 14336, 32), (2048, 28672, 32), (64, 28672, 64)])
+def test_linear_gemm_long_k_small_groups(P, m, k, g):
+    # the scales and zero words of a tile's whole K range exceed LDS (K / g up
+    # to 896 groups): the GEMM splits K until one slice's groups fit, at any m
+    n = 264
+    w = S.weights(n, k, 0.02, 720 + k // g)
+    xc = S.activations(64, k, 721, S.outlier_channels(k, 0.01, 722), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.35)
+    x = S.activations(m, k, 723 + m, S.outlier_channels(k, 0.01, 722), 20.0)
+    cols = np.unique(np.concatenate([np.arange(0, 8), np.arange(128, 136), np.arange(n - 8, n)]))
+    _check_linear(P, w, x, s16, g, cols=None if m <= 300 else cols)
+
+
 def test_linear_split_k_graph_replays(P):
     # a captured split-K call (GEMM launch + slice-sum launch over scratch
     # partials) replayed several times, with eager calls of other sizes in

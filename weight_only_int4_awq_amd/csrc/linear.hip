@@ -37,7 +37,7 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static int64_t gemm_row_chunk(int64_t k);
 
-static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k);
+static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k, int32_t g);
 
 static bool skinny_wide(const LinItem& it, int64_t m, int64_t k);
 
@@ -45,14 +45,14 @@ size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, in
                                   int32_t g) {
   size_t total = linear_scratch_bytes(m, k, g, count);
   if (m > 32) {
-    for (int l = 0; l < count; ++l) total += gemm_part_bytes(m, items[l].n, k);
+    for (int l = 0; l < count; ++l) total += gemm_part_bytes(m, items[l].n, k, g);
   } else if (m > 16) {
     // wide linears run the GEMM: x_tilde slots and partial tiles
     size_t gemm = 0;
     int nw = 0;
     for (int l = 0; l < count; ++l)
       if (skinny_wide(items[l], m, k)) {
-        gemm += gemm_part_bytes(m, items[l].n, k);
+        gemm += gemm_part_bytes(m, items[l].n, k, g);
         ++nw;
       }
     gemm += (size_t)nw * align256((size_t)m * (size_t)k * 2);
@@ -247,6 +247,7 @@ struct LinGroup {
   // linears split along K (ks = 1: not split)
   int32_t ks[kGroupMax];
   float* part[kGroupMax];
+  int32_t gmax;                      // most groups of a K slice (LDS rows)
 };
 struct LinPick {
   const uint16_t* x;
@@ -1499,6 +1500,24 @@ size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
 //    once.  The next K-step's global loads are in flight while the current
 //    one is multiplied.
 constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 64;
+constexpr int kGemmSRow = kGemmBN + 2, kGemmZRow = kGemmBN + 1;   // padded LDS rows
+
+// dynamic LDS of the GEMM (the two activation stages are static): the
+// scales [gmax][kGemmSRow] halves and zero words [gmax / 8 + 2][kGemmZRow] of
+// the groups one K slice spans
+__host__ __device__ inline size_t gemm_s_bytes(int gmax) {
+  return ((size_t)kGemmSRow * gmax * 2 + 15) & ~(size_t)15;
+}
+static size_t gemm_lds_bytes(int gmax) {
+  return gemm_s_bytes(gmax) + (size_t)kGemmZRow * (gmax / 8 + 2) * 4;
+}
+// most groups a slice of ks slices of the K-steps spans
+static int gemm_slice_groups(int64_t k, int32_t g, int ks) {
+  const int64_t nk = k / kGemmBK;
+  const int64_t steps = (nk + ks - 1) / ks;
+  return (int)((steps * kGemmBK + g - 1) / g + 1);
+}
+static size_t gemm_static_lds(int bm) { return (size_t)2 * bm * kGemmBK * 2; }
 
 // rows of one GEMM launch: its x_tilde stays below 2^31 bytes
 static int64_t gemm_row_chunk(int64_t k) {
@@ -1523,7 +1542,7 @@ static int gemm_bm(int64_t m) { return m <= AWQ_GEMM_SMALL_M ? 64 : kGemmBM; }
 // costs more than the idle CUs: measured on the Llama-shaped linears).  A
 // property of the linear alone, so a group call computes every linear exactly
 // as a call of it alone.
-static int gemm_split(int64_t m, int64_t n, int64_t k) {
+static int gemm_split_occupancy(int64_t m, int64_t n, int64_t k) {
   const int bm = gemm_bm(m);
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + kGemmBN - 1) / kGemmBN);
   if (m > gemm_row_chunk(k) || tiles >= AWQ_GEMM_SPLIT_TARGET) return 1;
@@ -1534,11 +1553,22 @@ static int gemm_split(int64_t m, int64_t n, int64_t k) {
   sk = sk < smax ? sk : smax;
   return sk > 1 ? (int)sk : 1;
 }
+// Also split where the scales and zero words of a tile's whole K range would
+// not fit LDS (long K with small groups: K / g beyond about 300); 0 when that
+// would need a split and the call's activations are too large for one launch.
+static int gemm_split(int64_t m, int64_t n, int64_t k, int32_t g) {
+  int sk = gemm_split_occupancy(m, n, k);
+  const int64_t nk = k / kGemmBK;
+  const size_t budget = (size_t)160 * 1024 - gemm_static_lds(gemm_bm(m));
+  while (gemm_lds_bytes(gemm_slice_groups(k, g, sk)) > budget && sk < nk) ++sk;
+  if (sk > 1 && m > gemm_row_chunk(k)) return 0;
+  return sk;
+}
 
 // fp32 partial tiles of a split linear: [tile][slice][min(m, 256) rows][128]
-static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k) {
-  const int sk = gemm_split(m, n, k);
-  if (sk == 1) return 0;
+static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k, int32_t g) {
+  const int sk = gemm_split(m, n, k, g);
+  if (sk <= 1) return 0;
   const int bm = gemm_bm(m);
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + kGemmBN - 1) / kGemmBN);
   const int64_t rows_t = m < bm ? m : bm;
@@ -1587,15 +1617,6 @@ __global__ __launch_bounds__(256) void linear_xprep_kernel(const LinGroup gp, in
   }
 }
 
-// dynamic LDS of the GEMM (the two activation stages are static: 64 KiB)
-size_t gemm_lds_bytes(int64_t k, int32_t g) {
-  const size_t ng = (size_t)(k / g), nzw = (ng + 7) / 8;
-  const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
-  return s_bytes + (size_t)kGemmBN * nzw * 4;
-}
-
-// A launch covers the tiles of up to kGroupMax linears (same m and k): tiles
-// [wg0[l], wg0[l+1]) belong to linear l, whose x is its x_tilde.
 template <int G, int BM>
 __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, int64_t m,
                                                              int64_t k, int tiles_m) {
@@ -1614,11 +1635,13 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
   __shared__ __attribute__((aligned(16))) uint16_t a_st0[BM * kGemmBK];
   __shared__ __attribute__((aligned(16))) uint16_t a_st1[BM * kGemmBK];
   const int ng = (int)(k / G), nzw = (ng + 7) / 8;
-  // scales and zero words of the tile's columns, column fastest: the lanes of
-  // a wave read 32 consecutive columns of one group (no bank conflicts)
-  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem);                          // [ng][128]
-  const size_t s_bytes = ((size_t)kGemmBN * ng * 2 + 15) & ~(size_t)15;
-  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + s_bytes);                // [nzw][128]
+  // scales and zero words of the tile's columns for the groups of this
+  // work-group's K slice, column fastest with a padded row (kGemmSRow halves,
+  // kGemmZRow words): the lanes of a wave read 32 consecutive columns of one
+  // group, and the staging writes of consecutive groups of one column land in
+  // different banks.  Sized on the host for the longest slice of the launch.
+  uint16_t* s_l = reinterpret_cast<uint16_t*>(smem);                          // [gmax][kGemmSRow]
+  uint32_t* z_l = reinterpret_cast<uint32_t*>(smem + gemm_s_bytes(gp.gmax));  // [gmax/8+2][kGemmZRow]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1647,17 +1670,21 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
   const int kt0 = (int)((int64_t)sl * nk / ks), kt1 = (int)((int64_t)(sl + 1) * nk / ks);
 
   // ---- scales and zero words of this tile's columns (rows of W)
-  for (int i = tid; i < kGemmBN * ng; i += 256) {
-    const int r = i / ng, gg = i % ng;
+  // (consecutive threads read consecutive groups of one column)
+  const int g0 = (kt0 * kGemmBK) / G, g1 = (kt1 * kGemmBK + G - 1) / G;
+  const int w0 = g0 >> 3, w1 = ((g1 - 1) >> 3) + 1;
+  const int gn = g1 - g0, wn_ = w1 - w0;
+  for (int i = tid; i < kGemmBN * gn; i += 256) {
+    const int r = i / gn, gi = i - r * gn;
     int64_t col = n0 + r;
     col = col < n ? col : n - 1;
-    s_l[gg * kGemmBN + r] = scales[col * ng + gg];
+    s_l[gi * kGemmSRow + r] = scales[col * ng + g0 + gi];
   }
-  for (int i = tid; i < kGemmBN * nzw; i += 256) {
-    const int r = i / nzw, w = i % nzw;
+  for (int i = tid; i < kGemmBN * wn_; i += 256) {
+    const int r = i / wn_, wi = i - r * wn_;
     int64_t col = n0 + r;
     col = col < n ? col : n - 1;
-    z_l[w * kGemmBN + r] = qzeros[col * nzw + w];
+    z_l[wi * kGemmZRow + r] = qzeros[col * nzw + w0 + wi];
   }
 
   // ---- A loader: direct global -> LDS copies (global_load_lds_dwordx4).  One
@@ -1749,8 +1776,8 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
     half2_t dd[BNB], o1024[BNB], o64[BNB];                                              \
     _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) {                                \
       const int r = wn * CW + bn * 32 + bj;                                             \
-      const float d = h2f(s_l[grp * kGemmBN + r]);                                      \
-      const float z = (float)((z_l[(grp >> 3) * kGemmBN + r] >> (4 * (grp & 7))) & 0xFu); \
+      const float d = h2f(s_l[(grp - g0) * kGemmSRow + r]);                             \
+      const float z = (float)((z_l[((grp >> 3) - w0) * kGemmZRow + r] >> (4 * (grp & 7))) & 0xFu); \
       dd[bn] = half2_t{(half_t)d, (half_t)d};                                           \
       o1024[bn] = half2_t{(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};             \
       o64[bn] = half2_t{(half_t)(-64.0f - z), (half_t)(-64.0f - z)};                    \
@@ -2040,9 +2067,20 @@ static bool skinny_wide(const LinItem& it, int64_t m, int64_t k) {
 template <int G>
 static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, int64_t k,
                                     void* scratch, hipStream_t stream) {
-  const size_t lds = gemm_lds_bytes(k, G);
   const int bm = gemm_bm(m);
-  const size_t lds_static = (size_t)2 * bm * kGemmBK * 2;
+  const int64_t chunk = gemm_row_chunk(k);
+  const bool whole = m <= chunk;
+  // slices of every linear (one when the call runs in row chunks), and the
+  // LDS for the longest slice of the launch
+  int sks[kGroupMax];
+  int gmax = 0;
+  for (int l = 0; l < count; ++l) {
+    sks[l] = whole ? gemm_split(m, items[l].n, k, G) : 1;
+    const int gl = gemm_slice_groups(k, G, sks[l]);
+    gmax = gmax > gl ? gmax : gl;
+  }
+  const size_t lds = gemm_lds_bytes(gmax);
+  const size_t lds_static = gemm_static_lds(bm);
   const void* fn = bm == 64 ? reinterpret_cast<const void*>(&linear_gemm_kernel<G, 64>)
                             : reinterpret_cast<const void*>(&linear_gemm_kernel<G, kGemmBM>);
   if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
@@ -2051,8 +2089,6 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
     if (e != hipSuccess) return e;
   }
   const size_t slot_bytes = align256((size_t)m * (size_t)k * 2);
-  const int64_t chunk = gemm_row_chunk(k);
-  const bool whole = m <= chunk;
   const int n_batch = whole ? 1 : count;
   for (int bt = 0; bt < n_batch; ++bt) {
     const LinItem* its = whole ? items : items + bt;
@@ -2085,17 +2121,18 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
         gg.n[l] = n;
         gg.wg0[l] = total;
         // split along K only where the whole m is one launch (mc == m)
-        const int sk = whole ? gemm_split(m, n, k) : 1;
+        const int sk = whole ? sks[l] : 1;
         gg.ks[l] = sk;
         if (sk > 1) {
           gg.part[l] = reinterpret_cast<float*>(part);
-          part += gemm_part_bytes(m, n, k);
+          part += gemm_part_bytes(m, n, k, G);
           split = true;
         }
         total += tiles_m * (int)((n + kGemmBN - 1) / kGemmBN) * sk;
       }
       for (int l = cnt; l <= kGroupMax; ++l) gg.wg0[l] = total;
       gg.count = cnt;
+      gg.gmax = gmax;
       if (bm == 64)
         hipLaunchKernelGGL((linear_gemm_kernel<G, 64>), dim3((unsigned)total), dim3(256), lds, stream,
                            gg, mc, k, tiles_m);
