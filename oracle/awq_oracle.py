@@ -266,6 +266,31 @@ def search_scale(w16: np.ndarray, x16: np.ndarray, a: np.ndarray, g: int = 128,
 
 
 # ----------------------------------------------------------------------------
+# shared scale over projections that read one input, with 1/s folded into the
+# operation that produces that input ([bjdmk] 融合模块优化: merging steps into
+# one operation; [jsqmd] 二.1 (3): the activation is divided by s at inference)
+
+
+def fold_inv_scale(v16: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """Per-channel weight of the elementwise operation that produces a linear's
+    input (for example a normalisation weight), with the linear's division by s
+    folded in: fp16_rn(v_k / s_k), the float64 quotient of two fp16 values
+    rounded once to fp16.  The linear then runs with inv_s16 = None on the
+    activations that operation produces.
+
+    A shared s for several projections of one input is search_scale on their
+    weights stacked along N (the loss sums over all their output rows).
+
+    Pinned by: s = 1 (identity), s a power of two (exact scaling), the exact
+    rational quotient rounded once for random pairs, and the joint loss equal
+    to the sum of the stacked projections' losses (tests/test_oracle_pins.py).
+    """
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        return fp16_rn(np.asarray(v16, np.float16).astype(np.float64) /
+                       np.asarray(s16, np.float16).astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
 # a5: real quantization and packing (layout v1)  ([csdn] 量化流程优化)
 
 

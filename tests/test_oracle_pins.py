@@ -343,3 +343,40 @@ def test_check_linear_floor():
     bad[0, 1] *= 1.01
     ok, worst, raw = O.check_linear(bad.astype(np.float16), yr)
     assert not ok
+
+
+# ---------------------------------------------------------------- shared scale, folded 1/s
+
+
+def test_fold_inv_scale_special_cases():
+    r = _rng(90)
+    v = (r.standard_normal(512) * 3.0).astype(np.float16)
+    assert np.array_equal(O.fold_inv_scale(v, np.ones(512, np.float16)).view(np.uint16), v.view(np.uint16))
+    for e in (-14, -3, 0, 2, 5):
+        s = np.full(512, 2.0 ** e, np.float16)
+        want = O.fp16_rn(v.astype(np.float64) * 2.0 ** -e)     # exact scaling, then one rounding
+        assert np.array_equal(O.fold_inv_scale(v, s).view(np.uint16), want.view(np.uint16))
+
+
+def test_fold_inv_scale_exact_quotient():
+    r = _rng(91)
+    v = (r.standard_normal(3000) * 10.0 ** r.integers(-4, 3, 3000)).astype(np.float16)
+    s = O.scale_candidate(np.abs(r.standard_normal(3000)) * 10.0 ** r.integers(-3, 3, 3000), 0.7)
+    got = O.fold_inv_scale(v, s)
+    for a, b, h in zip(v, s, got):
+        want = X.f16_round_exact(X.frac_of_f16(a) / X.frac_of_f16(b))
+        assert float(h) == want or (np.isinf(want) and np.isinf(float(h))), (a, b, float(h), want)
+
+
+def test_joint_loss_is_sum_of_stacked_projections():
+    # q, k, v read one input: with one s for all three, the loss of their
+    # stacked weights is the sum of their own losses, for every alpha
+    k, m, g = 64, 5, 32
+    ws = [S.weights(n, k, 0.02, 92 + n) for n in (6, 3, 2)]
+    x = S.activations(m, k, 95, S.outlier_channels(k, 0.05, 96), 20.0)
+    a = O.calib_stats(x)
+    for alpha in O.alpha_grid(20)[::4]:
+        s16 = O.scale_candidate(a, alpha)
+        parts = sum(O.search_loss(w, x, s16, g) for w in ws)
+        joint = O.search_loss(np.concatenate(ws), x, s16, g)
+        assert abs(joint - parts) <= 1e-12 * abs(parts)
