@@ -10,6 +10,9 @@ One step is one pass of the whole path over one batch of synthetic input:
             awq_linear_w4a16_group call; o; gate and up in one group call;
             down; 128 calls, replayed as one HIP graph each) at M = 1, 8, 32
             and 128 tokens with g = 128, and at M = 1 and 32 with g = 64;
+  shared s  the same stack at M = 1 with one s for q/k/v and one for gate/up
+            (searched on their weights stacked along N), each pair packed and
+            run as one linear on activations that already carry 1/s;
   prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
             in the decode (4 calls, each one activation-prep launch and one
             GEMM launch over the tiles of its linears);
@@ -47,11 +50,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def gemv_bytes(m, n, k, g):
+def gemv_bytes(m, n, k, g, inv=True):
     """Algorithmic bytes of one W4A16 linear call: packed weights, fp16 scales,
-    packed zero points, the fp16 activation and inv_s read once, the fp16 output
-    written once."""
-    return n * k // 2 + 2 * n * (k // g) + 4 * n * (-(-k // (8 * g))) + 2 * m * k + 2 * k + 2 * m * n
+    packed zero points, the fp16 activation and inv_s (when given) read once,
+    the fp16 output written once."""
+    return (n * k // 2 + 2 * n * (k // g) + 4 * n * (-(-k // (8 * g))) + 2 * m * k + (2 * k if inv else 0)
+            + 2 * m * n)
 
 
 def measured_traffic(root):
@@ -204,9 +208,48 @@ def main():
                                   st[layer][li + len(shapes)][2], YR[m][layer][li]))
                 P.awq_linear_w4a16_group(items, g=g)
 
+    # the stack with one shared s for q/k/v and one for gate/up (searched on
+    # their weights stacked along N, 128 calibration tokens), packed as one
+    # linear each and run on activations that already carry 1/s (folded into
+    # the producing operation's weight): inv_s16 absent for those two
+    fused = []
+    for layer in range(L):
+        row = []
+        for grp_names in (("q", "k", "v"), ("gate", "up")):
+            idx = [li for li, (nm, n, k) in enumerate(shapes) if nm in grp_names]
+            wst = torch.cat([W[layer][li] for li in idx], 0)
+            inp = S.INPUT_OF[grp_names[0]]
+            xc = XC[layer][inp][:128].contiguous()
+            ws = torch.empty(P.awq_search_workspace_size(wst.shape[0], wst.shape[1], 128, 128, n_grid),
+                             dtype=torch.uint8, device=dev)
+            _, s16f, _, _ = P.awq_search_scale(wst, xc, P.awq_calib_stats(xc), g=128, n_grid=n_grid,
+                                               workspace=ws)
+            qwf, scf, qzf, _ = P.awq_pack_int4(wst, s16f, g=128)
+            row.append((inp, qwf, scf, qzf))
+            del wst, ws
+        fused.append(row)
+    torch.cuda.synchronize()
+    YF = [[torch.empty((1, 6144), dtype=torch.float16, device=dev),
+           torch.empty((1, 28672), dtype=torch.float16, device=dev)] for _ in range(L)]
+    li_o = [li for li, (nm, n, k) in enumerate(shapes) if nm == "o"][0]
+    li_d = [li for li, (nm, n, k) in enumerate(shapes) if nm == "down"][0]
+
+    def decode_fused():
+        st = stacks[128]
+        for layer in range(L):
+            for fi, (inp, qwf, scf, qzf) in enumerate(fused[layer]):
+                P.awq_linear_w4a16(XR[1][layer][inp], qwf, scf, qzf, None, g=128, out=YF[layer][fi])
+                li = li_o if fi == 0 else li_d
+                nm = shapes[li][0]
+                qw, sc, qz, _ = st[layer][li]
+                P.awq_linear_w4a16(XR[1][layer][S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2],
+                                   g=128, out=YR[1][layer][li])
+
     decode_cases = [(128, 1), (128, 8), (128, 32), (128, 128), (64, 1), (64, 32)]
     for g, m in decode_cases:        # eager run first: allocates the library scratch
         decode(g, m)
+    torch.cuda.synchronize()
+    decode_fused()
     torch.cuda.synchronize()
     graphs = {}
     for g, m in decode_cases:
@@ -214,6 +257,10 @@ def main():
         with torch.cuda.graph(gr):
             decode(g, m)
         graphs[(g, m)] = gr
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        decode_fused()
+    graphs["fused"] = gr
     torch.cuda.synchronize()
     log("captured the decode graphs")
 
@@ -273,7 +320,7 @@ def main():
     torch.cuda.synchronize()
     log("packed and captured the 70B-shaped linears")
 
-    phases = (["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["prefill"] +
+    phases = (["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["decode_fused"] + ["prefill"] +
               [f"big_{big[bi][0]}_m{m}" for bi, m in big_cases])
     acc = {p: 0.0 for p in phases}
 
@@ -286,11 +333,13 @@ def main():
         for pi, (g, m) in enumerate(decode_cases):
             graphs[(g, m)].replay()
             ev[2 + pi].record(stream)
-        prefill(layer)
+        graphs["fused"].replay()
         ev[2 + len(decode_cases)].record(stream)
+        prefill(layer)
+        ev[3 + len(decode_cases)].record(stream)
         for ci, key in enumerate(big_cases):
             big_graphs[key].replay()
-            ev[3 + len(decode_cases) + ci].record(stream)
+            ev[4 + len(decode_cases) + ci].record(stream)
         if timed:
             return ev
         return None
@@ -323,6 +372,12 @@ def main():
         rows[f"decode_g{g}_m{m}"] = {"us_per_stack": t * 1e6, "us_per_linear": t * 1e6 / nlin,
                                      "GBps": bytes_by[(g, m)] / t / 1e9,
                                      "frac_hbm_peak": bytes_by[(g, m)] / t / 1e9 / HBM_PEAK_GBS}
+    t_f = acc["decode_fused"] / K
+    by_f = L * (gemv_bytes(1, 6144, 4096, 128, inv=False) + gemv_bytes(1, 28672, 4096, 128, inv=False)
+                + gemv_bytes(1, 4096, 4096, 128) + gemv_bytes(1, 4096, 14336, 128))
+    rows["decode_shared_s_g128_m1"] = {"us_per_stack": t_f * 1e6, "GBps": by_f / t_f / 1e9,
+                                       "frac_hbm_peak": by_f / t_f / 1e9 / HBM_PEAK_GBS,
+                                       "launches_per_stack": 4 * L}
     prefill_flops = sum(2 * 2048 * n * k for nm, n, k in shapes)
     t_pf = acc["prefill"] / K
     rows["prefill_m2048"] = {"us_per_layer": t_pf * 1e6, "TFLOPs": prefill_flops / t_pf / 1e12,

@@ -145,6 +145,25 @@ awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n,
                          int32_t* nonfinite_groups, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_fold_inv_scale -- fold a linear's division by s into the per-channel
+ * weight of the elementwise operation that produces its input (for example
+ * a normalisation weight), so that the linear runs with inv_s16 = NULL.
+ * Passage: jsqmd.com page, section 二.1 (3) (the activation is divided by s
+ * at inference so the product is unchanged) and bjdmk.com.cn page, section
+ * "融合模块优化" (merging computation steps into one operation).  Projections
+ * that read one input (q, k, v; gate, up) share one s when awq_search_scale
+ * runs on their weights stacked along N (its loss then sums over all their
+ * output rows) and awq_pack_int4 packs the stack as one linear.
+ *
+ *   out_k = fp16_rn(v_k / s16_k): the exact quotient rounded once to fp16.
+ *   v, s16   [k] fp16 (device); out [k] fp16 (device, may alias v).
+ *   Errors: NULL pointers, k < 1, pointers not 2-byte aligned.  s16_k = 0
+ *   gives +-inf (NaN for v_k = 0), as the division does.
+ * ------------------------------------------------------------------------- */
+awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k,
+                              uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_linear_w4a16 -- y = x_tilde W_deq^T with 4-bit weights and fp16
  * activations.
  * Passage: bjdmk.com.cn page, section "量化参数配置" / "技术选型决策树"

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for want in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
-                 "awq_pack_int4", "awq_linear_w4a16", "awq_last_error", "awq_abi_version"):
+                 "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group", "awq_fold_inv_scale",
+                 "awq_last_error", "awq_abi_version"):
         assert want in names, names
 
 
@@ -94,6 +95,15 @@ def test_search_argument_errors(lib):
     assert call(wsb=ws - 1) == 4
     assert call(ws=None) == 4
     assert call(ws=FAKE + 16) == 3
+
+
+def test_fold_argument_errors(lib):
+    assert _status(lib, "awq_fold_inv_scale", None, FAKE, 16, FAKE, None)[0] == 1
+    assert _status(lib, "awq_fold_inv_scale", FAKE, None, 16, FAKE, None)[0] == 1
+    assert _status(lib, "awq_fold_inv_scale", FAKE, FAKE, 16, None, None)[0] == 1
+    assert _status(lib, "awq_fold_inv_scale", FAKE, FAKE, 0, FAKE, None)[0] == 2
+    st, msg = _status(lib, "awq_fold_inv_scale", FAKE + 1, FAKE, 16, FAKE, None)
+    assert st == 3 and "aligned" in msg
 
 
 def test_pack_argument_errors(lib):

@@ -504,3 +504,71 @@ def test_linear_group_mixed_plan(P, m):
     specs = [(14336, 0.5, 570), (1024, 0.4, 580), (264, None, 590)]
     items, meta = _group_case(P, m, 4096, 128, specs, 600 + m)
     _check_group(P, items, meta, 4096, 128, cols_per=128)
+
+
+# ----------------------------------------------------------------- shared scale, folded 1/s
+
+
+def test_fold_inv_scale_bit_exact(P):
+    r = np.random.Generator(np.random.PCG64(800))
+    k = 4099
+    v = (r.standard_normal(k) * 10.0 ** r.integers(-5, 4, k)).astype(np.float16)
+    v[:5] = np.array([0.0, -0.0, 65504.0, 6e-8, -3e-5], np.float16)
+    s16 = O.scale_candidate(np.abs(r.standard_normal(k)) * 10.0 ** r.integers(-4, 4, k), 0.8)
+    s16[:3] = np.array([2.0 ** -14, 1.0, 300.0], np.float16)
+    want = O.fold_inv_scale(v, s16)
+    vd, sd = dev(v), dev(s16)
+    got = P.awq_fold_inv_scale(vd, sd)
+    P.awq_fold_inv_scale(vd, sd, out=vd)          # in place
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    assert np.array_equal(vd.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+def test_shared_scale_stacked_qkv_full_size(P):
+    # q, k and v of one Llama-3-8B-shaped layer read one input and share one s:
+    # awq_search_scale on their weights stacked along N (6144 x 4096, 128
+    # calibration tokens).  On the GPU its losses are the sums of the three
+    # per-linear searches' losses; on sampled rows of each part the search
+    # matches the oracle bit for bit; the stacked linear, run with inv_s16 absent
+    # on activations produced with the folded weight fp16_rn(gamma / s), matches
+    # the oracle on sampled columns.
+    parts = [S.config_layer(2, nm, n, k, 128, 8, 0.02, 0.01, 20.0) for nm, n, k in S.LLAMA3_8B_LINEARS[:3]]
+    x_cal, x_run = parts[0][1], parts[0][2]
+    for p_ in parts[1:]:
+        assert np.array_equal(p_[1], x_cal)        # one shared input
+    wst = np.concatenate([p_[0] for p_ in parts])
+    wd, xd = dev(wst), dev(x_cal)
+    a = P.awq_calib_stats(xd)
+    best, s16, inv, losses = P.awq_search_scale(wd, xd, a)
+    sums = [P.awq_search_scale(dev(p_[0]), xd, a)[3] for p_ in parts]
+    torch.cuda.synchronize()
+    tot = sum(v.cpu().numpy() for v in sums)
+    assert np.max(np.abs(tot - losses.cpu().numpy()) / tot) < 1e-12
+    rows = np.concatenate([np.arange(0, 4096, 64), 4096 + np.arange(0, 1024, 32), 5120 + np.arange(0, 1024, 32)])
+    _check_search(P, np.ascontiguousarray(wst[rows]), x_cal, 128, 20)
+    # the full stack's choice: the first minimum of its losses, and its s16 the
+    # oracle's candidate at that alpha
+    gl = losses.cpu().numpy()
+    assert int(best.item()) == O.select_best(gl)
+    s16_want = O.scale_candidate(O.calib_stats(x_cal), O.alpha_grid(20)[int(best.item())])
+    assert np.array_equal(s16.cpu().numpy().view(np.uint16), s16_want.view(np.uint16))
+    # the operation producing the input (weight gamma) absorbs 1/s
+    r = np.random.Generator(np.random.PCG64(801))
+    gamma = (1.0 + 0.1 * r.standard_normal(4096)).astype(np.float16)
+    s16h = s16.cpu().numpy()
+    gfold = P.awq_fold_inv_scale(dev(gamma), s16)
+    torch.cuda.synchronize()
+    assert np.array_equal(gfold.cpu().numpy().view(np.uint16), O.fold_inv_scale(gamma, s16h).view(np.uint16))
+    x_tilde = O.fp16_rn(x_run.astype(np.float64) * gfold.cpu().numpy().astype(np.float64)[None, :])
+    qw, sc, qz, _ = P.awq_pack_int4(wd, s16, g=128)
+    y = P.awq_linear_w4a16(dev(x_tilde), qw, sc, qz, None, g=128)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([r.choice(6144, 192, replace=False), np.arange(4090, 4100), np.arange(6136, 6144)]))
+    ci = torch.from_numpy(cols).to(DEV)
+    yr = O.linear_ref(x_tilde, host_u32(qw[ci]), sc[ci].cpu().numpy(), host_u32(qz[ci]), None, 4096, 128)
+    ok, worst, raw = O.check_linear(host16(y[:, ci]), yr)
+    assert ok, (worst, raw)
+    # the packed rows of the stack are the oracle's pack at the shared s
+    oq, osc, oz = O.pack_int4(wst[rows[::8]], s16h, 128)[:3]
+    assert np.array_equal(host_u32(qw[torch.from_numpy(rows[::8]).to(DEV)]), oq)

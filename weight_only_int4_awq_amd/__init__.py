@@ -17,7 +17,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import AWQError  # noqa: F401
 
-__all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_pack_int4",
+__all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_fold_inv_scale",
+           "awq_pack_int4",
            "awq_linear_w4a16", "awq_linear_w4a16_group", "AWQError", "load"]
 
 
@@ -109,6 +110,24 @@ def awq_search_scale(w, x, mean_abs, g=128, n_grid=20, workspace=None, out=None)
                                       _ptr(workspace), workspace.numel(), _stream())
     _lib.check("awq_search_scale", st)
     return best, s16, inv, losses
+
+
+def awq_fold_inv_scale(v, s16, out=None):
+    """fp16_rn(v / s16) per channel (fp16 [k] each): the weight of the
+    operation producing a linear's input with the linear's 1/s folded in, so
+    the linear runs with inv_s16=None.  Returns the fp16 [k] tensor."""
+    torch = _torch()
+    _dev_tensor(v, torch.float16, "v", 1)
+    _dev_tensor(s16, torch.float16, "s16", 1)
+    k = v.shape[0]
+    if s16.shape[0] != k:
+        raise ValueError("v and s16 must have the same length")
+    if out is None:
+        out = torch.empty(k, dtype=torch.float16, device=v.device)
+    _out_tensor(out, torch.float16, (k,), "out")
+    st = _lib.load().awq_fold_inv_scale(_ptr(v), _ptr(s16), k, _ptr(out), _stream())
+    _lib.check("awq_fold_inv_scale", st)
+    return out
 
 
 def awq_pack_int4(w, s16=None, g=128, out=None):

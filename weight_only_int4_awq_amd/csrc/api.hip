@@ -123,6 +123,18 @@ awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n, int6
   return AWQ_OK;
 }
 
+awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
+                              void* stream) {
+  g_err[0] = 0;
+  if (!v || !s16 || !out) return fail(AWQ_ERR_NULL, "awq_fold_inv_scale: null pointer");
+  if (k < 1) return fail(AWQ_ERR_SHAPE, "awq_fold_inv_scale: k=%lld < 1", k);
+  if (!aligned(v, 2) || !aligned(s16, 2) || !aligned(out, 2))
+    return fail(AWQ_ERR_ALIGN, "awq_fold_inv_scale: misaligned pointer");
+  hipError_t e = awq::launch_fold_inv_scale(v, s16, k, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_fold_inv_scale launch");
+  return AWQ_OK;
+}
+
 }  // extern "C"
 
 namespace {

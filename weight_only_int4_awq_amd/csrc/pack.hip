@@ -121,4 +121,24 @@ hipError_t launch_pack(const uint16_t* w, const uint16_t* s16, int64_t n, int64_
   return hipGetLastError();
 }
 
+// fold of 1/s into the per-channel weight of the operation that produces a
+// linear's input: out_k = fp16_rn(v_k / s_k), the float64 quotient of two
+// fp16 values rounded once (a float64 quotient of 11-bit significands cannot
+// land on an fp16 rounding midpoint unless the exact quotient does, so the
+// result is the correctly rounded one)
+__global__ __launch_bounds__(256) void fold_inv_scale_kernel(const uint16_t* __restrict__ v,
+                                                             const uint16_t* __restrict__ s16,
+                                                             int64_t k, uint16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < k; i += (int64_t)gridDim.x * 256)
+    out[i] = f64_to_f16_rn((double)h2f(v[i]) / (double)h2f(s16[i]));
+}
+
+hipError_t launch_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
+                                 hipStream_t stream) {
+  const int64_t blocks = (k + 255) / 256 < 1024 ? (k + 255) / 256 : 1024;
+  hipLaunchKernelGGL(fold_inv_scale_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, v, s16, k,
+                     out);
+  return hipGetLastError();
+}
+
 }  // namespace awq
