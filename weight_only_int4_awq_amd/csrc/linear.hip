@@ -317,12 +317,11 @@ constexpr int kGemvSzRounds = 4;       // scale/zero octets per thread in the pr
 constexpr int kGemvXPre = 4;           // activation chunks per thread loaded up front
 
 // LDS: x_tilde [ng][4][2][g/4] halves, T/U [ng] float4, zero block [g/4]
-// halves, scale|zero words [nb][ng][16], reduction rows [2][W][16] floats,
-// outputs [nb][16] floats.
+// halves, scale|zero words [nb][ng][16], partial rows [nb][W][16] floats.
 size_t gemv_lds_bytes(int64_t k, int32_t g, int nb, int waves) {
   const size_t ng = (size_t)(k / g);
   return (size_t)k * 4 + ng * 16 + (size_t)(g / 4) * 2 + (size_t)nb * ng * 16 * 4 +
-         (size_t)2 * waves * 16 * 4 + (size_t)nb * 16 * 4;
+         (size_t)nb * waves * 16 * 4;
 }
 
 template <int WPL>
@@ -361,8 +360,7 @@ __device__ __forceinline__ void gemv_body(
   float4* tu = reinterpret_cast<float4*>(sp);              sp += (size_t)ng * 16;   // (T_hi, U_hi, T_lo, U_lo)
   uint16_t* zblk = reinterpret_cast<uint16_t*>(sp);        sp += HPL * 2;           // zeros
   uint32_t* szw = reinterpret_cast<uint32_t*>(sp);         sp += (size_t)my_blocks * ng * 16 * 4;
-  float* red = reinterpret_cast<float*>(sp);               sp += 2 * kGemvWaves * 16 * 4;   // [2][W][16]
-  float* ybuf = reinterpret_cast<float*>(sp);                                        // [nb][16]
+  float* red = reinterpret_cast<float*>(sp);               // [nb][W][16] partial rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave: keep it (and every group index
@@ -548,20 +546,13 @@ __device__ __forceinline__ void gemv_body(
   float yacc = 0.0f;
   int blocks_done = 0;
 
-  // end of a column block: combine the hi + lo rows, meet the other waves,
-  // reduce into the output row of the block (LDS only)
+  // end of a column block: combine the hi + lo rows into the wave's partial
+  // row of the block (LDS; each block has its own rows, so no wave waits for
+  // another until all blocks are done)
   auto finish_block = [&]() {
     const float other = __shfl_xor(yacc, 32, 64);
-    float* rb = red + (blocks_done & 1) * (kGemvWaves * 16);
-    if (lane < 16) rb[wave * 16 + lane] = yacc + other;
+    if (lane < 16) red[(blocks_done * kGemvWaves + wave) * 16 + lane] = yacc + other;
     yacc = 0.0f;
-    __syncthreads();
-    if (wave == reducer && lane < 16) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < kGemvWaves; ++wv) sum += rb[wv * 16 + lane];
-      ybuf[blocks_done * 16 + lane] = sum;
-    }
     ++blocks_done;
   };
   int c_j = jb, c_left = total;                       // consume cursor
@@ -630,11 +621,16 @@ __device__ __forceinline__ void gemv_body(
     for (int bi = 0; bi < my_blocks; ++bi) finish_block();
   }
 
-  // ---- outputs: the reducer wave wrote every row of ybuf itself
+  // ---- outputs: one barrier, then the reducer wave sums each block's W
+  // partial rows in wave order and stores the block
+  __syncthreads();
   if (wave == reducer && lane < 16) {
     for (int bi = 0; bi < my_blocks; ++bi) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kGemvWaves; ++wv) sum += red[(bi * kGemvWaves + wv) * 16 + lane];
       const int64_t col = ((int64_t)bid + (int64_t)bi * grid) * 16 + lane;
-      if (col < n) y[col] = f2h_rn(ybuf[bi * 16 + lane]);
+      if (col < n) y[col] = f2h_rn(sum);
     }
   }
 }
