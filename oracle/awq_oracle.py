@@ -147,13 +147,14 @@ def group_view(a: np.ndarray, g: int) -> np.ndarray:
     return a.reshape(n, k // g, g)
 
 
-def group_params(wp16: np.ndarray, g: int):
-    """Per (row, group): step D16 (fp16), zero z (int, 0..15) and a flag for
-    groups holding a non-finite W'.
+def group_params(wp16: np.ndarray, g: int, max_int: int = 15):
+    """Per (row, group): step D16 (fp16), zero z (int, 0..max_int) and a flag
+    for groups holding a non-finite W'.  max_int = 2**w_bit - 1 (15 for the
+    4-bit weights of the method; 7 and 255 for the 3- and 8-bit variants).
 
     mx, mn = max, min of W' over the group (the range is not forced to hold 0);
-    r = max(mx - mn, 2**-16) (exact in float64); D16 = fp16_rn(r / 15);
-    z = clamp(RNE(-mn / D16), 0, 15).  Non-finite groups get D16 = NaN, z = 0.
+    r = max(mx - mn, 2**-16) (exact in float64); D16 = fp16_rn(r / max_int);
+    z = clamp(RNE(-mn / D16), 0, max_int).  Non-finite groups get D16 = NaN, z = 0.
 
     Pinned by test_codes_brute_force_all_levels, test_known_answer_groups,
     test_invariants.
@@ -164,23 +165,24 @@ def group_params(wp16: np.ndarray, g: int):
         mx = wg.max(axis=2)
         mn = wg.min(axis=2)
         r = np.maximum(mx - mn, MIN_RANGE)
-        d16 = fp16_rn(r / 15.0)
+        d16 = fp16_rn(r / float(max_int))
         d = d16.astype(np.float64)
-        z = np.clip(rne(-mn / d), 0.0, 15.0)
+        z = np.clip(rne(-mn / d), 0.0, float(max_int))
     d16 = np.where(bad, np.float16(np.nan), d16)
     z = np.where(bad, 0.0, z).astype(np.int64)
     return d16, z, bad
 
 
 def quantize_codes(wp16: np.ndarray, d16: np.ndarray, z: np.ndarray, g: int,
-                   bad: np.ndarray | None = None) -> np.ndarray:
-    """q_nk = clamp(RNE(W'_nk / D16_nj) + z_nj, 0, 15) (quotient in float64,
-    which is exact-then-rounded for fp16 operands); non-finite groups get q = 0.
+                   bad: np.ndarray | None = None, max_int: int = 15) -> np.ndarray:
+    """q_nk = clamp(RNE(W'_nk / D16_nj) + z_nj, 0, max_int) (quotient in
+    float64, which is exact-then-rounded for fp16 operands); non-finite groups
+    get q = 0.
     """
     wg = group_view(np.asarray(wp16, np.float16).astype(np.float64), g)
     d = np.asarray(d16, np.float16).astype(np.float64)[:, :, None]
     with np.errstate(invalid="ignore", divide="ignore"):
-        q = np.clip(rne(wg / d) + np.asarray(z, np.float64)[:, :, None], 0.0, 15.0)
+        q = np.clip(rne(wg / d) + np.asarray(z, np.float64)[:, :, None], 0.0, float(max_int))
     if bad is not None:
         q = np.where(bad[:, :, None], 0.0, q)
     q = np.nan_to_num(q, nan=0.0)
@@ -196,11 +198,11 @@ def dequantize(q: np.ndarray, z: np.ndarray, d16: np.ndarray, g: int) -> np.ndar
     return ((qg - np.asarray(z, np.float64)[:, :, None]) * d).reshape(n, k)
 
 
-def fake_quantize(w16: np.ndarray, s16: np.ndarray | None, g: int):
+def fake_quantize(w16: np.ndarray, s16: np.ndarray | None, g: int, max_int: int = 15):
     """Scale, quantize and dequantize: returns (W'16, q, z, D16, bad, deq)."""
     wp = scale_weights(w16, s16)
-    d16, z, bad = group_params(wp, g)
-    q = quantize_codes(wp, d16, z, g, bad)
+    d16, z, bad = group_params(wp, g, max_int)
+    q = quantize_codes(wp, d16, z, g, bad, max_int)
     deq = dequantize(q, z, d16, g)
     return wp, q, z, d16, bad, deq
 
@@ -210,7 +212,8 @@ def fake_quantize(w16: np.ndarray, s16: np.ndarray | None, g: int):
 # quantized layer; the objective ||Q(W diag(s)) (diag(s)^-1 X) - W X||^2)
 
 
-def search_loss(w16: np.ndarray, x16: np.ndarray, s16: np.ndarray, g: int) -> float:
+def search_loss(w16: np.ndarray, x16: np.ndarray, s16: np.ndarray, g: int,
+                max_int: int = 15) -> float:
     """L = sum_{t,n} (sum_k ((q - z) D16 / s_k - W_nk) X_tk)^2 in float64.
 
     Infinite or NaN when a group of W' is non-finite.
@@ -221,7 +224,7 @@ def search_loss(w16: np.ndarray, x16: np.ndarray, s16: np.ndarray, g: int) -> fl
     w = np.asarray(w16, np.float16).astype(np.float64)
     x = np.asarray(x16, np.float16).astype(np.float64)
     s = np.asarray(s16, np.float16).astype(np.float64)
-    wp, q, z, d16, bad, deq = fake_quantize(w16, s16, g)
+    wp, q, z, d16, bad, deq = fake_quantize(w16, s16, g, max_int)
     if bad.any():
         return float("inf")
     dw = deq / s[None, :] - w                  # [N, K]
@@ -241,7 +244,7 @@ def select_best(losses: np.ndarray) -> int:
 
 
 def search_scale(w16: np.ndarray, x16: np.ndarray, a: np.ndarray, g: int = 128,
-                 n_grid: int = 20):
+                 n_grid: int = 20, w_bit: int = 4):
     """Grid search of s = a^alpha.  Returns (best, s16, inv_s16, losses).
 
     s16 = candidate at the chosen alpha; inv_s16 = fp16_rn(1 / s16) (float64
@@ -253,7 +256,8 @@ def search_scale(w16: np.ndarray, x16: np.ndarray, a: np.ndarray, g: int = 128,
     L[best] <= L[0] is checked.
     """
     alphas = alpha_grid(n_grid)
-    losses = np.array([search_loss(w16, x16, scale_candidate(a, al), g) for al in alphas])
+    max_int = (1 << w_bit) - 1
+    losses = np.array([search_loss(w16, x16, scale_candidate(a, al), g, max_int) for al in alphas])
     best = select_best(losses)
     k = np.asarray(w16).shape[1]
     if best < 0:
@@ -333,16 +337,102 @@ def unpack_int4(qweight: np.ndarray, qzeros: np.ndarray, k: int, g: int):
 
 
 # ----------------------------------------------------------------------------
+# other weight widths ([csdn] 量化流程优化: the w_bit option; [jsqmd] 五: 3- and
+# 4-bit quantization; [zeeklog]: the INT3 result; [bjdmk]: INT4 / INT8).  The
+# same rule with max_int = 2**w_bit - 1, packed (layouts of this library):
+#   w_bit 8: qweight[n][k/4] uint32, byte k%4 of word k/4 holds q_nk;
+#            qzeros[n][ceil(ng/4)] uint32, byte j%4 holds z_nj (unused bytes 0).
+#   w_bit 3: qweight[n][3k/32] uint32: the 32 codes of k in [32p, 32p+32) fill
+#            words 3p..3p+2, code k at bit 3(k%32) of their 96-bit
+#            little-endian value; qzeros as for 4 bits (nibbles; z <= 7).
+
+
+def pack_weights(w16: np.ndarray, s16: np.ndarray | None, g: int = 128, w_bit: int = 4):
+    """pack_int4 for w_bit 4, the layouts above for 3 and 8.  Returns
+    (qweight u32, scales f16 [N, K/g], qzeros u32, n_nonfinite_groups).
+
+    Pinned by test_pack_wbit_roundtrip and the brute-force / known-answer
+    tests at 3 and 8 bits.
+    """
+    if w_bit == 4:
+        return pack_int4(w16, s16, g)
+    max_int = (1 << w_bit) - 1
+    wp, q, z, d16, bad, _ = fake_quantize(w16, s16, g, max_int)
+    n, k = q.shape
+    ng = k // g
+    if w_bit == 8:
+        qw = np.zeros((n, k // 4), dtype=np.uint64)
+        for i in range(4):
+            qw |= (q[:, i::4].astype(np.uint64) & 0xFF) << np.uint64(8 * i)
+        nzw = (ng + 3) // 4
+        zpad = np.zeros((n, nzw * 4), dtype=np.uint64)
+        zpad[:, :ng] = z
+        qz = np.zeros((n, nzw), dtype=np.uint64)
+        for i in range(4):
+            qz |= (zpad[:, i::4] & 0xFF) << np.uint64(8 * i)
+    elif w_bit == 3:
+        assert k % 32 == 0
+        qw = np.zeros((n, 3 * k // 32), dtype=np.uint64)
+        for kk in range(32):                      # code kk of every pack of 32
+            bit = 3 * kk
+            word, off = bit // 32, bit % 32
+            code = q[:, kk::32].astype(np.uint64)
+            qw[:, word::3] |= (code << np.uint64(off)) & np.uint64(0xFFFFFFFF)
+            if off > 29:                          # the code straddles into the next word
+                qw[:, word + 1::3] |= code >> np.uint64(32 - off)
+        nzw = (ng + 7) // 8
+        zpad = np.zeros((n, nzw * 8), dtype=np.uint64)
+        zpad[:, :ng] = z
+        qz = np.zeros((n, nzw), dtype=np.uint64)
+        for i in range(8):
+            qz |= (zpad[:, i::8] & 0xF) << np.uint64(4 * i)
+    else:
+        raise ValueError("w_bit must be 3, 4 or 8")
+    return qw.astype(np.uint32), d16.astype(np.float16), qz.astype(np.uint32), int(bad.sum())
+
+
+def unpack_weights(qweight: np.ndarray, qzeros: np.ndarray, k: int, g: int, w_bit: int = 4):
+    """Inverse of pack_weights: (q [N, K] int, z [N, K/g] int)."""
+    if w_bit == 4:
+        return unpack_int4(qweight, qzeros, k, g)
+    qw = np.asarray(qweight, np.uint32).astype(np.uint64)
+    qz = np.asarray(qzeros, np.uint32).astype(np.uint64)
+    n = qw.shape[0]
+    ng = k // g
+    q = np.zeros((n, k), dtype=np.int64)
+    if w_bit == 8:
+        for i in range(4):
+            q[:, i::4] = ((qw >> np.uint64(8 * i)) & 0xFF).astype(np.int64)
+        zall = np.zeros((n, qz.shape[1] * 4), dtype=np.int64)
+        for i in range(4):
+            zall[:, i::4] = ((qz >> np.uint64(8 * i)) & 0xFF).astype(np.int64)
+    elif w_bit == 3:
+        for kk in range(32):
+            bit = 3 * kk
+            word, off = bit // 32, bit % 32
+            v = qw[:, word::3] >> np.uint64(off)
+            if off > 29:
+                v |= qw[:, word + 1::3] << np.uint64(32 - off)
+            q[:, kk::32] = (v & 0x7).astype(np.int64)
+        zall = np.zeros((n, qz.shape[1] * 8), dtype=np.int64)
+        for i in range(8):
+            zall[:, i::8] = ((qz >> np.uint64(4 * i)) & 0xF).astype(np.int64)
+    else:
+        raise ValueError("w_bit must be 3, 4 or 8")
+    return q, zall[:, :ng]
+
+
+# ----------------------------------------------------------------------------
 # a6-a8: the W4A16 linear  ([bjdmk] GEMV / GEMM modes; [zeeklog] W4A16)
 
 
-def dequantized_weight(qweight, scales, qzeros, k: int, g: int) -> np.ndarray:
+def dequantized_weight(qweight, scales, qzeros, k: int, g: int, w_bit: int = 4) -> np.ndarray:
     """Unpacked (q - z) * D as float64 [N, K]."""
-    q, z = unpack_int4(qweight, qzeros, k, g)
+    q, z = unpack_weights(qweight, qzeros, k, g, w_bit)
     return dequantize(q, z, np.asarray(scales, np.float16), g)
 
 
-def linear_ref(x16, qweight, scales, qzeros, inv_s16, k: int, g: int) -> np.ndarray:
+def linear_ref(x16, qweight, scales, qzeros, inv_s16, k: int, g: int, w_bit: int = 4) -> np.ndarray:
     """y_ref[t, n] = sum_k xt_tk (q_nk - z) D in float64, with
     xt = x * inv_s16 (exact: a product of two fp16) or xt = x when inv_s16 is None.
 
@@ -352,17 +442,17 @@ def linear_ref(x16, qweight, scales, qzeros, inv_s16, k: int, g: int) -> np.ndar
     x = np.asarray(x16, np.float16).astype(np.float64)
     if inv_s16 is not None:
         x = x * np.asarray(inv_s16, np.float16).astype(np.float64)[None, :]
-    wd = dequantized_weight(qweight, scales, qzeros, k, g)
+    wd = dequantized_weight(qweight, scales, qzeros, k, g, w_bit)
     return x @ wd.T
 
 
 def linear_ref_rows(x16, qweight, scales, qzeros, inv_s16, k: int, g: int,
-                    rows: np.ndarray) -> np.ndarray:
+                    rows: np.ndarray, w_bit: int = 4) -> np.ndarray:
     """linear_ref restricted to output columns ``rows`` (used for sampled
     checks at full size)."""
     rows = np.asarray(rows)
     return linear_ref(x16, np.asarray(qweight)[rows], np.asarray(scales)[rows],
-                      np.asarray(qzeros)[rows], inv_s16, k, g)
+                      np.asarray(qzeros)[rows], inv_s16, k, g, w_bit)
 
 
 def check_linear(y16, y_ref, tol: float = 5e-3):

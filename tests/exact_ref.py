@@ -46,11 +46,11 @@ def f16_round_exact(v: Fraction) -> float:
     return sign * float(n * quantum)
 
 
-def brute_force_level(wv: Fraction, d: Fraction, z: int) -> int:
-    """Code q in 0..15 whose level (q - z) d is nearest to wv; on an exact tie
-    the level with (q - z) even wins."""
+def brute_force_level(wv: Fraction, d: Fraction, z: int, max_int: int = 15) -> int:
+    """Code q in 0..max_int whose level (q - z) d is nearest to wv; on an
+    exact tie the level with (q - z) even wins."""
     best = None
-    for q in range(16):
+    for q in range(max_int + 1):
         dist = abs(wv - (q - z) * d)
         key = (dist, (q - z) % 2)
         if best is None or key < best[0]:
@@ -58,10 +58,10 @@ def brute_force_level(wv: Fraction, d: Fraction, z: int) -> int:
     return best[1]
 
 
-def brute_force_zero(mn: Fraction, d: Fraction) -> int:
-    """Zero z in 0..15 nearest to -mn / d; ties go to the even z."""
+def brute_force_zero(mn: Fraction, d: Fraction, max_int: int = 15) -> int:
+    """Zero z in 0..max_int nearest to -mn / d; ties go to the even z."""
     best = None
-    for z in range(16):
+    for z in range(max_int + 1):
         dist = abs(-mn / d - z)
         key = (dist, z % 2)
         if best is None or key < best[0]:
@@ -69,20 +69,21 @@ def brute_force_zero(mn: Fraction, d: Fraction) -> int:
     return best[1]
 
 
-def exact_group_quant(row_vals, g: int):
+def exact_group_quant(row_vals, g: int, max_int: int = 15):
     """Independent exact quantization of one row of W' values (fp16, given as
-    floats): returns (steps, zeros, codes) with steps as Python floats."""
+    floats) with levels 0..max_int: returns (steps, zeros, codes) with steps
+    as Python floats."""
     vals = [Fraction(float(v)) for v in row_vals]
     steps, zeros, codes = [], [], []
     for j in range(0, len(vals), g):
         grp = vals[j:j + g]
         mx, mn = max(grp), min(grp)
         r = max(mx - mn, Fraction(1, 2 ** 16))
-        d = Fraction(f16_round_exact(r / 15))
-        z = brute_force_zero(mn, d)
+        d = Fraction(f16_round_exact(r / max_int))
+        z = brute_force_zero(mn, d, max_int)
         steps.append(float(d))
         zeros.append(z)
-        codes.extend(brute_force_level(v, d, z) for v in grp)
+        codes.extend(brute_force_level(v, d, z, max_int) for v in grp)
     return steps, zeros, codes
 
 

@@ -223,7 +223,7 @@ def test_loss_matches_exact_fractions():
         assert abs(got - float(want)) <= 1e-12 * float(want), alpha
 
 
-def _textbook_rtn_error(w16, x16, g):
+def _textbook_rtn_error(w16, x16, g, max_int=15):
     """Loop-based min-max asymmetric round-to-nearest quantizer (s = 1), written
     independently of the oracle with exact rationals; returns the output error
     sum of squares."""
@@ -236,10 +236,10 @@ def _textbook_rtn_error(w16, x16, g):
         for j in range(0, k, g):
             grp = [Fraction(float(v)) for v in w[r, j:j + g]]
             lo, hi = min(grp), max(grp)
-            step = Fraction(X.f16_round_exact(max(hi - lo, Fraction(1, 2 ** 16)) / 15))
-            zero = min(15, max(0, X.round_half_even(-lo / step)))
+            step = Fraction(X.f16_round_exact(max(hi - lo, Fraction(1, 2 ** 16)) / max_int))
+            zero = min(max_int, max(0, X.round_half_even(-lo / step)))
             for c, v in enumerate(grp):
-                code = min(15, max(0, X.round_half_even(v / step) + zero))
+                code = min(max_int, max(0, X.round_half_even(v / step) + zero))
                 deq[r][j + c] = (code - zero) * step
     for t in range(x.shape[0]):
         for r in range(n):
@@ -380,3 +380,82 @@ def test_joint_loss_is_sum_of_stacked_projections():
         parts = sum(O.search_loss(w, x, s16, g) for w in ws)
         joint = O.search_loss(np.concatenate(ws), x, s16, g)
         assert abs(joint - parts) <= 1e-12 * abs(parts)
+
+
+# ---------------------------------------------------------------- other weight widths (3, 8 bits)
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+@pytest.mark.parametrize("g", [32, 128])
+def test_codes_brute_force_all_levels_wbit(w_bit, g):
+    max_int = (1 << w_bit) - 1
+    wp = _random_wp(6, 2 * g, 200 + g + w_bit)
+    wp[0, :g] = np.abs(wp[0, :g]) + np.float16(0.5)
+    wp[1, g:] = np.float16(-0.75)
+    wp[2, :g] = (wp[2, :g].astype(np.float64) * 1e-3).astype(np.float16)
+    wp[3, g:] = (wp[3, g:].astype(np.float64) * 3000).astype(np.float16)
+    d16, z, bad = O.group_params(wp, g, max_int)
+    q = O.quantize_codes(wp, d16, z, g, bad, max_int)
+    assert not bad.any() and q.min() >= 0 and q.max() <= max_int
+    for r in range(wp.shape[0]):
+        steps, zeros, codes = X.exact_group_quant(wp[r], g, max_int)
+        assert list(d16[r].astype(np.float64)) == steps, r
+        assert list(z[r]) == zeros, r
+        assert list(q[r]) == codes, r
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+def test_known_answer_random_groups_wbit(w_bit):
+    max_int = (1 << w_bit) - 1
+    g, n, ng = 64, 6, 3
+    r = _rng(40 + w_bit)
+    # at most 3 significant bits, so (q - z) * d0 (|q - z| <= 255) is exact in fp16
+    d0 = (2.0 ** r.integers(-12, -6, (n, ng)) * (1 + r.integers(0, 4, (n, ng)) / 4)).astype(np.float16)
+    z0 = r.integers(0, max_int + 1, (n, ng))
+    q0 = r.integers(0, max_int + 1, (n, ng, g))
+    q0[:, :, 0] = 0
+    q0[:, :, 1] = max_int
+    wp = ((q0 - z0[:, :, None]) * d0.astype(np.float64)[:, :, None]).reshape(n, ng * g).astype(np.float16)
+    d16, z, bad = O.group_params(wp, g, max_int)
+    q = O.quantize_codes(wp, d16, z, g, bad, max_int)
+    assert np.array_equal(d16, d0) and np.array_equal(z, z0)
+    assert np.array_equal(q.reshape(n, ng, g), q0)
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+@pytest.mark.parametrize("g", [32, 128])
+def test_pack_wbit_roundtrip(w_bit, g):
+    max_int = (1 << w_bit) - 1
+    w = _random_wp(5, 3 * g if g == 128 else 9 * g, 50 + w_bit)
+    k = w.shape[1]
+    qw, sc, qz, nbad = O.pack_weights(w, None, g, w_bit)
+    assert nbad == 0
+    _, q2, z2, d2, _, _ = O.fake_quantize(w, None, g, max_int)
+    q, z = O.unpack_weights(qw, qz, k, g, w_bit)
+    assert np.array_equal(q, q2) and np.array_equal(z, z2) and np.array_equal(sc, d2)
+    # the bit positions, checked by hand on row 1
+    row = [int(v) for v in qw[1]]
+    if w_bit == 8:
+        assert qw.shape == (5, k // 4) and qz.shape == (5, -(-(k // g) // 4))
+        assert (row[2] >> 8) & 0xFF == q2[1, 9]                  # k = 9: word 2, byte 1
+    else:
+        assert qw.shape == (5, 3 * k // 32) and qz.shape == (5, -(-(k // g) // 8))
+        big = row[3] | (row[4] << 32) | (row[5] << 64)          # codes 32..63
+        for kk in (0, 10, 21, 31):                              # 10 and 21 straddle words
+            assert (big >> (3 * kk)) & 7 == q2[1, 32 + kk]
+        assert (row[0] >> 30) | ((row[1] & 1) << 2) == q2[1, 10]
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+def test_alpha0_is_plain_rtn_wbit(w_bit):
+    w = _random_wp(3, 64, 61 + w_bit)
+    x = S.activations(4, 64, 62, np.array([1, 9]), 20.0)
+    a = O.calib_stats(x)
+    best, s16, inv, losses = O.search_scale(w, x, a, g=32, n_grid=4, w_bit=w_bit)
+    want = _textbook_rtn_error(w, x, 32, (1 << w_bit) - 1)
+    assert abs(losses[0] - float(want)) <= 1e-12 * float(want)
+    # fewer bits, larger error at the same s
+    l3 = O.search_loss(w, x, np.ones(64, np.float16), 32, 7)
+    l4 = O.search_loss(w, x, np.ones(64, np.float16), 32, 15)
+    l8 = O.search_loss(w, x, np.ones(64, np.float16), 32, 255)
+    assert l3 > l4 > l8
