@@ -164,6 +164,66 @@ awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k,
                               uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_search_scale_wbit -- awq_search_scale for 3-, 4- or 8-bit codes.
+ * Passage: CSDN page, section "量化流程优化" (the weight bit width is a
+ * parameter of the search and of the real quantization); jsqmd.com page,
+ * section 六 (AWQ for 3- and 4-bit weights); zeeklog.com page (INT3 weights
+ * with activation-aware scaling); bjdmk.com.cn page (INT4 and INT8 weights).
+ * The per-group rule of awq_search_scale with max_int = 2^w_bit - 1 in place
+ * of 15: D = fp16_rn(max(max W' - min W', 2^-16) / max_int),
+ * z = clamp(RNE(-min W' / D), 0, max_int), q = clamp(RNE(W' / D) + z, 0,
+ * max_int).  Arguments, outputs, workspace and limits as awq_search_scale
+ * (w_bit = 4 gives its exact results); w_bit must be 3, 4 or 8.
+ * ------------------------------------------------------------------------- */
+awq_status awq_search_scale_wbit(const uint16_t* w, const uint16_t* x,
+                                 const double* mean_abs, int64_t n, int64_t k,
+                                 int64_t m, int32_t g, int32_t n_grid, int32_t w_bit,
+                                 int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
+                                 double* losses, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_pack_wbit -- real quantization and packing for 3-, 4- or 8-bit codes.
+ * Passage: as awq_search_scale_wbit.  The codes and zero points are those of
+ * awq_search_scale_wbit's rule at s = s16; w_bit = 4 is awq_pack_int4.
+ *
+ *   w, s16, scales, nonfinite_groups: as awq_pack_int4.
+ *   w_bit 8: qweight [n][k/4] uint32, code k at bits 8*(k%4)..+7 of word
+ *            k/4; qzeros [n][ceil(k/(4g))] uint32, z_nj at bits 8*(j%4)..+7
+ *            of word j/4.
+ *   w_bit 3: qweight [n][3k/32] uint32: codes 32p .. 32p+31 of a row fill
+ *            the 96-bit little-endian value of words 3p, 3p+1, 3p+2, code
+ *            32p+i at bits 3i..3i+2 (codes 10 and 21 straddle two words);
+ *            qzeros [n][ceil(k/(8g))] uint32 with 4-bit fields as layout v1.
+ *   Unused fields of the last qzeros word are 0.
+ *   Limits: those of awq_pack_int4; w_bit in {3, 4, 8}.
+ * ------------------------------------------------------------------------- */
+awq_status awq_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n,
+                         int64_t k, int32_t g, int32_t w_bit, uint32_t* qweight,
+                         uint16_t* scales, uint32_t* qzeros,
+                         int32_t* nonfinite_groups, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * awq_linear_wbit -- y = x_tilde W_deq^T for the layouts of awq_pack_wbit.
+ * Passage: as awq_search_scale_wbit, and the W4A16 contract of
+ * awq_linear_w4a16 (16-bit activations, dequantization in the kernel).
+ *
+ *   y[t][n] = fp16_rn( sum_k x_tilde_tk (q_nk - z_nj) D_nj ), as
+ *   awq_linear_w4a16, within the same 5e-3 bound.  w_bit = 4 runs
+ *   awq_linear_w4a16 (and takes its limits); w_bit 3 and 8 run one MFMA
+ *   kernel for every m, which stages nothing and needs no scratch.
+ *   x [m][k] fp16 and inv_s16 [k] fp16 (or NULL) 16-byte aligned; qweight
+ *   and qzeros 4-byte aligned, scales 2-byte aligned; y [m][n] fp16 out.
+ *   Limits: g in {32, 64, 128}; k % g == 0; k % 64 == 0; 1 <= m, n
+ *           <= 2^31 - 1; w_bit in {3, 4, 8}.
+ * ------------------------------------------------------------------------- */
+awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight,
+                           const uint16_t* scales, const uint32_t* qzeros,
+                           const uint16_t* inv_s16, int64_t m, int64_t n,
+                           int64_t k, int32_t g, int32_t w_bit, uint16_t* y,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_linear_w4a16 -- y = x_tilde W_deq^T with 4-bit weights and fp16
  * activations.
  * Passage: bjdmk.com.cn page, section "量化参数配置" / "技术选型决策树"

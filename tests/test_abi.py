@@ -33,6 +33,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for want in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
                  "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group", "awq_fold_inv_scale",
+                 "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit",
                  "awq_last_error", "awq_abi_version"):
         assert want in names, names
 
@@ -146,10 +147,93 @@ def test_linear_argument_errors(lib):
     assert call(qw=FAKE + 4) == 3
 
 
+def test_search_wbit_argument_errors(lib):
+    ws = lib.awq_search_workspace_size(64, 256, 16, 128, 20)
+    base = [FAKE, FAKE, FAKE, 64, 256, 16, 128, 20, 3, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None]
+    names = ["w", "x", "a", "n", "k", "m", "g", "ng", "wb", "best", "s", "inv", "loss", "ws", "wsb",
+             "st"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_search_scale_wbit", *a)
+
+    for wb in (0, 2, 5, 16):
+        st, msg = call(wb=wb)
+        assert st == 2 and "w_bit" in msg and msg.startswith("awq_search_scale_wbit"), msg
+    assert call(w=None)[0] == 1
+    assert call(g=96)[0] == 2
+    assert call(m=9000)[0] == 2
+    assert call(w=MISALIGNED)[0] == 3
+    assert call(wsb=ws - 1)[0] == 4
+    # the 4-bit entry keeps its own name in its messages
+    st, msg = _status(lib, "awq_search_scale", FAKE, FAKE, FAKE, 64, 256, 16, 96, 20, FAKE, FAKE,
+                      FAKE, FAKE, FAKE, ws, None)
+    assert st == 2 and msg.startswith("awq_search_scale:"), msg
+
+
+def test_pack_wbit_argument_errors(lib):
+    base = [FAKE, None, 16, 256, 128, 8, FAKE, FAKE, FAKE, None, None]
+    names = ["w", "s", "n", "k", "g", "wb", "qw", "sc", "qz", "bad", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_pack_wbit", *a)
+
+    for wb in (1, 2, 6, 7):
+        st, msg = call(wb=wb)
+        assert st == 2 and "w_bit" in msg, msg
+    assert call(w=None)[0] == 1
+    assert call(g=16)[0] == 2
+    assert call(k=192)[0] == 2
+    assert call(n=0)[0] == 2
+    assert call(qw=MISALIGNED)[0] == 3
+    assert call(qz=FAKE + 2)[0] == 3
+
+
+def test_linear_wbit_argument_errors(lib):
+    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, 3, FAKE, None]
+    names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "wb", "y", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_linear_wbit", *a)
+
+    for wb in (2, 5, 16):
+        st, msg = call(wb=wb)
+        assert st == 2 and "w_bit" in msg, msg
+    for wb in (3, 8):
+        assert call(wb=wb, x=None)[0] == 1
+        assert call(wb=wb, g=48)[0] == 2
+        assert call(wb=wb, k=96, g=32)[0] == 2
+        assert call(wb=wb, m=0)[0] == 2
+        assert call(wb=wb, n=0)[0] == 2
+        assert call(wb=wb, x=MISALIGNED)[0] == 3
+        assert call(wb=wb, inv=FAKE + 8)[0] == 3
+        assert call(wb=wb, qw=FAKE + 2)[0] == 3
+    # w_bit 4 takes the 4-bit entry's checks (qweight 16-byte aligned there)
+    st, msg = call(wb=4, qw=FAKE + 4)
+    assert st == 3 and "awq_linear_w4a16" in msg, msg
+
+
+def test_packed_shapes():
+    import weight_only_int4_awq_amd as P
+    assert P.packed_shapes(5, 4096, 128, 4) == ((5, 512), (5, 32), (5, 4))
+    assert P.packed_shapes(5, 4096, 128, 8) == ((5, 1024), (5, 32), (5, 8))
+    assert P.packed_shapes(5, 4096, 128, 3) == ((5, 384), (5, 32), (5, 4))
+    assert P.packed_shapes(5, 4160, 64, 8) == ((5, 1040), (5, 65), (5, 17))
+
+
 def test_python_binding_has_the_c_names():
     import weight_only_int4_awq_amd as P
     for name in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
-                 "awq_pack_int4", "awq_linear_w4a16"):
+                 "awq_pack_int4", "awq_linear_w4a16", "awq_search_scale_wbit", "awq_pack_wbit",
+                 "awq_linear_wbit"):
         assert callable(getattr(P, name))
 
 

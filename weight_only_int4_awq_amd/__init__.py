@@ -18,8 +18,9 @@ from . import _lib
 from ._lib import AWQError  # noqa: F401
 
 __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_fold_inv_scale",
-           "awq_pack_int4",
-           "awq_linear_w4a16", "awq_linear_w4a16_group", "AWQError", "load"]
+           "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group",
+           "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit", "packed_shapes",
+           "AWQError", "load"]
 
 
 def load():
@@ -81,6 +82,15 @@ def awq_search_scale(w, x, mean_abs, g=128, n_grid=20, workspace=None, out=None)
     """Grid search of s = mean_abs ** alpha.  Returns (best_idx int32 [1], s16 fp16 [k],
     inv_s16 fp16 [k], losses float64 [n_grid]) as device tensors (written into
     ``out`` when given)."""
+    return _search(w, x, mean_abs, g, n_grid, None, workspace, out)
+
+
+def awq_search_scale_wbit(w, x, mean_abs, g=128, n_grid=20, w_bit=4, workspace=None, out=None):
+    """awq_search_scale for codes of w_bit = 3, 4 or 8 bits."""
+    return _search(w, x, mean_abs, g, n_grid, w_bit, workspace, out)
+
+
+def _search(w, x, mean_abs, g, n_grid, w_bit, workspace, out):
     torch = _torch()
     _dev_tensor(w, torch.float16, "w", 2)
     _dev_tensor(x, torch.float16, "x", 2)
@@ -105,10 +115,17 @@ def awq_search_scale(w, x, mean_abs, g=128, n_grid=20, workspace=None, out=None)
     _out_tensor(inv, torch.float16, (k,), "inv_s16")
     _out_tensor(losses, torch.float64, (n_grid,), "losses")
     _dev_tensor(workspace, torch.uint8, "workspace")
-    st = _lib.load().awq_search_scale(_ptr(w), _ptr(x), _ptr(mean_abs), n, k, m, g, n_grid,
-                                      _ptr(best), _ptr(s16), _ptr(inv), _ptr(losses),
-                                      _ptr(workspace), workspace.numel(), _stream())
-    _lib.check("awq_search_scale", st)
+    if w_bit is None:
+        st = _lib.load().awq_search_scale(_ptr(w), _ptr(x), _ptr(mean_abs), n, k, m, g, n_grid,
+                                          _ptr(best), _ptr(s16), _ptr(inv), _ptr(losses),
+                                          _ptr(workspace), workspace.numel(), _stream())
+        _lib.check("awq_search_scale", st)
+    else:
+        st = _lib.load().awq_search_scale_wbit(_ptr(w), _ptr(x), _ptr(mean_abs), n, k, m, g,
+                                               n_grid, w_bit, _ptr(best), _ptr(s16), _ptr(inv),
+                                               _ptr(losses), _ptr(workspace), workspace.numel(),
+                                               _stream())
+        _lib.check("awq_search_scale_wbit", st)
     return best, s16, inv, losses
 
 
@@ -159,6 +176,76 @@ def awq_pack_int4(w, s16=None, g=128, out=None):
                                    _ptr(bad), _stream())
     _lib.check("awq_pack_int4", st)
     return qw, sc, qz, bad
+
+
+def packed_shapes(n, k, g, w_bit=4):
+    """(qweight, scales, qzeros) shapes of the packed layout for w_bit bits."""
+    if w_bit == 4:
+        return (n, k // 8), (n, k // g), (n, -(-k // (8 * g)))
+    if w_bit == 8:
+        return (n, k // 4), (n, k // g), (n, -(-k // (4 * g)))
+    if w_bit == 3:
+        return (n, 3 * k // 32), (n, k // g), (n, -(-k // (8 * g)))
+    raise ValueError("w_bit must be 3, 4 or 8")
+
+
+def awq_pack_wbit(w, s16=None, g=128, w_bit=4, out=None):
+    """awq_pack_int4 for codes of w_bit = 3, 4 or 8 bits (layouts of the C
+    header).  Returns (qweight int32, scales fp16 [n, k/g], qzeros int32,
+    nonfinite int32 [1])."""
+    torch = _torch()
+    _dev_tensor(w, torch.float16, "w", 2)
+    n, k = w.shape
+    if s16 is not None:
+        _dev_tensor(s16, torch.float16, "s16", 1)
+        if s16.shape[0] != k:
+            raise ValueError("s16 must have k entries")
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
+    shq, shs, shz = packed_shapes(n, k, g, w_bit)
+    dev = w.device
+    if out is None:
+        qw = torch.empty(shq, dtype=torch.int32, device=dev)
+        sc = torch.empty(shs, dtype=torch.float16, device=dev)
+        qz = torch.empty(shz, dtype=torch.int32, device=dev)
+        bad = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        qw, sc, qz, bad = out
+    _out_tensor(qw, torch.int32, shq, "qweight")
+    _out_tensor(sc, torch.float16, shs, "scales")
+    _out_tensor(qz, torch.int32, shz, "qzeros")
+    if bad is not None:
+        _out_tensor(bad, torch.int32, (1,), "nonfinite")
+    st = _lib.load().awq_pack_wbit(_ptr(w), _ptr(s16), n, k, g, w_bit, _ptr(qw), _ptr(sc),
+                                   _ptr(qz), _ptr(bad), _stream())
+    _lib.check("awq_pack_wbit", st)
+    return qw, sc, qz, bad
+
+
+def awq_linear_wbit(x, qweight, scales, qzeros, inv_s16=None, g=128, w_bit=4, out=None):
+    """awq_linear_w4a16 for the layouts of awq_pack_wbit: x fp16 [m, k] -> y fp16 [m, n]."""
+    torch = _torch()
+    _dev_tensor(x, torch.float16, "x", 2)
+    _dev_tensor(qweight, torch.int32, "qweight", 2)
+    _dev_tensor(scales, torch.float16, "scales", 2)
+    _dev_tensor(qzeros, torch.int32, "qzeros", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
+    shq, shs, shz = packed_shapes(n, k, g, w_bit)
+    if tuple(qweight.shape) != shq or tuple(scales.shape) != shs or tuple(qzeros.shape) != shz:
+        raise ValueError("packed tensors do not match x, g and w_bit")
+    if inv_s16 is not None:
+        _dev_tensor(inv_s16, torch.float16, "inv_s16", 1)
+        if inv_s16.shape[0] != k:
+            raise ValueError("inv_s16 must have k entries")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _out_tensor(y, torch.float16, (m, n), "y")
+    st = _lib.load().awq_linear_wbit(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
+                                     _ptr(inv_s16), m, n, k, g, w_bit, _ptr(y), _stream())
+    _lib.check("awq_linear_wbit", st)
+    return y
 
 
 def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):

@@ -80,47 +80,91 @@ size_t awq_search_workspace_size(int64_t n, int64_t k, int64_t m, int32_t g, int
   return awq::search_layout(n, k, m, g, n_grid).total;
 }
 
+static awq_status search_scale_impl(const char* fn, const uint16_t* w, const uint16_t* x,
+                                    const double* mean_abs, int64_t n, int64_t k, int64_t m,
+                                    int32_t g, int32_t n_grid, int32_t w_bit, int32_t* best_idx,
+                                    uint16_t* s16, uint16_t* inv_s16, double* losses,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  char msg[96];
+  auto err = [&](awq_status st, const char* what, long long a = 0, long long b = 0) {
+    snprintf(msg, sizeof(msg), "%s: %s", fn, what);
+    return fail(st, msg, a, b);
+  };
+  if (!w || !x || !mean_abs || !best_idx || !s16 || !inv_s16) return err(AWQ_ERR_NULL, "null pointer");
+  if (w_bit != 3 && w_bit != 4 && w_bit != 8) return err(AWQ_ERR_SHAPE, "w_bit=%lld not in {3,4,8}", w_bit);
+  if (!group_ok(g)) return err(AWQ_ERR_SHAPE, "g=%lld not in {32,64,128}", g);
+  if (k < g || k % g != 0) return err(AWQ_ERR_SHAPE, "k=%lld not a positive multiple of g=%lld", k, g);
+  if (n < 1) return err(AWQ_ERR_SHAPE, "n=%lld < 1", n);
+  if (m < 1 || m > 8192) return err(AWQ_ERR_SHAPE, "m=%lld outside 1..8192", m);
+  if (n_grid < 1 || n_grid > 64) return err(AWQ_ERR_SHAPE, "n_grid=%lld outside 1..64", n_grid);
+  if (!aligned(w, 16) || !aligned(x, 16)) return err(AWQ_ERR_ALIGN, "w and x must be 16-byte aligned");
+  if (!aligned(mean_abs, 8) || !aligned(s16, 2) || !aligned(inv_s16, 2) || (losses && !aligned(losses, 8)))
+    return err(AWQ_ERR_ALIGN, "misaligned output");
+  const size_t need = awq::search_layout(n, k, m, g, n_grid).total;
+  if (!workspace || ws_bytes < need)
+    return err(AWQ_ERR_WORKSPACE, "workspace of %lld bytes < %lld needed", (long long)ws_bytes, (long long)need);
+  if (!aligned(workspace, 256)) return err(AWQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipError_t e = awq::launch_search(w, x, mean_abs, n, k, m, g, n_grid, w_bit, best_idx, s16,
+                                    inv_s16, losses, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return AWQ_OK;
+}
+
 awq_status awq_search_scale(const uint16_t* w, const uint16_t* x, const double* mean_abs,
                             int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid,
                             int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
                             double* losses, void* workspace, size_t ws_bytes, void* stream) {
+  return search_scale_impl("awq_search_scale", w, x, mean_abs, n, k, m, g, n_grid, 4, best_idx,
+                           s16, inv_s16, losses, workspace, ws_bytes, stream);
+}
+
+awq_status awq_search_scale_wbit(const uint16_t* w, const uint16_t* x, const double* mean_abs,
+                                 int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid,
+                                 int32_t w_bit, int32_t* best_idx, uint16_t* s16,
+                                 uint16_t* inv_s16, double* losses, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  return search_scale_impl("awq_search_scale_wbit", w, x, mean_abs, n, k, m, g, n_grid, w_bit,
+                           best_idx, s16, inv_s16, losses, workspace, ws_bytes, stream);
+}
+
+static awq_status pack_impl(const char* fn, const uint16_t* w, const uint16_t* s16, int64_t n,
+                            int64_t k, int32_t g, int32_t w_bit, uint32_t* qweight,
+                            uint16_t* scales, uint32_t* qzeros, int32_t* nonfinite_groups,
+                            void* stream) {
   g_err[0] = 0;
-  if (!w || !x || !mean_abs || !best_idx || !s16 || !inv_s16)
-    return fail(AWQ_ERR_NULL, "awq_search_scale: null pointer");
-  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_search_scale: g=%lld not in {32,64,128}", g);
-  if (k < g || k % g != 0) return fail(AWQ_ERR_SHAPE, "awq_search_scale: k=%lld not a positive multiple of g=%lld", k, g);
-  if (n < 1) return fail(AWQ_ERR_SHAPE, "awq_search_scale: n=%lld < 1", n);
-  if (m < 1 || m > 8192) return fail(AWQ_ERR_SHAPE, "awq_search_scale: m=%lld outside 1..8192", m);
-  if (n_grid < 1 || n_grid > 64) return fail(AWQ_ERR_SHAPE, "awq_search_scale: n_grid=%lld outside 1..64", n_grid);
-  if (!aligned(w, 16) || !aligned(x, 16)) return fail(AWQ_ERR_ALIGN, "awq_search_scale: w and x must be 16-byte aligned");
-  if (!aligned(mean_abs, 8) || !aligned(s16, 2) || !aligned(inv_s16, 2) || (losses && !aligned(losses, 8)))
-    return fail(AWQ_ERR_ALIGN, "awq_search_scale: misaligned output");
-  const size_t need = awq::search_layout(n, k, m, g, n_grid).total;
-  if (!workspace || ws_bytes < need)
-    return fail(AWQ_ERR_WORKSPACE, "awq_search_scale: workspace of %lld bytes < %lld needed", (long long)ws_bytes, (long long)need);
-  if (!aligned(workspace, 256)) return fail(AWQ_ERR_ALIGN, "awq_search_scale: workspace must be 256-byte aligned");
-  hipError_t e = awq::launch_search(w, x, mean_abs, n, k, m, g, n_grid, best_idx, s16, inv_s16,
-                                    losses, workspace, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "awq_search_scale launch");
+  char msg[96];
+  auto err = [&](awq_status st, const char* what, long long a = 0, long long b = 0) {
+    snprintf(msg, sizeof(msg), "%s: %s", fn, what);
+    return fail(st, msg, a, b);
+  };
+  if (!w || !qweight || !scales || !qzeros) return err(AWQ_ERR_NULL, "null pointer");
+  if (w_bit != 3 && w_bit != 4 && w_bit != 8) return err(AWQ_ERR_SHAPE, "w_bit=%lld not in {3,4,8}", w_bit);
+  if (!group_ok(g)) return err(AWQ_ERR_SHAPE, "g=%lld not in {32,64,128}", g);
+  if (k < g || k % g != 0) return err(AWQ_ERR_SHAPE, "k=%lld not a positive multiple of g=%lld", k, g);
+  if (n < 1 || n > 0x7FFFFFFF) return err(AWQ_ERR_SHAPE, "n=%lld out of range", n);
+  if (!aligned(w, 16) || !aligned(qweight, 16) || (s16 && !aligned(s16, 16)))
+    return err(AWQ_ERR_ALIGN, "w, s16 and qweight must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(qzeros, 4) || (nonfinite_groups && !aligned(nonfinite_groups, 4)))
+    return err(AWQ_ERR_ALIGN, "misaligned output");
+  hipError_t e = awq::launch_pack_wbit(w, s16, n, k, g, w_bit, qweight, scales, qzeros,
+                                       nonfinite_groups, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
   return AWQ_OK;
 }
 
 awq_status awq_pack_int4(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k, int32_t g,
                          uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
                          int32_t* nonfinite_groups, void* stream) {
-  g_err[0] = 0;
-  if (!w || !qweight || !scales || !qzeros) return fail(AWQ_ERR_NULL, "awq_pack_int4: null pointer");
-  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_pack_int4: g=%lld not in {32,64,128}", g);
-  if (k < g || k % g != 0) return fail(AWQ_ERR_SHAPE, "awq_pack_int4: k=%lld not a positive multiple of g=%lld", k, g);
-  if (n < 1 || n > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_pack_int4: n=%lld out of range", n);
-  if (!aligned(w, 16) || !aligned(qweight, 16) || (s16 && !aligned(s16, 16)))
-    return fail(AWQ_ERR_ALIGN, "awq_pack_int4: w, s16 and qweight must be 16-byte aligned");
-  if (!aligned(scales, 2) || !aligned(qzeros, 4) || (nonfinite_groups && !aligned(nonfinite_groups, 4)))
-    return fail(AWQ_ERR_ALIGN, "awq_pack_int4: misaligned output");
-  hipError_t e = awq::launch_pack(w, s16, n, k, g, qweight, scales, qzeros, nonfinite_groups,
-                                  (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "awq_pack_int4 launch");
-  return AWQ_OK;
+  return pack_impl("awq_pack_int4", w, s16, n, k, g, 4, qweight, scales, qzeros, nonfinite_groups,
+                   stream);
+}
+
+awq_status awq_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k, int32_t g,
+                         int32_t w_bit, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
+                         int32_t* nonfinite_groups, void* stream) {
+  return pack_impl("awq_pack_wbit", w, s16, n, k, g, w_bit, qweight, scales, qzeros,
+                   nonfinite_groups, stream);
 }
 
 awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
@@ -220,6 +264,36 @@ awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count, i
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group launch");
+  return AWQ_OK;
+}
+
+awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
+                           int64_t k, int32_t g, int32_t w_bit, uint16_t* y, void* stream) {
+  g_err[0] = 0;
+  if (w_bit == 4) {
+    awq_status st = awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, stream);
+    if (st != AWQ_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "awq_linear_wbit (w_bit 4) -> %s", g_err);
+      snprintf(g_err, sizeof(g_err), "%s", msg);
+    }
+    return st;
+  }
+  if (!x || !qweight || !scales || !qzeros || !y) return fail(AWQ_ERR_NULL, "awq_linear_wbit: null pointer");
+  if (w_bit != 3 && w_bit != 8) return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: w_bit=%lld not in {3,4,8}", w_bit);
+  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: g=%lld not in {32,64,128}", g);
+  if (k < 64 || k % g != 0 || k % 64 != 0)
+    return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: k=%lld must be a multiple of g=%lld and of 64", k, g);
+  if (m < 1 || m > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: m=%lld out of range", m);
+  if (n < 1 || n > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: n=%lld out of range", n);
+  if (!aligned(x, 16) || (inv_s16 && !aligned(inv_s16, 16)))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: x and inv_s16 must be 16-byte aligned");
+  if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(y, 2))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: misaligned pointer");
+  hipError_t e = awq::launch_linear_wbit(x, qweight, scales, qzeros, inv_s16, m, n, k, g, w_bit, y,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_linear_wbit launch");
   return AWQ_OK;
 }
 

@@ -74,30 +74,35 @@ __device__ __forceinline__ float rne_quot(float w, float d, float rd) {
   return __builtin_rintf(t2);
 }
 
-// Per-group step, zero and reciprocal from the group's fp16 max and min.
+// Per-group step, zero and reciprocal from the group's fp16 max and min, for
+// codes 0..qmax (qmax = 2^w_bit - 1: 15 for 4-bit weights, 7 and 255 for the
+// 3- and 8-bit variants).  rne_quot is exact for |w / D| <= 2^10; beyond that
+// the clamp to -z .. qmax - z decides whatever the rounding, as qmax <= 255.
 struct GroupQ {
   float d;      // step D (an fp16 value)
   float rd;     // 1/D, correctly rounded fp32
-  float z;      // zero point, integer 0..15
+  float z;      // zero point, integer 0..qmax
+  float qmax;
   uint16_t d_bits;
 };
 
-__device__ __forceinline__ GroupQ group_q(float mx, float mn) {
+__device__ __forceinline__ GroupQ group_q(float mx, float mn, float qmax = 15.0f) {
   GroupQ gq;
   double r = (double)mx - (double)mn;          // exact in float64
   r = r > 0x1p-16 ? r : 0x1p-16;
-  gq.d_bits = f64_to_f16_rn(r / 15.0);
+  gq.d_bits = f64_to_f16_rn(r / (double)qmax);
   gq.d = h2f(gq.d_bits);
   gq.rd = 1.0f / gq.d;
+  gq.qmax = qmax;
   float z = rne_quot(-mn, gq.d, gq.rd);
-  gq.z = __builtin_fminf(__builtin_fmaxf(z, 0.0f), 15.0f);
+  gq.z = __builtin_fminf(__builtin_fmaxf(z, 0.0f), qmax);
   return gq;
 }
 
-// (q - z) for one element: clamp(RNE(w/D) + z, 0, 15) - z as a float.
+// (q - z) for one element: clamp(RNE(w/D) + z, 0, qmax) - z as a float.
 __device__ __forceinline__ float code_minus_zero(float w, const GroupQ& gq) {
   float t = rne_quot(w, gq.d, gq.rd);
-  return __builtin_fminf(__builtin_fmaxf(t, -gq.z), 15.0f - gq.z);
+  return __builtin_fminf(__builtin_fmaxf(t, -gq.z), gq.qmax - gq.z);
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {

@@ -24,7 +24,7 @@ SearchLayout search_layout(int64_t n, int64_t k, int64_t m, int32_t g, int32_t n
 
 hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mean_abs,
                          int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid,
-                         int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
+                         int32_t w_bit, int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
                          double* losses, void* workspace, hipStream_t stream);
 
 hipError_t launch_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
@@ -33,6 +33,11 @@ hipError_t launch_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t
 hipError_t launch_pack(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
                        int32_t g, uint32_t* qweight, uint16_t* scales, uint32_t* qzeros,
                        int32_t* nonfinite, hipStream_t stream);
+
+// 3- or 8-bit packing (layouts of awq_pack_wbit)
+hipError_t launch_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
+                            int32_t g, int32_t w_bit, uint32_t* qweight, uint16_t* scales,
+                            uint32_t* qzeros, int32_t* nonfinite, hipStream_t stream);
 
 // Most linears one grouped decode launch takes.
 constexpr int kGroupMax = 4;
@@ -62,5 +67,11 @@ size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, in
 // holds the bits launch_linear writes for that linear alone.
 hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
                                void* scratch, hipStream_t stream);
+
+// the linear for 3- and 8-bit weights (layouts of awq_pack_wbit)
+hipError_t launch_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                              const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
+                              int64_t n, int64_t k, int32_t g, int32_t w_bit, uint16_t* y,
+                              hipStream_t stream);
 
 }  // namespace awq

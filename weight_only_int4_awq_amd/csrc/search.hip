@@ -184,7 +184,8 @@ template <int G, int NT>
 __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ x, int64_t n, int64_t k,
     int64_t m, int32_t n_grid, int64_t n_blocks, const uint16_t* __restrict__ s16_all,
-    const float* __restrict__ rs_all, const uint32_t* __restrict__ bmax, double* __restrict__ part) {
+    const float* __restrict__ rs_all, const uint32_t* __restrict__ bmax, double* __restrict__ part,
+    float qmax) {
   constexpr int EPT = G / 4;          // elements of one row-group per producer thread
   constexpr int KSTEPS = G / 16;      // MFMA k-steps per group (even)
   constexpr int TOK = 128 * NT;       // tokens per pass
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     mn = __builtin_fminf(mn, dpp_mov<0xB1>(mn));                                            \
     mx = __builtin_fmaxf(mx, dpp_mov<0x4E>(mx));                                            \
     mn = __builtin_fminf(mn, dpp_mov<0x4E>(mn));                                            \
-    const GroupQ gq = group_q(mx, mn);                                                      \
+    const GroupQ gq = group_q(mx, mn, qmax);                                                \
     _Pragma("unroll") for (int q = 0; q < WLD; ++q) {                                       \
       __builtin_amdgcn_sched_barrier(0);                                                    \
       const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * EPT + 8 * q]);        \
@@ -495,8 +496,9 @@ __global__ __launch_bounds__(256) void search_select_kernel(
 
 hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mean_abs,
                          int64_t n, int64_t k, int64_t m, int32_t g, int32_t n_grid,
-                         int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
+                         int32_t w_bit, int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
                          double* losses, void* workspace, hipStream_t stream) {
+  const float qmax = (float)((1 << w_bit) - 1);
   const SearchLayout L = search_layout(n, k, m, g, n_grid);
   char* ws = static_cast<char*>(workspace);
   uint16_t* s16_all = reinterpret_cast<uint16_t*>(ws + L.off_s16);
@@ -514,7 +516,7 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
   const int nt = m <= 128 ? 1 : (m <= 256 ? 2 : 4);
 #define AWQ_SEARCH_LAUNCH(GG, NTT)                                                              \
   hipLaunchKernelGGL((search_loss_kernel<GG, NTT>), dim3(nwg), dim3(512), 0, stream, w, x, n, k, \
-                     m, n_grid, L.n_blocks, s16_all, rs_all, bmax, part)
+                     m, n_grid, L.n_blocks, s16_all, rs_all, bmax, part, qmax)
 #define AWQ_SEARCH_NT(GG)                     \
   switch (nt) {                               \
     case 1: AWQ_SEARCH_LAUNCH(GG, 1); break;  \
