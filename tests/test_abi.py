@@ -215,7 +215,8 @@ def test_linear_wbit_argument_errors(lib):
         assert call(wb=wb, n=0)[0] == 2
         assert call(wb=wb, x=MISALIGNED)[0] == 3
         assert call(wb=wb, inv=FAKE + 8)[0] == 3
-        assert call(wb=wb, qw=FAKE + 2)[0] == 3
+        assert call(wb=wb, qw=FAKE + 4)[0] == 3
+        assert call(wb=wb, qz=FAKE + 2)[0] == 3
     # w_bit 4 takes the 4-bit entry's checks (qweight 16-byte aligned there)
     st, msg = call(wb=4, qw=FAKE + 4)
     assert st == 3 and "awq_linear_w4a16" in msg, msg

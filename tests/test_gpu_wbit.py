@@ -259,6 +259,49 @@ def test_linear_wbit_prefill_full_size_sampled(P, w_bit):
     _check_linear(P, w, x_run, s16, 128, w_bit, cols=cols)
 
 
+@pytest.mark.parametrize("w_bit", [3, 8])
+@pytest.mark.parametrize("g,k", [(64, 1856), (32, 960), (128, 3712), (32, 14336)])
+def test_linear_wbit_gemm_windows(P, w_bit, g, k):
+    # the GEMM restages scales every 28 groups: K ranges that end in a
+    # one-step window, a short window and 16 windows; tiles of 64 and 256 rows
+    # with ragged m and n
+    n = 200
+    w = S.weights(n, k, 0.02, 1450 + k)
+    xc = S.activations(64, k, 1451, S.outlier_channels(k, 0.01, 1452), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.5)
+    for m in (33, 129, 300):
+        x = S.activations(m, k, 1453 + m, S.outlier_channels(k, 0.01, 1452), 20.0)
+        _check_linear(P, w, x, s16, g, w_bit)
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+def test_linear_wbit_decode_long_k(P, w_bit):
+    # k = 28672 (the Llama-3-70B down projection's K): one token's x_tilde and
+    # scale table take more than 64 KiB of LDS, two tokens more than 128 KiB,
+    # three do not fit and take the unstaged kernel
+    n, k = 257, 28672
+    w = S.weights(n, k, 0.015, 1460)
+    xc = S.activations(32, k, 1461, S.outlier_channels(k, 0.005, 1462), 30.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.5)
+    for m in (1, 2, 3):
+        x = S.activations(m, k, 1463 + m, S.outlier_channels(k, 0.005, 1462), 30.0)
+        _check_linear(P, w, x, s16, 128, w_bit)
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+@pytest.mark.parametrize("g", [64, 128])
+def test_linear_wbit_decode_many_blocks(P, w_bit, g):
+    # 1101 column blocks (the last one ragged): work-groups of the staged
+    # decode kernel own 3 blocks, some of the last ones fewer
+    n, k = 16 * 1100 + 5, 1024
+    w = S.weights(n, k, 0.02, 1470)
+    cols = np.sort(np.random.Generator(np.random.PCG64(1471)).choice(n, 300, replace=False))
+    cols[-1] = n - 1
+    for m in (1, 3):
+        x = S.activations(m, k, 1472 + m, S.outlier_channels(k, 0.01, 1473), 20.0)
+        _check_linear(P, w, x, None, g, w_bit, cols=np.unique(cols))
+
+
 def test_linear_wbit_4_is_linear_w4a16(P):
     w = S.weights(96, 1024, 0.02, 1431)
     qw, sc, qz, _ = P.awq_pack_int4(dev(w), None, g=128)
@@ -272,10 +315,12 @@ def test_linear_wbit_4_is_linear_w4a16(P):
 
 def test_linear_wbit_deterministic(P):
     w = S.weights(300, 2048, 0.02, 1441)
+    inv = dev(np.full(2048, 0.5, np.float16))
     for wb in (3, 8):
         qw, sc, qz, _ = P.awq_pack_wbit(dev(w), None, g=128, w_bit=wb)
-        x = dev(S.activations(20, 2048, 1442))
-        a = P.awq_linear_wbit(x, qw, sc, qz, None, g=128, w_bit=wb)
-        b = P.awq_linear_wbit(x, qw, sc, qz, None, g=128, w_bit=wb)
-        torch.cuda.synchronize()
-        assert torch.equal(a, b)
+        for m in (20, 300):
+            x = dev(S.activations(m, 2048, 1442))
+            a = P.awq_linear_wbit(x, qw, sc, qz, inv, g=128, w_bit=wb)
+            b = P.awq_linear_wbit(x, qw, sc, qz, inv, g=128, w_bit=wb)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b)

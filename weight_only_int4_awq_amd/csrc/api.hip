@@ -287,12 +287,15 @@ awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uin
     return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: k=%lld must be a multiple of g=%lld and of 64", k, g);
   if (m < 1 || m > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: m=%lld out of range", m);
   if (n < 1 || n > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_linear_wbit: n=%lld out of range", n);
-  if (!aligned(x, 16) || (inv_s16 && !aligned(inv_s16, 16)))
-    return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: x and inv_s16 must be 16-byte aligned");
-  if (!aligned(qweight, 4) || !aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(y, 2))
+  if (!aligned(x, 16) || !aligned(qweight, 16) || (inv_s16 && !aligned(inv_s16, 16)))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: x, qweight and inv_s16 must be 16-byte aligned");
+  if (!aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(y, 2))
     return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: misaligned pointer");
+  void* scratch = nullptr;
+  awq_status st = get_scratch(awq::linear_wbit_scratch_bytes(m, n, k, g, inv_s16 != nullptr), &scratch);
+  if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear_wbit(x, qweight, scales, qzeros, inv_s16, m, n, k, g, w_bit, y,
-                                         (hipStream_t)stream);
+                                         scratch, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_wbit launch");
   return AWQ_OK;
 }

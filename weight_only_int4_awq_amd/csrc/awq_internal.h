@@ -68,10 +68,12 @@ size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, in
 hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
                                void* scratch, hipStream_t stream);
 
-// the linear for 3- and 8-bit weights (layouts of awq_pack_wbit)
+// the linear for 3- and 8-bit weights (layouts of awq_pack_wbit); scratch of
+// linear_wbit_scratch_bytes(m, n, k, g, inv_s16 != NULL) bytes, 256-byte aligned
+size_t linear_wbit_scratch_bytes(int64_t m, int64_t n, int64_t k, int32_t g, bool has_inv);
 hipError_t launch_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                               const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
                               int64_t n, int64_t k, int32_t g, int32_t w_bit, uint16_t* y,
-                              hipStream_t stream);
+                              void* scratch, hipStream_t stream);
 
 }  // namespace awq
