@@ -16,6 +16,10 @@ One step is one pass of the whole path over one batch of synthetic input:
   prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
             in the decode (4 calls, each one activation-prep launch and one
             GEMM launch over the tiles of its linears);
+  3/8-bit   the stack searched at 3 and at 8 bits (per-linear alpha, 128
+            calibration tokens) and packed in those layouts: all 224 linears
+            at M = 1 (one awq_linear_wbit call each, replayed as one HIP
+            graph) and the 7 linears of layer L at M = 2048;
   70B rows  the four Llama-3-70B-shaped linears (8192<-8192, 1024<-8192,
             28672<-8192, 8192<-28672) at M = 1 and 16, each call on its own
             copy of the packed weights (>= 512 MB of copies per shape), so
@@ -55,6 +59,14 @@ def gemv_bytes(m, n, k, g, inv=True):
     packed zero points, the fp16 activation and inv_s (when given) read once,
     the fp16 output written once."""
     return (n * k // 2 + 2 * n * (k // g) + 4 * n * (-(-k // (8 * g))) + 2 * m * k + (2 * k if inv else 0)
+            + 2 * m * n)
+
+
+def wbit_bytes(m, n, k, g, w_bit):
+    """gemv_bytes for the 3- and 8-bit layouts (codes, fp16 scales, zero-point
+    words, activation, inv_s and output)."""
+    zpw = 4 if w_bit == 8 else 8
+    return (n * k * w_bit // 8 + 2 * n * (k // g) + 4 * n * (-(-(k // g) // zpw)) + 2 * m * k + 2 * k
             + 2 * m * n)
 
 
@@ -303,6 +315,49 @@ def main():
         big.append((nm, n, k, packs, inv, xr, yb))
     big_cases = [(bi, m) for bi in range(len(big)) for m in (1, 16)]
 
+    # 3- and 8-bit stacks: searched per linear at that width (128 calibration
+    # tokens of the stack's calibration set) and packed in its layout
+    wbits = (3, 8)
+    wstacks = {}
+    for wb in wbits:
+        st = []
+        for layer in range(L):
+            stats = {inp: P.awq_calib_stats(XC[layer][inp][:128].contiguous()) for inp in inputs}
+            row = []
+            for li, (nm, n, k) in enumerate(shapes):
+                inp = S.INPUT_OF[nm]
+                _, s16, inv, _ = P.awq_search_scale_wbit(W[layer][li], XC[layer][inp][:128].contiguous(),
+                                                         stats[inp], g=128, n_grid=n_grid, w_bit=wb,
+                                                         workspace=ws_setup[128][li])
+                qw, sc, qz, _ = P.awq_pack_wbit(W[layer][li], s16, g=128, w_bit=wb)
+                row.append((qw, sc, qz, inv))
+            st.append(row)
+        wstacks[wb] = st
+
+    def decode_wbit(wb):
+        for layer in range(L):
+            for li, (nm, n, k) in enumerate(shapes):
+                qw, sc, qz, inv = wstacks[wb][layer][li]
+                P.awq_linear_wbit(XR[1][layer][S.INPUT_OF[nm]], qw, sc, qz, inv, g=128, w_bit=wb,
+                                  out=YR[1][layer][li])
+
+    def prefill_wbit(wb, layer):
+        for li, (nm, n, k) in enumerate(shapes):
+            qw, sc, qz, inv = wstacks[wb][layer][li]
+            P.awq_linear_wbit(XP[S.INPUT_OF[nm]], qw, sc, qz, inv, g=128, w_bit=wb, out=YP[li])
+
+    for wb in wbits:                  # eager runs first: the library scratch is allocated
+        decode_wbit(wb)
+        prefill_wbit(wb, 0)
+    torch.cuda.synchronize()
+    for wb in wbits:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            decode_wbit(wb)
+        graphs[f"w{wb}"] = gr
+    torch.cuda.synchronize()
+    log("searched, packed and captured the 3- and 8-bit stacks")
+
     def big_calls(bi, m):
         nm, n, k, packs, inv, xr, yb = big[bi]
         for qw, sc, qz in packs:
@@ -321,7 +376,8 @@ def main():
     log("packed and captured the 70B-shaped linears")
 
     phases = (["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["decode_fused"] + ["prefill"] +
-              [f"big_{big[bi][0]}_m{m}" for bi, m in big_cases])
+              [f"big_{big[bi][0]}_m{m}" for bi, m in big_cases] +
+              [f"decode_w{wb}_m1" for wb in wbits] + [f"prefill_w{wb}" for wb in wbits])
     acc = {p: 0.0 for p in phases}
 
     def step(i, timed):
@@ -340,6 +396,13 @@ def main():
         for ci, key in enumerate(big_cases):
             big_graphs[key].replay()
             ev[4 + len(decode_cases) + ci].record(stream)
+        e0 = 4 + len(decode_cases) + len(big_cases)
+        for wi, wb in enumerate(wbits):
+            graphs[f"w{wb}"].replay()
+            ev[e0 + wi].record(stream)
+        for wi, wb in enumerate(wbits):
+            prefill_wbit(wb, layer)
+            ev[e0 + len(wbits) + wi].record(stream)
         if timed:
             return ev
         return None
@@ -394,6 +457,15 @@ def main():
         rows[f"llama3_70b_{nm}_m{m}"] = {"us_per_call": t * 1e6, "GBps": by / t / 1e9,
                                          "frac_hbm_peak": by / t / 1e9 / HBM_PEAK_GBS,
                                          "n": n, "k": k, "cold_copies": len(packs)}
+    for wb in wbits:
+        t = acc[f"decode_w{wb}_m1"] / K
+        by = L * sum(wbit_bytes(1, n, k, 128, wb) for nm, n, k in shapes)
+        rows[f"decode_w{wb}_g128_m1"] = {"us_per_stack": t * 1e6, "us_per_linear": t * 1e6 / nlin,
+                                         "GBps": by / t / 1e9, "frac_hbm_peak": by / t / 1e9 / HBM_PEAK_GBS,
+                                         "stack_bytes": by}
+        t = acc[f"prefill_w{wb}"] / K
+        rows[f"prefill_w{wb}_m2048"] = {"us_per_layer": t * 1e6, "TFLOPs": prefill_flops / t / 1e12,
+                                        "frac_mfma_peak": prefill_flops / t / 1e12 / F16_MFMA_PEAK_TFLOPS}
     # the two 122 MB shapes (28672<-8192, 8192<-28672) at M = 1 together
     bp = [rows[f"llama3_70b_{nm}_m1"] for nm in ("gate_up", "down")]
     bp_bytes = sum(gemv_bytes(1, r["n"], r["k"], 128) for r in bp)
@@ -422,7 +494,8 @@ def main():
         "config": {"workload": "llama3-8b-shaped linear stack: producer (calib 512 tok, 20-pt alpha "
                                "search, int4 g128 pack) on one layer + 32-layer decode at M=1/8/32/128 "
                                "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048 + llama3-70b-"
-                               "shaped linears at M=1/16 (cold copies)",
+                               "shaped linears at M=1/16 (cold copies) + the stack at 3 and 8 bits "
+                               "(M=1 decode, M=2048 prefill of one layer)",
                    "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32, 128],
                    "m_prefill": 2048, "m_calib": m_cal, "n_grid": n_grid, "group_size": [128, 64]},
         "gemm_tflops_m2048": round(rows["prefill_m2048"]["TFLOPs"], 2),
