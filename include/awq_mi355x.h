@@ -293,6 +293,29 @@ typedef struct {
 awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count,
                                   int64_t m, int64_t k, int32_t g, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * awq_linear_w4a16_bf16, awq_linear_w4a16_group_bf16 -- the 4-bit linear and
+ * its group call with bf16 activations: x and y hold bf16 bit patterns.
+ * Passage: jsqmd.com page, section 二.1 (3) and bjdmk.com.cn page, section
+ * "量化参数配置", as awq_linear_w4a16 (16-bit activations; the pages pair the
+ * 4-bit weights with 16-bit activations without fixing the 16-bit format).
+ *
+ *   Each x is rounded once to fp16 (exact for |x| in [2^-14, 65504]; smaller
+ *   values lose the bits below 2^-24, larger ones become +-inf) and the call
+ *   then computes what awq_linear_w4a16 computes for that fp16 x; each output
+ *   is rounded once from the fp32 accumulation to bf16 (nearest, ties to even)
+ *   instead of fp16.  Within 5e-3 * max(|y_ref|, rms of the row of y_ref) of
+ *   the float64 value for x in that range.  inv_s16, qweight, scales, qzeros:
+ *   as awq_linear_w4a16 (fp16 scales and inv_s16).  Arguments, limits, scratch
+ *   and errors: those of awq_linear_w4a16 and awq_linear_w4a16_group.
+ * ------------------------------------------------------------------------- */
+awq_status awq_linear_w4a16_bf16(const uint16_t* x, const uint32_t* qweight,
+                                 const uint16_t* scales, const uint32_t* qzeros,
+                                 const uint16_t* inv_s16, int64_t m, int64_t n,
+                                 int64_t k, int32_t g, uint16_t* y, void* stream);
+awq_status awq_linear_w4a16_group_bf16(const awq_linear_item* items, int32_t count,
+                                       int64_t m, int64_t k, int32_t g, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -432,14 +432,34 @@ def dequantized_weight(qweight, scales, qzeros, k: int, g: int, w_bit: int = 4) 
     return dequantize(q, z, np.asarray(scales, np.float16), g)
 
 
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) as float64: a bf16 value is the upper half
+    of an IEEE binary32, so the conversion is exact.  Pinned by
+    test_bf16_decode (values fixed by the format's definition)."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def exact_f64(a) -> np.ndarray:
+    """A float array's values as float64: fp16 arrays convert exactly, float32
+    and float64 arrays are taken as the exact values they hold (bf16 inputs
+    arrive decoded by bf16_to_f64)."""
+    a = np.asarray(a)
+    if a.dtype in (np.float16, np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"expected a float array, got {a.dtype}")
+
+
 def linear_ref(x16, qweight, scales, qzeros, inv_s16, k: int, g: int, w_bit: int = 4) -> np.ndarray:
     """y_ref[t, n] = sum_k xt_tk (q_nk - z) D in float64, with
-    xt = x * inv_s16 (exact: a product of two fp16) or xt = x when inv_s16 is None.
+    xt = x * inv_s16 (exact: a product of two fp16, or of a bf16 and an fp16)
+    or xt = x when inv_s16 is None.  x is an fp16 array, or float64 holding
+    the exact values (bf16 activations).
 
     Pinned by test_linear_ref_identity (scaling identity) and the fact that it
     is one float64 matrix product of the unpacked weights.
     """
-    x = np.asarray(x16, np.float16).astype(np.float64)
+    x = exact_f64(x16)
     if inv_s16 is not None:
         x = x * np.asarray(inv_s16, np.float16).astype(np.float64)[None, :]
     wd = dequantized_weight(qweight, scales, qzeros, k, g, w_bit)
@@ -463,7 +483,7 @@ def check_linear(y16, y_ref, tol: float = 5e-3):
     |y - y_ref| / (tol * floor) and raw_max_rel the plain relative error over
     outputs with |y_ref| >= rms_t.
     """
-    y = np.asarray(y16, np.float16).astype(np.float64)
+    y = exact_f64(y16)
     yr = np.asarray(y_ref, np.float64)
     if y.size == 0:
         return True, 0.0, 0.0

@@ -60,6 +60,19 @@ def activations(m: int, k: int, seed: int, channels: np.ndarray | None = None,
     return x.astype(np.float16)
 
 
+def activations_bf16(m: int, k: int, seed: int, channels: np.ndarray | None = None,
+                     mult: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns (uint16) [m, k] of the same draws as ``activations``:
+    float64 values rounded to float32, then to the nearest bf16 (ties to even
+    on the float32 bits)."""
+    x = rng(seed).standard_normal((m, k))
+    if channels is not None and len(channels):
+        x[:, channels] *= mult
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
 def config_layer(cfg: int, name: str, n: int, k: int, m_cal: int, m_run: int,
                  sigma: float, frac: float, mult: float, layer: int = 0):
     """Weights, calibration tokens and run-time tokens of one linear."""

@@ -34,6 +34,7 @@ def test_header_declares_the_path():
     for want in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
                  "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group", "awq_fold_inv_scale",
                  "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit",
+                 "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
                  "awq_last_error", "awq_abi_version"):
         assert want in names, names
 
@@ -230,11 +231,32 @@ def test_packed_shapes():
     assert P.packed_shapes(5, 4160, 64, 8) == ((5, 1040), (5, 65), (5, 17))
 
 
+def test_linear_bf16_argument_errors(lib):
+    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, FAKE, None]
+    names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "y", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_linear_w4a16_bf16", *a)
+
+    st, msg = call(x=None)
+    assert st == 1 and msg.startswith("awq_linear_w4a16_bf16"), msg
+    assert call(g=48)[0] == 2
+    assert call(k=96, g=32)[0] == 2
+    assert call(m=0)[0] == 2
+    assert call(x=MISALIGNED)[0] == 3
+    assert _status(lib, "awq_linear_w4a16_group_bf16", None, 1, 1, 256, 128, None)[0] == 1
+    st, msg = _status(lib, "awq_linear_w4a16_group_bf16", _items(2), 5, 1, 256, 128, None)
+    assert st == 2 and msg.startswith("awq_linear_w4a16_group_bf16"), msg
+
+
 def test_python_binding_has_the_c_names():
     import weight_only_int4_awq_amd as P
     for name in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
                  "awq_pack_int4", "awq_linear_w4a16", "awq_search_scale_wbit", "awq_pack_wbit",
-                 "awq_linear_wbit"):
+                 "awq_linear_wbit", "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16"):
         assert callable(getattr(P, name))
 
 

@@ -459,3 +459,41 @@ def test_alpha0_is_plain_rtn_wbit(w_bit):
     l4 = O.search_loss(w, x, np.ones(64, np.float16), 32, 15)
     l8 = O.search_loss(w, x, np.ones(64, np.float16), 32, 255)
     assert l3 > l4 > l8
+
+
+def test_bf16_decode():
+    # bf16 is the upper 16 bits of an IEEE binary32: values fixed by the format
+    bits = np.array([0x3F80, 0xC020, 0x4049, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x0080, 0x7F7F],
+                    np.uint16)
+    want = [1.0, -2.5, 3.140625, 0.0, -0.0, np.inf, -np.inf, 2.0 ** -133, 2.0 ** -126,
+            (2 - 2.0 ** -7) * 2.0 ** 127]
+    got = O.bf16_to_f64(bits)
+    for g_, w_ in zip(got, want):
+        assert g_ == w_ and np.signbit(g_) == np.signbit(w_)
+    assert np.isnan(O.bf16_to_f64(np.array([0x7FC0], np.uint16))[0])
+    with pytest.raises(TypeError):
+        O.exact_f64(np.array([1, 2], np.int32))
+
+
+def test_linear_ref_bf16_exact_small():
+    # bf16 activations (float64 values) against a rational sum over the unpacked bits
+    g = 32
+    w = _random_wp(3, 64, 91)
+    xb = S.activations_bf16(2, 64, 92, np.array([3]), 40.0)
+    x = O.bf16_to_f64(xb)
+    s = O.scale_candidate(O.calib_stats(S.activations(8, 64, 93, np.array([5]), 20.0)), 0.4)
+    inv = O.fp16_rn(1.0 / s.astype(np.float64))
+    qw, sc, qz, _ = O.pack_int4(w, s, g)
+    y = O.linear_ref(x, qw, sc, qz, inv, 64, g)
+    for t in range(2):
+        for n in range(3):
+            acc = Fraction(0)
+            for c in range(64):
+                code = (int(qw[n, c // 8]) >> (4 * (c % 8))) & 0xF
+                j = c // g
+                zero = (int(qz[n, j // 8]) >> (4 * (j % 8))) & 0xF
+                acc += Fraction(float(x[t, c])) * Fraction(float(inv[c])) * (code - zero) * Fraction(float(sc[n, j]))
+            assert abs(y[t, n] - float(acc)) <= 1e-13 * max(1.0, abs(float(acc)))
+    # the generator's draws are those of the fp16 generator, rounded to bf16
+    xh = S.activations(2, 64, 92, np.array([3]), 40.0).astype(np.float64)
+    assert np.all(np.abs(x - xh) <= 2.0 ** -8 * np.abs(xh) + 2.0 ** -10 * np.abs(xh) + 1e-30)

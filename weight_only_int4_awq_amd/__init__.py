@@ -20,6 +20,7 @@ from ._lib import AWQError  # noqa: F401
 __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_fold_inv_scale",
            "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group",
            "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit", "packed_shapes",
+           "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
            "AWQError", "load"]
 
 
@@ -250,8 +251,19 @@ def awq_linear_wbit(x, qweight, scales, qzeros, inv_s16=None, g=128, w_bit=4, ou
 
 def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
     """y = (x * inv_s16) @ dequant(W)^T in fp16: x fp16 [m, k] -> y fp16 [m, n]."""
+    return _linear(x, qweight, scales, qzeros, inv_s16, g, out, False)
+
+
+def awq_linear_w4a16_bf16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
+    """awq_linear_w4a16 with bf16 activations: x bf16 [m, k] -> y bf16 [m, n]
+    (inv_s16 and the packed tensors as for fp16)."""
+    return _linear(x, qweight, scales, qzeros, inv_s16, g, out, True)
+
+
+def _linear(x, qweight, scales, qzeros, inv_s16, g, out, bf):
     torch = _torch()
-    _dev_tensor(x, torch.float16, "x", 2)
+    adt = torch.bfloat16 if bf else torch.float16
+    _dev_tensor(x, adt, "x", 2)
     _dev_tensor(qweight, torch.int32, "qweight", 2)
     _dev_tensor(scales, torch.float16, "scales", 2)
     _dev_tensor(qzeros, torch.int32, "qzeros", 2)
@@ -263,11 +275,12 @@ def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
         _dev_tensor(inv_s16, torch.float16, "inv_s16", 1)
         if inv_s16.shape[0] != k:
             raise ValueError("inv_s16 must have k entries")
-    y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
-    _out_tensor(y, torch.float16, (m, n), "y")
-    st = _lib.load().awq_linear_w4a16(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
-                                      _ptr(inv_s16), m, n, k, g, _ptr(y), _stream())
-    _lib.check("awq_linear_w4a16", st)
+    y = out if out is not None else torch.empty((m, n), dtype=adt, device=x.device)
+    _out_tensor(y, adt, (m, n), "y")
+    fn = "awq_linear_w4a16_bf16" if bf else "awq_linear_w4a16"
+    st = getattr(_lib.load(), fn)(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
+                                  _ptr(inv_s16), m, n, k, g, _ptr(y), _stream())
+    _lib.check(fn, st)
     return y
 
 
@@ -276,14 +289,24 @@ def awq_linear_w4a16_group(items, g=128):
     up) in one call.  ``items`` holds up to four tuples (x, qweight, scales,
     qzeros, inv_s16, out) with x fp16 [m, k] and out fp16 [m, n] or None.
     Returns the list of outputs; each equals awq_linear_w4a16 of that linear."""
+    return _linear_group(items, g, False)
+
+
+def awq_linear_w4a16_group_bf16(items, g=128):
+    """awq_linear_w4a16_group with bf16 activations (x and out bf16)."""
+    return _linear_group(items, g, True)
+
+
+def _linear_group(items, g, bf):
     torch = _torch()
+    adt = torch.bfloat16 if bf else torch.float16
     if not 1 <= len(items) <= 4:
         raise ValueError("a group holds 1 to 4 linears")
     arr = (_lib.LinearItem * len(items))()
     outs = []
     m = k = None
     for i, (x, qweight, scales, qzeros, inv_s16, out) in enumerate(items):
-        _dev_tensor(x, torch.float16, "x", 2)
+        _dev_tensor(x, adt, "x", 2)
         _dev_tensor(qweight, torch.int32, "qweight", 2)
         _dev_tensor(scales, torch.float16, "scales", 2)
         _dev_tensor(qzeros, torch.int32, "qzeros", 2)
@@ -299,12 +322,13 @@ def awq_linear_w4a16_group(items, g=128):
             _dev_tensor(inv_s16, torch.float16, "inv_s16", 1)
             if inv_s16.shape[0] != k:
                 raise ValueError(f"linear {i}: inv_s16 must have k entries")
-        y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
-        _out_tensor(y, torch.float16, (m, n), "y")
+        y = out if out is not None else torch.empty((m, n), dtype=adt, device=x.device)
+        _out_tensor(y, adt, (m, n), "y")
         a = arr[i]
         a.x, a.inv_s16, a.qweight = _ptr(x), _ptr(inv_s16), _ptr(qweight)
         a.scales, a.qzeros, a.y, a.n = _ptr(scales), _ptr(qzeros), _ptr(y), n
         outs.append(y)
-    st = _lib.load().awq_linear_w4a16_group(arr, len(items), m, k, g, _stream())
-    _lib.check("awq_linear_w4a16_group", st)
+    fn = "awq_linear_w4a16_group_bf16" if bf else "awq_linear_w4a16_group"
+    st = getattr(_lib.load(), fn)(arr, len(items), m, k, g, _stream())
+    _lib.check(fn, st)
     return outs

@@ -50,6 +50,8 @@ class LinearItem(C.Structure):
 
 SIGNATURES["awq_linear_w4a16_group"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
                                                   C.c_int32, C.c_void_p])
+SIGNATURES["awq_linear_w4a16_bf16"] = SIGNATURES["awq_linear_w4a16"]
+SIGNATURES["awq_linear_w4a16_group_bf16"] = SIGNATURES["awq_linear_w4a16_group"]
 
 _lib = None
 

@@ -225,6 +225,52 @@ awq_status check_linear_args(const char* fn, const uint16_t* x, const uint32_t* 
   return AWQ_OK;
 }
 
+awq_status linear_impl(const char* fn, const uint16_t* x, const uint32_t* qweight,
+                       const uint16_t* scales, const uint32_t* qzeros, const uint16_t* inv_s16,
+                       int64_t m, int64_t n, int64_t k, int32_t g, uint16_t* y, int32_t bf,
+                       void* stream) {
+  g_err[0] = 0;
+  awq_status st0 = check_linear_args(fn, x, qweight, scales, qzeros, inv_s16, m, n, k, g, y);
+  if (st0 != AWQ_OK) return st0;
+  awq::LinItem it{x, inv_s16, qweight, scales, qzeros, y, n};
+  it.bf = bf;
+  void* scratch = nullptr;
+  awq_status st = get_scratch(awq::linear_group_scratch_bytes(&it, 1, m, k, g), &scratch);
+  if (st != AWQ_OK) return st;
+  hipError_t e = awq::launch_linear_group(&it, 1, m, k, g, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return AWQ_OK;
+}
+
+awq_status linear_group_impl(const char* fn, const awq_linear_item* items, int32_t count, int64_t m,
+                             int64_t k, int32_t g, int32_t bf, void* stream) {
+  g_err[0] = 0;
+  if (!items) {
+    snprintf(g_err, sizeof(g_err), "%s: null items", fn);
+    return AWQ_ERR_NULL;
+  }
+  if (count < 1 || count > awq::kGroupMax) {
+    snprintf(g_err, sizeof(g_err), "%s: count=%lld outside 1..%lld", fn, (long long)count,
+             (long long)awq::kGroupMax);
+    return AWQ_ERR_SHAPE;
+  }
+  awq::LinItem li[awq::kGroupMax];
+  for (int32_t i = 0; i < count; ++i) {
+    const awq_linear_item& it = items[i];
+    awq_status st = check_linear_args(fn, it.x, it.qweight, it.scales, it.qzeros, it.inv_s16, m, it.n,
+                                      k, g, it.y);
+    if (st != AWQ_OK) return st;
+    li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
+    li[i].bf = bf;
+  }
+  void* scratch = nullptr;
+  awq_status st = get_scratch(awq::linear_group_scratch_bytes(li, count, m, k, g), &scratch);
+  if (st != AWQ_OK) return st;
+  hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return AWQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,39 +278,25 @@ extern "C" {
 awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                             const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
                             int64_t k, int32_t g, uint16_t* y, void* stream) {
-  g_err[0] = 0;
-  awq_status st0 = check_linear_args("awq_linear_w4a16", x, qweight, scales, qzeros, inv_s16, m, n, k,
-                                     g, y);
-  if (st0 != AWQ_OK) return st0;
-  const awq::LinItem it{x, inv_s16, qweight, scales, qzeros, y, n};
-  void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_group_scratch_bytes(&it, 1, m, k, g), &scratch);
-  if (st != AWQ_OK) return st;
-  hipError_t e = awq::launch_linear_group(&it, 1, m, k, g, scratch, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16 launch");
-  return AWQ_OK;
+  return linear_impl("awq_linear_w4a16", x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, 0,
+                     stream);
+}
+
+awq_status awq_linear_w4a16_bf16(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                                 const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
+                                 int64_t n, int64_t k, int32_t g, uint16_t* y, void* stream) {
+  return linear_impl("awq_linear_w4a16_bf16", x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, 1,
+                     stream);
 }
 
 awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count, int64_t m, int64_t k,
                                   int32_t g, void* stream) {
-  g_err[0] = 0;
-  if (!items) return fail(AWQ_ERR_NULL, "awq_linear_w4a16_group: null items");
-  if (count < 1 || count > awq::kGroupMax)
-    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16_group: count=%lld outside 1..%lld", count, awq::kGroupMax);
-  awq::LinItem li[awq::kGroupMax];
-  for (int32_t i = 0; i < count; ++i) {
-    const awq_linear_item& it = items[i];
-    awq_status st = check_linear_args("awq_linear_w4a16_group", it.x, it.qweight, it.scales, it.qzeros,
-                                      it.inv_s16, m, it.n, k, g, it.y);
-    if (st != AWQ_OK) return st;
-    li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
-  }
-  void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_group_scratch_bytes(li, count, m, k, g), &scratch);
-  if (st != AWQ_OK) return st;
-  hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group launch");
-  return AWQ_OK;
+  return linear_group_impl("awq_linear_w4a16_group", items, count, m, k, g, 0, stream);
+}
+
+awq_status awq_linear_w4a16_group_bf16(const awq_linear_item* items, int32_t count, int64_t m,
+                                       int64_t k, int32_t g, void* stream) {
+  return linear_group_impl("awq_linear_w4a16_group_bf16", items, count, m, k, g, 1, stream);
 }
 
 awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,

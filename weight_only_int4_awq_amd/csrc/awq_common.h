@@ -37,6 +37,33 @@ __device__ __forceinline__ bool f16_nonfinite(uint16_t b) {
 
 // binary16 round-to-nearest-even of a float64, from the float64 bits (one
 // rounding; subnormal results kept; overflow to inf; NaN stays NaN).
+// bf16 activations: a bf16 bit pattern as float (exact), a float rounded to
+// bf16 (nearest, ties to even; NaN stays NaN), and 16-bit activation patterns
+// as fp16: fp16 patterns unchanged, bf16 patterns rounded once to fp16 (exact
+// for |x| in the fp16 normal range [2^-14, 65504]).
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t f2bf_rn(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t act_h(uint16_t raw, bool bf) {
+  return bf ? f2h_rn(bf2f(raw)) : raw;
+}
+__device__ __forceinline__ uint32_t act2_h(uint32_t raw, bool bf) {
+  if (!bf) return raw;
+  return (uint32_t)f2h_rn(bf2f((uint16_t)raw)) | ((uint32_t)f2h_rn(bf2f((uint16_t)(raw >> 16))) << 16);
+}
+__device__ __forceinline__ uint4 act8_h(uint4 raw, bool bf) {
+  if (!bf) return raw;
+  return make_uint4(act2_h(raw.x, true), act2_h(raw.y, true), act2_h(raw.z, true), act2_h(raw.w, true));
+}
+// an output value rounded once to the activation type
+__device__ __forceinline__ uint16_t f2act(float f, bool bf) { return bf ? f2bf_rn(f) : f2h_rn(f); }
+
 __host__ __device__ __forceinline__ uint16_t f64_to_f16_rn(double d) {
   uint64_t b = __builtin_bit_cast(uint64_t, d);
   uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;

@@ -52,6 +52,7 @@ struct LinItem {
   const uint32_t* qz;
   uint16_t* y;
   int64_t n;
+  int32_t bf = 0;          // 1: x and y hold bf16 patterns (the same for every item of a call)
 };
 
 // Scratch bytes a call of count linears (same m, k, g) needs for the staged

@@ -79,7 +79,7 @@ __device__ __forceinline__ int slot_nibble(int s) { return (s >> 1) + 4 * (s & 1
 template <int G>
 __global__ __launch_bounds__(256) void linear_prep_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s, int64_t m, int64_t k,
-    int64_t n_pairs, uint16_t* __restrict__ a_st, float2* __restrict__ tu) {
+    int64_t n_pairs, uint16_t* __restrict__ a_st, float2* __restrict__ tu, bool bf) {
   constexpr int WPL = G / 32;                  // qweight words per lane per group
   constexpr int HPL = G / 4;                   // staged halves per lane per group
   const int64_t ng = k / G;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void linear_prep_kernel(
       const int nib = slot_nibble(s);
       uint16_t h = 0;
       if (t < m) {
-        float xv = h2f(x[t * k + kw + nib]);
+        float xv = h2f(act_h(x[t * k + kw + nib], bf));
         if (inv_s != nullptr) xv *= h2f(inv_s[kw + nib]);   // exact: fp16 x fp16
         uint16_t hb = f2h_rn(xv);
         h = lo_row ? f2h_rn(xv - h2f(hb)) : hb;
@@ -134,7 +134,8 @@ template <int G, int TC>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, const uint16_t* __restrict__ a_st,
-    const float2* __restrict__ tu, int64_t m, int64_t n, int64_t k, uint16_t* __restrict__ y) {
+    const float2* __restrict__ tu, int64_t m, int64_t n, int64_t k, uint16_t* __restrict__ y,
+    bool bf) {
   constexpr int WPL = G / 32;
   constexpr int HPL = G / 4;
   __shared__ floatx4_t red[kSkinnyWaves][TC][64];
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void linear_skinny_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t t = (int64_t)tc * kSkinnyTok + 4 * c + i;
-          if (t < m) y[t * n + col] = f2h_rn(s[i] + o[i]);
+          if (t < m) y[t * n + col] = f2act(s[i] + o[i], bf);
         }
       }
     }
@@ -248,6 +249,7 @@ struct LinGroup {
   int32_t ks[kGroupMax];
   float* part[kGroupMax];
   int32_t gmax;                      // most groups of a K slice (LDS rows)
+  int32_t bf;                        // 1: x and y hold bf16 patterns (else fp16)
 };
 struct LinPick {
   const uint16_t* x;
@@ -344,7 +346,7 @@ __device__ __forceinline__ void gemv_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, int64_t n, int64_t k, uint16_t* __restrict__ y,
-    int bid, int grid_in) {
+    int bid, int grid_in, bool bf) {
   constexpr int WPL = G / 32;            // qweight words per lane per group
   constexpr int HPL = G / 4;             // staged halves per (group, lane group, row)
   constexpr int LPG = G / 8;             // words per group
@@ -454,8 +456,9 @@ __device__ __forceinline__ void gemv_body(
   // ---- 4. stage x_tilde (hi, lo) and the offset sums in LDS
   if (tid < HPL / 2) reinterpret_cast<uint32_t*>(zblk)[tid] = 0u;
   const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-  auto stage = [&](int wi, const uint4& xq, const uint4& sq) {
+  auto stage = [&](int wi, const uint4& xraw, const uint4& sq) {
     const uint4 sv_ = has_inv ? sq : ones;
+    const uint4 xq = act8_h(xraw, bf);
     const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
     const uint32_t sw[4] = {sv_.x, sv_.y, sv_.z, sv_.w};
     // hi = fp16_rn(x s) (v_pk_mul_f16) and lo = fp16_rn(x s - hi)
@@ -630,7 +633,7 @@ __device__ __forceinline__ void gemv_body(
 #pragma unroll
       for (int wv = 0; wv < kGemvWaves; ++wv) sum += red[(bi * kGemvWaves + wv) * 16 + lane];
       const int64_t col = ((int64_t)bid + (int64_t)bi * grid) * 16 + lane;
-      if (col < n) y[col] = f2h_rn(sum);
+      if (col < n) y[col] = f2act(sum, bf);
     }
   }
 }
@@ -638,7 +641,7 @@ __device__ __forceinline__ void gemv_body(
 template <int G, bool SZV, int W>
 __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(const LinGroup gp, int64_t k) {
   const LinPick L = pick_linear(gp);
-  gemv_body<G, SZV, W>(L.x, L.inv, L.qw, L.sc, L.qz, L.n, k, L.y, L.bid, L.grid);
+  gemv_body<G, SZV, W>(L.x, L.inv, L.qw, L.sc, L.qz, L.n, k, L.y, L.bid, L.grid, gp.bf != 0);
 }
 
 // ---------------------------------------------------------------- skinny, 2 <= m <= 32
@@ -654,7 +657,7 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(const LinGroup g
 template <int G>
 __global__ __launch_bounds__(256) void linear_prep16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s, int64_t m, int64_t k,
-    int64_t n_pairs, uint16_t* __restrict__ a16, float2* __restrict__ tu16) {
+    int64_t n_pairs, uint16_t* __restrict__ a16, float2* __restrict__ tu16, bool bf) {
   constexpr int WPL = G / 32, HPL = G / 4;
   const int64_t ng = k / G;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (chunk, group)
@@ -673,7 +676,7 @@ __global__ __launch_bounds__(256) void linear_prep16_kernel(
       const int nib = slot_nibble(s);
       uint16_t h = 0;
       if (t < m) {
-        float xv = h2f(x[t * k + kw + nib]);
+        float xv = h2f(act_h(x[t * k + kw + nib], bf));
         if (inv_s != nullptr) xv *= h2f(inv_s[kw + nib]);   // exact: fp16 x fp16
         h = f2h_rn(xv);
       }
@@ -718,7 +721,7 @@ __global__ __launch_bounds__(kSk16Threads, 4) void linear_skinny16_kernel(
     const uint16_t* __restrict__ a16, const float2* __restrict__ tu16,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, bool bf) {
   constexpr int WPL = G / 32, HPL = G / 4, LPG = G / 8;
   constexpr int W = kSk16Waves;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -937,7 +940,7 @@ __global__ __launch_bounds__(kSk16Threads, 4) void linear_skinny16_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t t = (int64_t)tc * 16 + 4 * c + e;
-          if (t < m && col < n) y[t * n + col] = f2h_rn(v[e]);
+          if (t < m && col < n) y[t * n + col] = f2act(v[e], bf);
         }
       }
     }
@@ -960,7 +963,7 @@ __device__ __forceinline__ void skinny_fused_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
-    uint16_t* __restrict__ y, int bid, int grid_in) {
+    uint16_t* __restrict__ y, int bid, int grid_in, bool bf) {
   constexpr int WPL = G / 32, LPG = G / 8;
   constexpr int W = kSk16Waves;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1133,7 +1136,7 @@ __device__ __forceinline__ void skinny_fused_body(
                                  : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
 #pragma unroll
         for (int tc = 0; tc < TC; ++tc) {
-          const uint4 xv = xq[p][tc][i];
+          const uint4 xv = act8_h(xq[p][tc][i], bf);
           const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, sv.x));
           const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
           const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
@@ -1194,7 +1197,7 @@ __device__ __forceinline__ void skinny_fused_body(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t t = (int64_t)tc * 16 + 4 * c + e;
-          if (t < m && col < n) y[t * n + col] = f2h_rn(v[e]);
+          if (t < m && col < n) y[t * n + col] = f2act(v[e], bf);
         }
       }
     }
@@ -1217,7 +1220,7 @@ __device__ __forceinline__ void skinny_gm_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, int64_t m, int64_t n, int64_t k,
-    uint16_t* __restrict__ y, int bid, int grid) {
+    uint16_t* __restrict__ y, int bid, int grid, bool bf) {
   constexpr int WPL = G / 32, LPG = G / 8;
   constexpr int W = kSk16Waves;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1348,7 +1351,7 @@ __device__ __forceinline__ void skinny_gm_body(
       for (int i = 0; i < WPL; ++i) {
         const uint4 sv = has_inv ? *reinterpret_cast<const uint4*>(inv_l + j * G + 8 * (WPL * c + i))
                                  : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-        const uint4 xv = xq[p][i];
+        const uint4 xv = act8_h(xq[p][i], bf);
         const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, sv.x));
         const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
         const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
@@ -1430,7 +1433,7 @@ __device__ __forceinline__ void skinny_gm_body(
         for (int e = 0; e < 4; ++e) {
           const float v = sacc[e];
           const int64_t t = 4 * c + e;
-          if (t < m && col < n) y[t * n + col] = f2h_rn(v);
+          if (t < m && col < n) y[t * n + col] = f2act(v, bf);
         }
       }
     }
@@ -1444,7 +1447,8 @@ template <int G, bool SZV, int NB, int PF>
 __global__ __launch_bounds__(kSk16Threads, AWQ_SKINNY_GM_MINW) void linear_skinny_gm_kernel(const LinGroup gp,
                                                                            int64_t m, int64_t k) {
   const LinPick L = pick_linear(gp);
-  skinny_gm_body<G, SZV, NB, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid);
+  skinny_gm_body<G, SZV, NB, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid,
+                                 gp.bf != 0);
 }
 
 // LDS of the group-major skinny kernel: inv_s (whole 1 KiB copies), scale|zero
@@ -1463,7 +1467,8 @@ template <int G, int TC, bool SZV, int PF>
 __global__ __launch_bounds__(kSk16Threads, 2) void linear_skinny_fused_kernel(const LinGroup gp,
                                                                               int64_t m, int64_t k) {
   const LinPick L = pick_linear(gp);
-  skinny_fused_body<G, TC, SZV, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid);
+  skinny_fused_body<G, TC, SZV, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid,
+                                    gp.bf != 0);
 }
 
 size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
@@ -1597,7 +1602,7 @@ __global__ __launch_bounds__(256) void linear_xprep_kernel(const LinGroup gp, in
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks;
        c += (int64_t)gridDim.x * 256) {
     const int64_t kk = (c % (k / 8)) * 8;
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + c * 8);
+    const uint4 xv = act8_h(*reinterpret_cast<const uint4*>(x + c * 8), gp.bf != 0);
     const uint4 iv = has_inv ? *reinterpret_cast<const uint4*>(inv_s + kk)
                              : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
     const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, iv.x));
@@ -1827,7 +1832,7 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
         for (int e = 0; e < 16; ++e) {
           const int64_t t = m0 + wm * RW + bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
           const int64_t cidx = n0 + wn * CW + bn * 32 + (lane & 31);
-          if (t < m && cidx < n) y[t * n + cidx] = f2h_rn(acc[bm][bn][e]);
+          if (t < m && cidx < n) y[t * n + cidx] = f2act(acc[bm][bn][e], gp.bf != 0);
         }
     return;
   }
@@ -1897,7 +1902,7 @@ __global__ __launch_bounds__(256) void linear_gemm_reduce_kernel(const LinGroup 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (col + i < n) y[t * n + col + i] = f2h_rn(sum[i]);
+      if (col + i < n) y[t * n + col + i] = f2act(sum[i], gp.bf != 0);
   }
 }
 
@@ -1941,6 +1946,7 @@ static int split_group_grid(const LinItem* items, int count, int64_t slots, int 
   }
   for (int l = count; l <= kGroupMax; ++l) gp.wg0[l] = start;
   gp.count = count;
+  gp.bf = items[0].bf;
   return nb;
 }
 
@@ -1974,6 +1980,7 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   const uint16_t* inv_s16 = it.inv;
   uint16_t* y = it.y;
   const int64_t n = it.n;
+  const bool bf = it.bf != 0;
   // 16 < m <= 32: prep16 + skinny16 when its LDS plan fits (with 32 tokens the
   // activation operand formed once per call beats forming it per item)
   if (m > 16 && m <= 32 && offsets32_ok(&it, 1, k)) {
@@ -1999,7 +2006,7 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
       float2* tu16 = reinterpret_cast<float2*>(sp16 + align256((size_t)tcs * (size_t)k * 16 * 2));
       const int64_t n_pairs = tcs * ng_all;
       hipLaunchKernelGGL(linear_prep16_kernel<G>, dim3((unsigned)((n_pairs + 3) / 4)), dim3(256), 0,
-                         stream, x, inv_s16, m, k, n_pairs, a16, tu16);
+                         stream, x, inv_s16, m, k, n_pairs, a16, tu16, bf);
       const dim3 gd((unsigned)grid), bd(kSk16Threads);
 #define AWQ_SK16(SZ)                                                                           \
   {                                                                                            \
@@ -2009,7 +2016,7 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
       if (e_ != hipSuccess) return e_;                                                         \
     }                                                                                          \
     hipLaunchKernelGGL((linear_skinny16_kernel<G, 2, SZ, 1>), gd, bd, lds, stream, a16, tu16,   \
-                       qweight, scales, qzeros, m, n, k, y);                                   \
+                       qweight, scales, qzeros, m, n, k, y, bf);                               \
   }
       if (szv) AWQ_SK16(true) else AWQ_SK16(false)
 #undef AWQ_SK16
@@ -2024,25 +2031,25 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   float2* tu = reinterpret_cast<float2*>(sp + align256((size_t)tc * (size_t)k * 16 * 2));
   const int64_t n_pairs = tc * ng;
   hipLaunchKernelGGL(linear_prep_kernel<G>, dim3((unsigned)((n_pairs + 3) / 4)), dim3(256), 0,
-                     stream, x, inv_s16, m, k, n_pairs, a_st, tu);
+                     stream, x, inv_s16, m, k, n_pairs, a_st, tu, bf);
   dim3 grid((unsigned)((n + 15) / 16));
   dim3 block(kSkinnyWaves * 64);
   switch (tc) {
     case 1:
       hipLaunchKernelGGL((linear_skinny_kernel<G, 1>), grid, block, 0, stream, qweight, scales,
-                         qzeros, a_st, tu, m, n, k, y);
+                         qzeros, a_st, tu, m, n, k, y, bf);
       break;
     case 2:
       hipLaunchKernelGGL((linear_skinny_kernel<G, 2>), grid, block, 0, stream, qweight, scales,
-                         qzeros, a_st, tu, m, n, k, y);
+                         qzeros, a_st, tu, m, n, k, y, bf);
       break;
     case 3:
       hipLaunchKernelGGL((linear_skinny_kernel<G, 3>), grid, block, 0, stream, qweight, scales,
-                         qzeros, a_st, tu, m, n, k, y);
+                         qzeros, a_st, tu, m, n, k, y, bf);
       break;
     default:
       hipLaunchKernelGGL((linear_skinny_kernel<G, 4>), grid, block, 0, stream, qweight, scales,
-                         qzeros, a_st, tu, m, n, k, y);
+                         qzeros, a_st, tu, m, n, k, y, bf);
       break;
   }
   return hipGetLastError();
@@ -2096,6 +2103,7 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
       xg.y[l] = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + (size_t)l * slot_bytes);
     }
     xg.count = cnt;
+    xg.bf = its[0].bf;
     const int64_t chunks = m * (k / 8);
     const int64_t pgrid = (chunks + 255) / 256 < 4096 ? (chunks + 255) / 256 : 4096;
     hipLaunchKernelGGL(linear_xprep_kernel, dim3((unsigned)pgrid, (unsigned)cnt), dim3(256), 0,
@@ -2128,6 +2136,7 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
       }
       for (int l = cnt; l <= kGroupMax; ++l) gg.wg0[l] = total;
       gg.count = cnt;
+      gg.bf = its[0].bf;
       gg.gmax = gmax;
       if (bm == 64)
         hipLaunchKernelGGL((linear_gemm_kernel<G, 64>), dim3((unsigned)total), dim3(256), lds, stream,
