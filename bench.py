@@ -16,6 +16,8 @@ One step is one pass of the whole path over one batch of synthetic input:
   prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
             in the decode (4 calls, each one activation-prep launch and one
             GEMM launch over the tiles of its linears);
+  bf16      the M = 1 decode of the stack and the layer's M = 2048 prefill
+            with bf16 activations and outputs (awq_linear_w4a16_group_bf16);
   3/8-bit   the stack searched at 3 and at 8 bits (per-linear alpha, 128
             calibration tokens) and packed in those layouts: all 224 linears
             at M = 1 (one awq_linear_wbit call each, replayed as one HIP
@@ -346,6 +348,42 @@ def main():
             qw, sc, qz, inv = wstacks[wb][layer][li]
             P.awq_linear_wbit(XP[S.INPUT_OF[nm]], qw, sc, qz, inv, g=128, w_bit=wb, out=YP[li])
 
+    # bf16 activations: the same inputs rounded to bf16, bf16 outputs
+    XRb = [{inp: XR[1][layer][inp].to(torch.bfloat16) for inp in inputs} for layer in range(L)]
+    YRb = [[torch.empty((1, n), dtype=torch.bfloat16, device=dev) for nm, n, k in shapes] for _ in range(L)]
+    XPb = {inp: XP[inp].to(torch.bfloat16) for inp in inputs}
+    YPb = [torch.empty((2048, n), dtype=torch.bfloat16, device=dev) for nm, n, k in shapes]
+
+    def decode_bf16():
+        st = stacks[128]
+        for layer in range(L):
+            for grp in groups:
+                items = []
+                for li in grp:
+                    nm = shapes[li][0]
+                    qw, sc, qz, _ = st[layer][li]
+                    items.append((XRb[layer][S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2],
+                                  YRb[layer][li]))
+                P.awq_linear_w4a16_group_bf16(items, g=128)
+
+    def prefill_bf16(layer):
+        st = stacks[128]
+        for grp in groups:
+            items = []
+            for li in grp:
+                nm = shapes[li][0]
+                qw, sc, qz, _ = st[layer][li]
+                items.append((XPb[S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2], YPb[li]))
+            P.awq_linear_w4a16_group_bf16(items, g=128)
+
+    decode_bf16()
+    prefill_bf16(0)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        decode_bf16()
+    graphs["bf16"] = gr
+
     for wb in wbits:                  # eager runs first: the library scratch is allocated
         decode_wbit(wb)
         prefill_wbit(wb, 0)
@@ -377,7 +415,8 @@ def main():
 
     phases = (["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["decode_fused"] + ["prefill"] +
               [f"big_{big[bi][0]}_m{m}" for bi, m in big_cases] +
-              [f"decode_w{wb}_m1" for wb in wbits] + [f"prefill_w{wb}" for wb in wbits])
+              [f"decode_w{wb}_m1" for wb in wbits] + [f"prefill_w{wb}" for wb in wbits] +
+              ["decode_bf16_m1", "prefill_bf16"])
     acc = {p: 0.0 for p in phases}
 
     def step(i, timed):
@@ -403,6 +442,10 @@ def main():
         for wi, wb in enumerate(wbits):
             prefill_wbit(wb, layer)
             ev[e0 + len(wbits) + wi].record(stream)
+        graphs["bf16"].replay()
+        ev[e0 + 2 * len(wbits)].record(stream)
+        prefill_bf16(layer)
+        ev[e0 + 2 * len(wbits) + 1].record(stream)
         if timed:
             return ev
         return None
@@ -466,6 +509,13 @@ def main():
         t = acc[f"prefill_w{wb}"] / K
         rows[f"prefill_w{wb}_m2048"] = {"us_per_layer": t * 1e6, "TFLOPs": prefill_flops / t / 1e12,
                                         "frac_mfma_peak": prefill_flops / t / 1e12 / F16_MFMA_PEAK_TFLOPS}
+    t = acc["decode_bf16_m1"] / K
+    rows["decode_bf16_g128_m1"] = {"us_per_stack": t * 1e6, "us_per_linear": t * 1e6 / nlin,
+                                   "GBps": bytes_by[(128, 1)] / t / 1e9,
+                                   "frac_hbm_peak": bytes_by[(128, 1)] / t / 1e9 / HBM_PEAK_GBS}
+    t = acc["prefill_bf16"] / K
+    rows["prefill_bf16_m2048"] = {"us_per_layer": t * 1e6, "TFLOPs": prefill_flops / t / 1e12,
+                                  "frac_mfma_peak": prefill_flops / t / 1e12 / F16_MFMA_PEAK_TFLOPS}
     # the two 122 MB shapes (28672<-8192, 8192<-28672) at M = 1 together
     bp = [rows[f"llama3_70b_{nm}_m1"] for nm in ("gate_up", "down")]
     bp_bytes = sum(gemv_bytes(1, r["n"], r["k"], 128) for r in bp)
@@ -495,7 +545,8 @@ def main():
                                "search, int4 g128 pack) on one layer + 32-layer decode at M=1/8/32/128 "
                                "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048 + llama3-70b-"
                                "shaped linears at M=1/16 (cold copies) + the stack at 3 and 8 bits "
-                               "(M=1 decode, M=2048 prefill of one layer)",
+                               "(M=1 decode, M=2048 prefill of one layer) + bf16 activations (M=1 "
+                               "decode, M=2048 prefill)",
                    "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32, 128],
                    "m_prefill": 2048, "m_calib": m_cal, "n_grid": n_grid, "group_size": [128, 64]},
         "gemm_tflops_m2048": round(rows["prefill_m2048"]["TFLOPs"], 2),
