@@ -49,6 +49,11 @@ contains inf or NaN is "non-finite"; pack writes q = 0, z = 0 and the fp16
 NaN 0x7E00 as its scale and counts it.  In the search such an alpha gets an
 infinite loss.
 
+Mixed-precision baseline (a reading; the pages give the ratio only): the
+protected channels are the round(frac * K) largest a_k (ties to the lower
+index); the rest of W is quantized with the same RTN quantizer (s = 1, groups
+over all channels) and the protected columns keep their fp16 values.
+
 Parity status of each function is stated in its docstring ("pinned by ..." or
 "parity unpinned").
 """
@@ -496,3 +501,75 @@ def check_linear(y16, y_ref, tol: float = 5e-3):
     raw = float(np.max(err[big] / np.abs(yr[big]))) if big.any() else 0.0
     worst = float(np.max(ratio))
     return bool(np.all(np.isfinite(y)) and worst <= 1.0), worst, raw
+
+
+# ----------------------------------------------------------------------------
+# mixed-precision baseline ([jsqmd] 二.1(1): a small share (0.1 - 1 %) of the
+# weights, on the input channels with large activations, matters most and
+# loses accuracy under direct quantization; 五.1: protection ratio 0.1 - 1 %
+# by default.  [csdn]: mixed-precision optimisation named beside the scaling.)
+# The contrasting approach to the search: keep those channels in fp16 and
+# quantize the rest with plain round-to-nearest.
+
+def salient_count(k: int, frac: float) -> int:
+    """Number of protected channels: round(frac * k), at least 0, at most k."""
+    return int(min(max(int(np.floor(frac * k + 0.5)), 0), k))
+
+
+def salient_channels(a: np.ndarray, count: int) -> np.ndarray:
+    """Indices (ascending) of the ``count`` channels with the largest a_k; among
+    equal a_k the lower index wins.  NaN ranks above +inf.
+
+    Pinned by test_salient_channels_brute_force (every subset of tiny inputs)
+    and its special cases.
+    """
+    a = np.asarray(a, np.float64)
+    key = np.where(np.isnan(a), np.inf, a)
+    nan_first = np.isnan(a).astype(np.int64)
+    # sort by (NaN first, a descending, index ascending)
+    order = np.lexsort((np.arange(a.size), -key, -nan_first))
+    return np.sort(order[:count]).astype(np.int32)
+
+
+def mixed_weight(w16: np.ndarray, idx: np.ndarray, g: int, max_int: int = 15) -> np.ndarray:
+    """The mixed-precision weight as float64 [N, K]: plain RTN (s = 1, the
+    quantizer of every other step) of the whole W, then the protected columns
+    ``idx`` restored to their fp16 values.  Groups are formed over all
+    channels, protected ones included (the plainest reading: quantize, then
+    keep the protected channels).
+
+    Pinned by test_mixed_loss_two_ways (against the masked-activation form of
+    the loss) and test_mixed_extremes (no channel / every channel protected).
+    """
+    w = np.asarray(w16, np.float16).astype(np.float64)
+    deq = fake_quantize(w16, None, g, max_int)[5].copy()
+    deq[:, np.asarray(idx, np.int64)] = w[:, np.asarray(idx, np.int64)]
+    return deq
+
+
+def mixed_loss(w16: np.ndarray, x16: np.ndarray, idx: np.ndarray, g: int,
+               max_int: int = 15) -> float:
+    """L_mixed = sum_{t,n} (sum_k (Wm_nk - W_nk) X_tk)^2 in float64, the search's
+    output-error objective for the mixed-precision weight.
+
+    Pinned by test_mixed_loss_two_ways and test_mixed_extremes.
+    """
+    w = np.asarray(w16, np.float16).astype(np.float64)
+    x = np.asarray(x16, np.float16).astype(np.float64)
+    if fake_quantize(w16, None, g, max_int)[4].any():
+        return float("inf")
+    e = (mixed_weight(w16, idx, g, max_int) - w) @ x.T
+    return float(np.sum(e * e))
+
+
+def linear_mixed_ref(x16, qweight, scales, qzeros, w16, idx, k: int, g: int) -> np.ndarray:
+    """y_ref = x Wm^T in float64 for the packed RTN weights with the protected
+    columns ``idx`` taken from the fp16 weight w16 [N, K] instead.
+
+    Pinned by test_linear_mixed_ref_exact_small (rational sum).
+    """
+    x = exact_f64(x16)
+    wd = dequantized_weight(qweight, scales, qzeros, k, g)
+    ii = np.asarray(idx, np.int64)
+    wd[:, ii] = np.asarray(w16, np.float16).astype(np.float64)[:, ii]
+    return x @ wd.T

@@ -497,3 +497,86 @@ def test_linear_ref_bf16_exact_small():
     # the generator's draws are those of the fp16 generator, rounded to bf16
     xh = S.activations(2, 64, 92, np.array([3]), 40.0).astype(np.float64)
     assert np.all(np.abs(x - xh) <= 2.0 ** -8 * np.abs(xh) + 2.0 ** -10 * np.abs(xh) + 1e-30)
+
+
+def test_salient_channels_brute_force():
+    r = np.random.Generator(np.random.PCG64(2501))
+    for trial in range(200):
+        k = int(r.integers(1, 8))
+        a = r.integers(0, 4, size=k).astype(np.float64)     # many ties
+        if trial % 5 == 0:
+            a[int(r.integers(0, k))] = np.nan
+        if trial % 7 == 0:
+            a[int(r.integers(0, k))] = np.inf
+        rank = np.where(np.isnan(a), np.inf, a)
+        for count in range(k + 1):
+            sel = O.salient_channels(a, count)
+            assert len(sel) == count and np.all(np.diff(sel) > 0)
+            chosen = np.zeros(k, bool)
+            chosen[sel] = True
+            for i in range(k):
+                for j in range(k):
+                    if chosen[i] and not chosen[j]:
+                        # i outranks j: NaN first, then larger a, then lower index
+                        ki = (np.isnan(a[i]), rank[i], -i)
+                        kj = (np.isnan(a[j]), rank[j], -j)
+                        assert ki > kj, (a, count, sel)
+
+
+def test_salient_count():
+    assert O.salient_count(4096, 0.01) == 41
+    assert O.salient_count(14336, 0.01) == 143
+    assert O.salient_count(100, 0.005) == 1          # 0.5 rounds up
+    assert O.salient_count(10, 0.0) == 0 and O.salient_count(10, 2.0) == 10
+
+
+def test_mixed_loss_two_ways():
+    # protecting channels removes their error columns, which is the search loss
+    # at s = 1 on activations whose protected channels are zero
+    g = 32
+    w = S.weights(24, 256, 0.02, 2511)
+    ch = S.outlier_channels(256, 0.03, 2512)
+    x = S.activations(40, 256, 2513, ch, 30.0)
+    a = O.calib_stats(x)
+    idx = O.salient_channels(a, 5)
+    assert set(idx.tolist()) <= set(ch.tolist())       # the outlier channels rank first
+    xm = x.copy()
+    xm[:, idx] = 0
+    lm = O.mixed_loss(w, x, idx, g)
+    l0 = O.search_loss(w, xm, np.ones(256, np.float16), g)
+    assert abs(lm - l0) <= 1e-12 * l0
+    # and protecting the outlier channels beats plain RTN on this input
+    assert lm < 0.5 * O.search_loss(w, x, np.ones(256, np.float16), g)
+
+
+def test_mixed_extremes():
+    g = 64
+    w = S.weights(8, 128, 0.02, 2521)
+    x = S.activations(16, 128, 2522)
+    none = np.zeros(0, np.int32)
+    assert O.mixed_loss(w, x, none, g) == O.search_loss(w, x, np.ones(128, np.float16), g)
+    assert O.mixed_loss(w, x, np.arange(128, dtype=np.int32), g) == 0.0
+    wm = O.mixed_weight(w, np.array([3, 77], np.int32), g)
+    assert np.array_equal(wm[:, [3, 77]], w[:, [3, 77]].astype(np.float64))
+
+
+def test_linear_mixed_ref_exact_small():
+    g = 32
+    w = _random_wp(3, 64, 2531)
+    x = S.activations(2, 64, 2532, np.array([9]), 30.0)
+    idx = np.array([9, 40], np.int32)
+    qw, sc, qz, _ = O.pack_int4(w, None, g)
+    y = O.linear_mixed_ref(x, qw, sc, qz, w, idx, 64, g)
+    for t in range(2):
+        for n in range(3):
+            acc = Fraction(0)
+            for c in range(64):
+                if c in (9, 40):
+                    wv = Fraction(float(w[n, c]))
+                else:
+                    code = (int(qw[n, c // 8]) >> (4 * (c % 8))) & 0xF
+                    j = c // g
+                    zero = (int(qz[n, j // 8]) >> (4 * (j % 8))) & 0xF
+                    wv = (code - zero) * Fraction(float(sc[n, j]))
+                acc += Fraction(float(x[t, c])) * wv
+            assert abs(y[t, n] - float(acc)) <= 1e-13 * max(1.0, abs(float(acc)))
