@@ -164,6 +164,55 @@ awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k,
                               uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Mixed-precision baseline: awq_salient_channels, awq_channel_mask,
+ * awq_gather_channels, awq_mixed_loss, awq_linear_mixed.
+ * Passage: jsqmd.com page, section 二.1 (1) (a small share, 0.1 - 1 %, of the
+ * weights, on the input channels with large activations, decides the accuracy
+ * and suffers most from direct quantization) and section 五.1 (protection
+ * ratio 0.1 - 1 % by default); CSDN page (mixed-precision optimisation beside
+ * the scaling).  The contrasting approach to the search: keep the protected
+ * channels' weights in fp16, quantize the rest with plain RTN (awq_pack_int4
+ * with s16 = NULL; groups over all channels).
+ *
+ * awq_salient_channels: idx[count] (device int32, ascending) = the channels of
+ *   the `count` largest mean_abs[k] (device float64), ties to the lower index,
+ *   NaN above +inf.  count = round(frac * k) for a protection ratio frac.
+ *   Limits: 0 <= count <= min(k, 1024).
+ * awq_channel_mask: keep16[k] (device fp16) = 1.0, and 0.0 on idx[count].
+ * awq_gather_channels: w_s[n][count] (device fp16) = w[:, idx] of w[n][k].
+ * awq_mixed_loss: *loss (device float64) = sum_{t,n} (sum_k (Wm - W)_nk x_tk)^2
+ *   for the mixed weight Wm (RTN with the columns where keep16 = 0 restored
+ *   to W): the alpha = 0 loss of awq_search_scale on x with those channels
+ *   zeroed.  w [n][k], x [m][k] fp16 (16-byte aligned); workspace of
+ *   awq_mixed_loss_workspace_size(n, k, m, g) bytes, 256-byte aligned.
+ *   Limits: those of awq_search_scale.
+ * awq_linear_mixed: y[m][n] = x Wm^T: awq_linear_w4a16 with inv_s16 = keep16
+ *   (the protected channels leave the quantized product), then
+ *   y = fp16_rn(y + sum_j x[:, idx_j] w_s[:, j]) (fp32 accumulation in j
+ *   order; the quantized part is rounded to fp16 first).  Within 5e-3 *
+ *   max(|y_ref|, rms of the row of y_ref) of the float64 value.  qweight,
+ *   scales, qzeros: the RTN pack of W (layout v1).  Limits: those of
+ *   awq_linear_w4a16; 0 <= count <= min(k, 1024); m <= 1048560.
+ * Errors: NULL pointers, shapes and alignment as stated, before any launch.
+ * ------------------------------------------------------------------------- */
+awq_status awq_salient_channels(const double* mean_abs, int64_t k, int32_t count,
+                                int32_t* idx, void* stream);
+awq_status awq_channel_mask(const int32_t* idx, int32_t count, int64_t k,
+                            uint16_t* keep16, void* stream);
+awq_status awq_gather_channels(const uint16_t* w, int64_t n, int64_t k,
+                               const int32_t* idx, int32_t count, uint16_t* w_s,
+                               void* stream);
+size_t awq_mixed_loss_workspace_size(int64_t n, int64_t k, int64_t m, int32_t g);
+awq_status awq_mixed_loss(const uint16_t* w, const uint16_t* x, const uint16_t* keep16,
+                          int64_t n, int64_t k, int64_t m, int32_t g, double* loss,
+                          void* workspace, size_t ws_bytes, void* stream);
+awq_status awq_linear_mixed(const uint16_t* x, const uint32_t* qweight,
+                            const uint16_t* scales, const uint32_t* qzeros,
+                            const uint16_t* keep16, const uint16_t* w_s,
+                            const int32_t* idx, int32_t count, int64_t m, int64_t n,
+                            int64_t k, int32_t g, uint16_t* y, void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_search_scale_wbit -- awq_search_scale for 3-, 4- or 8-bit codes.
  * Passage: CSDN page, section "量化流程优化" (the weight bit width is a
  * parameter of the search and of the real quantization); jsqmd.com page,

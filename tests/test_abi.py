@@ -35,6 +35,8 @@ def test_header_declares_the_path():
                  "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group", "awq_fold_inv_scale",
                  "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit",
                  "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
+                 "awq_salient_channels", "awq_channel_mask", "awq_gather_channels",
+                 "awq_mixed_loss_workspace_size", "awq_mixed_loss", "awq_linear_mixed",
                  "awq_last_error", "awq_abi_version"):
         assert want in names, names
 
@@ -252,11 +254,57 @@ def test_linear_bf16_argument_errors(lib):
     assert st == 2 and msg.startswith("awq_linear_w4a16_group_bf16"), msg
 
 
+def test_mixed_argument_errors(lib):
+    assert _status(lib, "awq_salient_channels", None, 64, 3, FAKE, None)[0] == 1
+    assert _status(lib, "awq_salient_channels", FAKE, 64, 65, FAKE, None)[0] == 2
+    assert _status(lib, "awq_salient_channels", FAKE, 4096, 1025, FAKE, None)[0] == 2
+    assert _status(lib, "awq_salient_channels", FAKE, 64, -1, FAKE, None)[0] == 2
+    assert _status(lib, "awq_salient_channels", FAKE + 4, 64, 3, FAKE, None)[0] == 3
+    assert _status(lib, "awq_channel_mask", FAKE, 3, 64, None, None)[0] == 1
+    assert _status(lib, "awq_channel_mask", FAKE, 65, 64, FAKE, None)[0] == 2
+    assert _status(lib, "awq_gather_channels", FAKE, 0, 64, FAKE, 3, FAKE, None)[0] == 2
+    assert _status(lib, "awq_gather_channels", FAKE, 8, 64, None, 3, FAKE, None)[0] == 1
+    ws = lib.awq_mixed_loss_workspace_size(64, 256, 16, 128)
+    assert ws > lib.awq_search_workspace_size(64, 256, 16, 128, 1)
+    assert lib.awq_mixed_loss_workspace_size(64, 256, 16, 96) == 0
+    base = [FAKE, FAKE, FAKE, 64, 256, 16, 128, FAKE, FAKE, ws, None]
+    names = ["w", "x", "keep", "n", "k", "m", "g", "loss", "ws", "wsb", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return _status(lib, "awq_mixed_loss", *a)[0]
+
+    assert call(keep=None) == 1
+    assert call(g=96) == 2
+    assert call(m=9000) == 2
+    assert call(x=MISALIGNED) == 3
+    assert call(wsb=ws - 1) == 4
+    lbase = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 64, 256, 128, FAKE, None]
+    lnames = ["x", "qw", "sc", "qz", "keep", "ws", "idx", "cnt", "m", "n", "k", "g", "y", "st"]
+
+    def lcall(**kw):
+        a = list(lbase)
+        for key, v in kw.items():
+            a[lnames.index(key)] = v
+        return _status(lib, "awq_linear_mixed", *a)
+
+    assert lcall(keep=None)[0] == 1
+    assert lcall(ws=None)[0] == 1
+    assert lcall(cnt=257)[0] == 2
+    st, msg = lcall(g=48)
+    assert st == 2 and msg.startswith("awq_linear_mixed"), msg
+    assert lcall(x=MISALIGNED)[0] == 3
+
+
 def test_python_binding_has_the_c_names():
     import weight_only_int4_awq_amd as P
     for name in ("awq_calib_stats", "awq_search_scale", "awq_search_workspace_size",
                  "awq_pack_int4", "awq_linear_w4a16", "awq_search_scale_wbit", "awq_pack_wbit",
-                 "awq_linear_wbit", "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16"):
+                 "awq_linear_wbit", "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
+                 "awq_salient_channels", "awq_channel_mask", "awq_gather_channels", "awq_mixed_loss",
+                 "awq_linear_mixed"):
         assert callable(getattr(P, name))
 
 

@@ -21,6 +21,8 @@ __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "
            "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group",
            "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit", "packed_shapes",
            "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
+           "awq_salient_channels", "awq_channel_mask", "awq_gather_channels", "awq_mixed_loss",
+           "awq_linear_mixed",
            "AWQError", "load"]
 
 
@@ -332,3 +334,97 @@ def _linear_group(items, g, bf):
     st = getattr(_lib.load(), fn)(arr, len(items), m, k, g, _stream())
     _lib.check(fn, st)
     return outs
+
+
+# ---------------------------------------------------------------- mixed-precision baseline
+
+def awq_salient_channels(mean_abs, count):
+    """Indices (int32, ascending) of the ``count`` channels with the largest
+    mean |x| (float64 [k] device tensor), ties to the lower index."""
+    torch = _torch()
+    _dev_tensor(mean_abs, torch.float64, "mean_abs", 1)
+    k = mean_abs.shape[0]
+    idx = torch.empty(max(count, 0), dtype=torch.int32, device=mean_abs.device)
+    st = _lib.load().awq_salient_channels(_ptr(mean_abs), k, count, _ptr(idx) if count > 0 else None,
+                                          _stream())
+    _lib.check("awq_salient_channels", st)
+    return idx
+
+
+def awq_channel_mask(idx, k, out=None):
+    """fp16 [k]: 1.0, and 0.0 on the channels idx (int32 device tensor)."""
+    torch = _torch()
+    _dev_tensor(idx, torch.int32, "idx", 1)
+    keep = out if out is not None else torch.empty(k, dtype=torch.float16, device=idx.device)
+    _out_tensor(keep, torch.float16, (k,), "keep16")
+    cnt = idx.shape[0]
+    st = _lib.load().awq_channel_mask(_ptr(idx) if cnt > 0 else None, cnt, k, _ptr(keep), _stream())
+    _lib.check("awq_channel_mask", st)
+    return keep
+
+
+def awq_gather_channels(w, idx, out=None):
+    """fp16 [n, count]: the columns idx of w (fp16 [n, k])."""
+    torch = _torch()
+    _dev_tensor(w, torch.float16, "w", 2)
+    _dev_tensor(idx, torch.int32, "idx", 1)
+    n, k = w.shape
+    cnt = idx.shape[0]
+    ws = out if out is not None else torch.empty((n, cnt), dtype=torch.float16, device=w.device)
+    _out_tensor(ws, torch.float16, (n, cnt), "w_s")
+    st = _lib.load().awq_gather_channels(_ptr(w), n, k, _ptr(idx) if cnt > 0 else None, cnt,
+                                         _ptr(ws) if cnt > 0 else None, _stream())
+    _lib.check("awq_gather_channels", st)
+    return ws
+
+
+def awq_mixed_loss(w, x, keep16, g=128, workspace=None, out=None):
+    """Output-error loss (float64 [1]) of the mixed-precision weight: RTN of w
+    with the channels where keep16 is 0 kept in fp16."""
+    torch = _torch()
+    _dev_tensor(w, torch.float16, "w", 2)
+    _dev_tensor(x, torch.float16, "x", 2)
+    _dev_tensor(keep16, torch.float16, "keep16", 1)
+    n, k = w.shape
+    m = x.shape[0]
+    if x.shape[1] != k or keep16.shape[0] != k:
+        raise ValueError("w, x and keep16 disagree on k")
+    lib = _lib.load()
+    need = lib.awq_mixed_loss_workspace_size(n, k, m, g)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    loss = out if out is not None else torch.empty(1, dtype=torch.float64, device=w.device)
+    _out_tensor(loss, torch.float64, (1,), "loss")
+    st = lib.awq_mixed_loss(_ptr(w), _ptr(x), _ptr(keep16), n, k, m, g, _ptr(loss), _ptr(workspace),
+                            workspace.numel(), _stream())
+    _lib.check("awq_mixed_loss", st)
+    return loss
+
+
+def awq_linear_mixed(x, qweight, scales, qzeros, keep16, w_s, idx, g=128, out=None):
+    """y = x Wm^T (fp16 [m, n]) for the RTN pack of W with the channels idx kept
+    in fp16 (w_s [n, count], keep16 the matching mask)."""
+    torch = _torch()
+    _dev_tensor(x, torch.float16, "x", 2)
+    _dev_tensor(qweight, torch.int32, "qweight", 2)
+    _dev_tensor(scales, torch.float16, "scales", 2)
+    _dev_tensor(qzeros, torch.int32, "qzeros", 2)
+    _dev_tensor(keep16, torch.float16, "keep16", 1)
+    _dev_tensor(idx, torch.int32, "idx", 1)
+    m, k = x.shape
+    n = qweight.shape[0]
+    cnt = idx.shape[0]
+    if cnt > 0:
+        _dev_tensor(w_s, torch.float16, "w_s", 2)
+        if tuple(w_s.shape) != (n, cnt):
+            raise ValueError("w_s must be [n, count]")
+    if qweight.shape[1] * 8 != k or keep16.shape[0] != k:
+        raise ValueError("packed tensors or keep16 do not match x")
+    y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
+    _out_tensor(y, torch.float16, (m, n), "y")
+    st = _lib.load().awq_linear_mixed(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(keep16),
+                                      _ptr(w_s) if cnt > 0 else None, _ptr(idx) if cnt > 0 else None,
+                                      cnt, m, n, k, g, _ptr(y), _stream())
+    _lib.check("awq_linear_mixed", st)
+    return y
+

@@ -51,6 +51,17 @@ class LinearItem(C.Structure):
 SIGNATURES["awq_linear_w4a16_group"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
                                                   C.c_int32, C.c_void_p])
 SIGNATURES["awq_linear_w4a16_bf16"] = SIGNATURES["awq_linear_w4a16"]
+SIGNATURES["awq_salient_channels"] = (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p])
+SIGNATURES["awq_channel_mask"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p])
+SIGNATURES["awq_gather_channels"] = (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int32,
+                                               C.c_void_p, C.c_void_p])
+SIGNATURES["awq_mixed_loss_workspace_size"] = (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32])
+SIGNATURES["awq_mixed_loss"] = (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                                          C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,
+                                          C.c_void_p])
+SIGNATURES["awq_linear_mixed"] = (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                            C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                            C.c_int64, C.c_int32, C.c_void_p, C.c_void_p])
 SIGNATURES["awq_linear_w4a16_group_bf16"] = SIGNATURES["awq_linear_w4a16_group"]
 
 _lib = None

@@ -19,7 +19,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libawq_mi355x.so"
-SOURCES = ("api.hip", "calib_stats.hip", "search.hip", "pack.hip", "linear.hip", "linear_wbit.hip")
+SOURCES = ("api.hip", "calib_stats.hip", "search.hip", "pack.hip", "linear.hip", "linear_wbit.hip", "mixed.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",

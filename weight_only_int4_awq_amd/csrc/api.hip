@@ -332,4 +332,87 @@ awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uin
   return AWQ_OK;
 }
 
+awq_status awq_salient_channels(const double* mean_abs, int64_t k, int32_t count, int32_t* idx,
+                                void* stream) {
+  g_err[0] = 0;
+  if (!mean_abs || (!idx && count > 0)) return fail(AWQ_ERR_NULL, "awq_salient_channels: null pointer");
+  if (k < 1 || k > 0x7FFFFFFF) return fail(AWQ_ERR_SHAPE, "awq_salient_channels: k=%lld out of range", k);
+  if (count < 0 || count > k || count > awq::kMixedMaxCount)
+    return fail(AWQ_ERR_SHAPE, "awq_salient_channels: count=%lld outside 0..min(k, %lld)", count,
+                awq::kMixedMaxCount);
+  if (!aligned(mean_abs, 8) || (idx && !aligned(idx, 4)))
+    return fail(AWQ_ERR_ALIGN, "awq_salient_channels: misaligned pointer");
+  hipError_t e = awq::launch_salient_select(mean_abs, k, count, idx, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_salient_channels launch");
+  return AWQ_OK;
+}
+
+awq_status awq_channel_mask(const int32_t* idx, int32_t count, int64_t k, uint16_t* keep16,
+                            void* stream) {
+  g_err[0] = 0;
+  if (!keep16 || (!idx && count > 0)) return fail(AWQ_ERR_NULL, "awq_channel_mask: null pointer");
+  if (k < 1 || count < 0 || count > k) return fail(AWQ_ERR_SHAPE, "awq_channel_mask: count=%lld, k=%lld", count, k);
+  if (!aligned(keep16, 2) || (idx && !aligned(idx, 4))) return fail(AWQ_ERR_ALIGN, "awq_channel_mask: misaligned pointer");
+  hipError_t e = awq::launch_channel_mask(idx, count, k, keep16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_channel_mask launch");
+  return AWQ_OK;
+}
+
+awq_status awq_gather_channels(const uint16_t* w, int64_t n, int64_t k, const int32_t* idx,
+                               int32_t count, uint16_t* w_s, void* stream) {
+  g_err[0] = 0;
+  if (!w || ((!idx || !w_s) && count > 0)) return fail(AWQ_ERR_NULL, "awq_gather_channels: null pointer");
+  if (n < 1 || k < 1 || count < 0 || count > k)
+    return fail(AWQ_ERR_SHAPE, "awq_gather_channels: n=%lld, k=%lld out of range", n, k);
+  if (!aligned(w, 2) || (w_s && !aligned(w_s, 2)) || (idx && !aligned(idx, 4)))
+    return fail(AWQ_ERR_ALIGN, "awq_gather_channels: misaligned pointer");
+  hipError_t e = awq::launch_gather_channels(w, n, k, idx, count, w_s, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_gather_channels launch");
+  return AWQ_OK;
+}
+
+size_t awq_mixed_loss_workspace_size(int64_t n, int64_t k, int64_t m, int32_t g) {
+  if (n < 1 || k < 1 || m < 1 || !group_ok(g)) return 0;
+  return awq::mixed_loss_workspace_bytes(n, k, m, g);
+}
+
+awq_status awq_mixed_loss(const uint16_t* w, const uint16_t* x, const uint16_t* keep16, int64_t n,
+                          int64_t k, int64_t m, int32_t g, double* loss, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!w || !x || !keep16 || !loss) return fail(AWQ_ERR_NULL, "awq_mixed_loss: null pointer");
+  if (!group_ok(g)) return fail(AWQ_ERR_SHAPE, "awq_mixed_loss: g=%lld not in {32,64,128}", g);
+  if (k < g || k % g != 0) return fail(AWQ_ERR_SHAPE, "awq_mixed_loss: k=%lld not a positive multiple of g=%lld", k, g);
+  if (n < 1) return fail(AWQ_ERR_SHAPE, "awq_mixed_loss: n=%lld < 1", n);
+  if (m < 1 || m > 8192) return fail(AWQ_ERR_SHAPE, "awq_mixed_loss: m=%lld outside 1..8192", m);
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(keep16, 2) || !aligned(loss, 8))
+    return fail(AWQ_ERR_ALIGN, "awq_mixed_loss: w and x must be 16-byte aligned");
+  const size_t need = awq::mixed_loss_workspace_bytes(n, k, m, g);
+  if (!workspace || ws_bytes < need)
+    return fail(AWQ_ERR_WORKSPACE, "awq_mixed_loss: workspace of %lld bytes < %lld needed", (long long)ws_bytes, (long long)need);
+  if (!aligned(workspace, 256)) return fail(AWQ_ERR_ALIGN, "awq_mixed_loss: workspace must be 256-byte aligned");
+  hipError_t e = awq::launch_mixed_loss(w, x, keep16, n, k, m, g, loss, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_mixed_loss launch");
+  return AWQ_OK;
+}
+
+awq_status awq_linear_mixed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                            const uint32_t* qzeros, const uint16_t* keep16, const uint16_t* w_s,
+                            const int32_t* idx, int32_t count, int64_t m, int64_t n, int64_t k,
+                            int32_t g, uint16_t* y, void* stream) {
+  g_err[0] = 0;
+  if (!keep16 || ((!w_s || !idx) && count > 0)) return fail(AWQ_ERR_NULL, "awq_linear_mixed: null pointer");
+  if (count < 0 || count > k || count > awq::kMixedMaxCount)
+    return fail(AWQ_ERR_SHAPE, "awq_linear_mixed: count=%lld outside 0..min(k, %lld)", count, awq::kMixedMaxCount);
+  if (m > (int64_t)65535 * 16) return fail(AWQ_ERR_SHAPE, "awq_linear_mixed: m=%lld too large", m);
+  if (!aligned(keep16, 2) || (w_s && !aligned(w_s, 2)) || (idx && !aligned(idx, 4)))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_mixed: misaligned pointer");
+  awq_status st = linear_impl("awq_linear_mixed", x, qweight, scales, qzeros, keep16, m, n, k, g, y, 0,
+                              stream);
+  if (st != AWQ_OK) return st;
+  hipError_t e = awq::launch_salient_add(x, idx, count, w_s, m, n, k, y, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_linear_mixed launch");
+  return AWQ_OK;
+}
+
 }  // extern "C"

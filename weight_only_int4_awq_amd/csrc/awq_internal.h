@@ -69,6 +69,24 @@ size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, in
 hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
                                void* scratch, hipStream_t stream);
 
+// mixed-precision baseline (mixed.hip)
+hipError_t launch_salient_select(const double* a, int64_t k, int32_t count, int32_t* idx,
+                                 hipStream_t stream);
+hipError_t launch_channel_mask(const int32_t* idx, int32_t count, int64_t k, uint16_t* keep,
+                               hipStream_t stream);
+hipError_t launch_gather_channels(const uint16_t* w, int64_t n, int64_t k, const int32_t* idx,
+                                  int32_t count, uint16_t* w_s, hipStream_t stream);
+hipError_t launch_mask_rows(const uint16_t* x, const uint16_t* keep, int64_t m, int64_t k,
+                            uint16_t* out, hipStream_t stream);
+hipError_t launch_salient_add(const uint16_t* x, const int32_t* idx, int32_t count,
+                              const uint16_t* w_s, int64_t m, int64_t n, int64_t k, uint16_t* y,
+                              hipStream_t stream);
+size_t mixed_loss_workspace_bytes(int64_t n, int64_t k, int64_t m, int32_t g);
+hipError_t launch_mixed_loss(const uint16_t* w, const uint16_t* x, const uint16_t* keep, int64_t n,
+                             int64_t k, int64_t m, int32_t g, double* loss, void* workspace,
+                             hipStream_t stream);
+constexpr int32_t kMixedMaxCount = 1024;       // protected channels per linear (LDS of the add)
+
 // the linear for 3- and 8-bit weights (layouts of awq_pack_wbit); scratch of
 // linear_wbit_scratch_bytes(m, n, k, g, inv_s16 != NULL) bytes, 256-byte aligned
 size_t linear_wbit_scratch_bytes(int64_t m, int64_t n, int64_t k, int32_t g, bool has_inv);
