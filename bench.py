@@ -18,6 +18,11 @@ One step is one pass of the whole path over one batch of synthetic input:
             GEMM launch over the tiles of its linears);
   bf16      the M = 1 decode of the stack and the layer's M = 2048 prefill
             with bf16 activations and outputs (awq_linear_w4a16_group_bf16);
+  mixed     the mixed-precision baseline (1 % of channels by mean |x| kept in
+            fp16, the rest RTN): the M = 1 decode of the stack with
+            awq_linear_mixed (224 calls as one graph); untimed, its output-
+            error loss beside the RTN and searched losses of layer 0's 7
+            linears over the 512 calibration tokens (the ablation);
   3/8-bit   the stack searched at 3 and at 8 bits (per-linear alpha, 128
             calibration tokens) and packed in those layouts: all 224 linears
             at M = 1 (one awq_linear_wbit call each, replayed as one HIP
@@ -384,6 +389,53 @@ def main():
         decode_bf16()
     graphs["bf16"] = gr
 
+    # mixed-precision baseline: RTN packs, the 1 % protected channels of each
+    # linear (by mean |x| over 128 calibration tokens) and their fp16 columns
+    mixed = []
+    for layer in range(L):
+        stats = {inp: P.awq_calib_stats(XC[layer][inp][:128].contiguous()) for inp in inputs}
+        row = []
+        for li, (nm, n, k) in enumerate(shapes):
+            idx = P.awq_salient_channels(stats[S.INPUT_OF[nm]], int(np.floor(0.01 * k + 0.5)))
+            qw, sc, qz, _ = P.awq_pack_int4(W[layer][li], None, g=128)
+            row.append((qw, sc, qz, P.awq_channel_mask(idx, k), P.awq_gather_channels(W[layer][li], idx), idx))
+        mixed.append(row)
+
+    def decode_mixed():
+        for layer in range(L):
+            for li, (nm, n, k) in enumerate(shapes):
+                qw, sc, qz, keep, ws_, idx = mixed[layer][li]
+                P.awq_linear_mixed(XR[1][layer][S.INPUT_OF[nm]], qw, sc, qz, keep, ws_, idx, g=128,
+                                   out=YR[1][layer][li])
+
+    decode_mixed()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        decode_mixed()
+    graphs["mixed"] = gr
+
+    # the ablation on layer 0 (512 calibration tokens): plain RTN (alpha = 0),
+    # the searched scale and the mixed-precision weight at 1 % and 0.1 %
+    ablation = {}
+    stats0 = {inp: P.awq_calib_stats(XC[0][inp]) for inp in inputs}
+    for li, (nm, n, k) in enumerate(shapes):
+        inp = S.INPUT_OF[nm]
+        ws_a = torch.empty(P.awq_search_workspace_size(n, k, m_cal, 128, n_grid), dtype=torch.uint8, device=dev)
+        best, _, _, losses = P.awq_search_scale(W[0][li], XC[0][inp], stats0[inp], g=128, n_grid=n_grid,
+                                                workspace=ws_a)
+        lm = {}
+        for frac in (0.01, 0.001):
+            idx = P.awq_salient_channels(stats0[inp], int(np.floor(frac * k + 0.5)))
+            lm[frac] = P.awq_mixed_loss(W[0][li], XC[0][inp], P.awq_channel_mask(idx, k), g=128)
+        torch.cuda.synchronize()
+        lo = losses.cpu().numpy()
+        b = int(best.item())
+        ablation[nm] = {"loss_rtn": float(lo[0]), "loss_awq": float(lo[b]), "alpha": b / n_grid,
+                        "loss_mixed_1pct": float(lm[0.01].item()), "loss_mixed_0.1pct": float(lm[0.001].item())}
+        del ws_a
+    log("built the mixed-precision stack and the layer-0 ablation")
+
     for wb in wbits:                  # eager runs first: the library scratch is allocated
         decode_wbit(wb)
         prefill_wbit(wb, 0)
@@ -416,7 +468,7 @@ def main():
     phases = (["producer"] + [f"decode_g{g}_m{m}" for g, m in decode_cases] + ["decode_fused"] + ["prefill"] +
               [f"big_{big[bi][0]}_m{m}" for bi, m in big_cases] +
               [f"decode_w{wb}_m1" for wb in wbits] + [f"prefill_w{wb}" for wb in wbits] +
-              ["decode_bf16_m1", "prefill_bf16"])
+              ["decode_bf16_m1", "prefill_bf16", "decode_mixed_m1"])
     acc = {p: 0.0 for p in phases}
 
     def step(i, timed):
@@ -446,6 +498,8 @@ def main():
         ev[e0 + 2 * len(wbits)].record(stream)
         prefill_bf16(layer)
         ev[e0 + 2 * len(wbits) + 1].record(stream)
+        graphs["mixed"].replay()
+        ev[e0 + 2 * len(wbits) + 2].record(stream)
         if timed:
             return ev
         return None
@@ -516,6 +570,23 @@ def main():
     t = acc["prefill_bf16"] / K
     rows["prefill_bf16_m2048"] = {"us_per_layer": t * 1e6, "TFLOPs": prefill_flops / t / 1e12,
                                   "frac_mfma_peak": prefill_flops / t / 1e12 / F16_MFMA_PEAK_TFLOPS}
+    t = acc["decode_mixed_m1"] / K
+    cnt_of = {k: int(np.floor(0.01 * k + 0.5)) for nm, n, k in shapes}
+    # 4-bit bytes (keep16 read as inv_s) + protected fp16 columns and indices +
+    # the add pass's read and write of y
+    by_mx = L * sum(gemv_bytes(1, n, k, 128) + 2 * n * cnt_of[k] + 4 * cnt_of[k] + 4 * n for nm, n, k in shapes)
+    rows["decode_mixed_g128_m1"] = {"us_per_stack": t * 1e6, "us_per_linear": t * 1e6 / nlin,
+                                    "GBps": by_mx / t / 1e9, "frac_hbm_peak": by_mx / t / 1e9 / HBM_PEAK_GBS,
+                                    "launches_per_stack": 2 * nlin, "protected_frac": 0.01}
+    tot = {key: sum(v[key] for v in ablation.values()) for key in ("loss_rtn", "loss_awq", "loss_mixed_1pct",
+                                                                  "loss_mixed_0.1pct")}
+    rows["ablation_layer0_m512"] = {
+        "per_linear": {nm: {key: (round(v, 6) if key == "alpha" else float(f"{v:.6g}")) for key, v in d.items()}
+                       for nm, d in ablation.items()},
+        "sum": {key: float(f"{v:.6g}") for key, v in tot.items()},
+        "awq_over_rtn": round(tot["loss_awq"] / tot["loss_rtn"], 4),
+        "mixed_1pct_over_rtn": round(tot["loss_mixed_1pct"] / tot["loss_rtn"], 4),
+        "mixed_0.1pct_over_rtn": round(tot["loss_mixed_0.1pct"] / tot["loss_rtn"], 4)}
     # the two 122 MB shapes (28672<-8192, 8192<-28672) at M = 1 together
     bp = [rows[f"llama3_70b_{nm}_m1"] for nm in ("gate_up", "down")]
     bp_bytes = sum(gemv_bytes(1, r["n"], r["k"], 128) for r in bp)
@@ -546,7 +617,8 @@ def main():
                                "(g128) and M=1/32 (g64) + 7-linear prefill at M=2048 + llama3-70b-"
                                "shaped linears at M=1/16 (cold copies) + the stack at 3 and 8 bits "
                                "(M=1 decode, M=2048 prefill of one layer) + bf16 activations (M=1 "
-                               "decode, M=2048 prefill)",
+                               "decode, M=2048 prefill) + the mixed-precision baseline (M=1 decode; "
+                               "layer-0 loss ablation, untimed)",
                    "layers": L, "linears_per_layer": len(shapes), "m_decode": [1, 8, 32, 128],
                    "m_prefill": 2048, "m_calib": m_cal, "n_grid": n_grid, "group_size": [128, 64]},
         "gemm_tflops_m2048": round(rows["prefill_m2048"]["TFLOPs"], 2),

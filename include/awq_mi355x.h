@@ -179,7 +179,8 @@ awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k,
  *   NaN above +inf.  count = round(frac * k) for a protection ratio frac.
  *   Limits: 0 <= count <= min(k, 1024).
  * awq_channel_mask: keep16[k] (device fp16) = 1.0, and 0.0 on idx[count].
- * awq_gather_channels: w_s[n][count] (device fp16) = w[:, idx] of w[n][k].
+ * awq_gather_channels: w_s[count][n] (device fp16) = w[:, idx] of w[n][k],
+ *   channel-major (w_s[j][r] = w[r][idx[j]]).
  * awq_mixed_loss: *loss (device float64) = sum_{t,n} (sum_k (Wm - W)_nk x_tk)^2
  *   for the mixed weight Wm (RTN with the columns where keep16 = 0 restored
  *   to W): the alpha = 0 loss of awq_search_scale on x with those channels
@@ -188,8 +189,9 @@ awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k,
  *   Limits: those of awq_search_scale.
  * awq_linear_mixed: y[m][n] = x Wm^T: awq_linear_w4a16 with inv_s16 = keep16
  *   (the protected channels leave the quantized product), then
- *   y = fp16_rn(y + sum_j x[:, idx_j] w_s[:, j]) (fp32 accumulation in j
- *   order; the quantized part is rounded to fp16 first).  Within 5e-3 *
+ *   y = fp16_rn(y + sum_j x[:, idx_j] w_s[j, :]) (fp32 accumulation in eight
+ *   interleaved slices of j, added in slice order; the quantized part is
+ *   rounded to fp16 first).  Within 5e-3 *
  *   max(|y_ref|, rms of the row of y_ref) of the float64 value.  qweight,
  *   scales, qzeros: the RTN pack of W (layout v1).  Limits: those of
  *   awq_linear_w4a16; 0 <= count <= min(k, 1024); m <= 1048560.

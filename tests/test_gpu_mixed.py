@@ -84,7 +84,7 @@ def test_mask_and_gather_bit_exact(P):
     want = np.ones(k, np.float16)
     want[idx] = 0
     assert np.array_equal(keep.cpu().numpy().view(np.uint16), want.view(np.uint16))
-    assert np.array_equal(ws.cpu().numpy().view(np.uint16), w[:, idx].view(np.uint16))
+    assert np.array_equal(ws.cpu().numpy().view(np.uint16), np.ascontiguousarray(w[:, idx].T).view(np.uint16))
 
 
 # ----------------------------------------------------------------- loss
@@ -159,6 +159,16 @@ def test_linear_mixed_small(P, m, g):
     idx = O.salient_channels(O.calib_stats(S.activations(64, k, 2643, ch, 30.0)), O.salient_count(k, 0.02))
     _check_mixed_linear(P, w, x, idx, g)
     _check_mixed_linear(P, w, x, np.zeros(0, np.int32), g)
+
+
+def test_linear_mixed_many_protected(P):
+    # 1024 protected channels (the limit): the add pass's LDS takes 92 KiB
+    n, k, g = 130, 4096, 128
+    w = S.weights(n, k, 0.02, 2660)
+    idx = np.sort(np.random.Generator(np.random.PCG64(2661)).choice(k, 1024, replace=False)).astype(np.int32)
+    for m in (1, 20):
+        x = S.activations(m, k, 2662 + m)
+        _check_mixed_linear(P, w, x, idx, g)
 
 
 @pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)

@@ -364,14 +364,14 @@ def awq_channel_mask(idx, k, out=None):
 
 
 def awq_gather_channels(w, idx, out=None):
-    """fp16 [n, count]: the columns idx of w (fp16 [n, k])."""
+    """fp16 [count, n]: the columns idx of w (fp16 [n, k]), channel-major."""
     torch = _torch()
     _dev_tensor(w, torch.float16, "w", 2)
     _dev_tensor(idx, torch.int32, "idx", 1)
     n, k = w.shape
     cnt = idx.shape[0]
-    ws = out if out is not None else torch.empty((n, cnt), dtype=torch.float16, device=w.device)
-    _out_tensor(ws, torch.float16, (n, cnt), "w_s")
+    ws = out if out is not None else torch.empty((cnt, n), dtype=torch.float16, device=w.device)
+    _out_tensor(ws, torch.float16, (cnt, n), "w_s")
     st = _lib.load().awq_gather_channels(_ptr(w), n, k, _ptr(idx) if cnt > 0 else None, cnt,
                                          _ptr(ws) if cnt > 0 else None, _stream())
     _lib.check("awq_gather_channels", st)
@@ -403,7 +403,7 @@ def awq_mixed_loss(w, x, keep16, g=128, workspace=None, out=None):
 
 def awq_linear_mixed(x, qweight, scales, qzeros, keep16, w_s, idx, g=128, out=None):
     """y = x Wm^T (fp16 [m, n]) for the RTN pack of W with the channels idx kept
-    in fp16 (w_s [n, count], keep16 the matching mask)."""
+    in fp16 (w_s [count, n], keep16 the matching mask)."""
     torch = _torch()
     _dev_tensor(x, torch.float16, "x", 2)
     _dev_tensor(qweight, torch.int32, "qweight", 2)
@@ -416,8 +416,8 @@ def awq_linear_mixed(x, qweight, scales, qzeros, keep16, w_s, idx, g=128, out=No
     cnt = idx.shape[0]
     if cnt > 0:
         _dev_tensor(w_s, torch.float16, "w_s", 2)
-        if tuple(w_s.shape) != (n, cnt):
-            raise ValueError("w_s must be [n, count]")
+        if tuple(w_s.shape) != (cnt, n):
+            raise ValueError("w_s must be [count, n]")
     if qweight.shape[1] * 8 != k or keep16.shape[0] != k:
         raise ValueError("packed tensors or keep16 do not match x")
     y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)

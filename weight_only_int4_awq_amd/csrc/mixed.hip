@@ -13,11 +13,13 @@
 //  * channel_keep_kernel / channel_zero_kernel: the fp16 keep mask (1.0, and
 //    0.0 on the protected channels).  As inv_s16 of the 4-bit linear it removes
 //    the protected channels from the quantized product.
-//  * gather_channels_kernel: the protected columns of W, [n][count] fp16.
+//  * gather_channels_kernel: the protected columns of W, channel-major
+//    [count][n] fp16 (a wave's 64 columns of one channel are contiguous).
 //  * mask_rows_kernel: activations with the protected channels set to zero
 //    (the mixed loss is the s = 1 search loss on them).
-//  * salient_add_kernel: y = fp16_rn(y + sum_j x[:, idx_j] W_S[:, j]) after the
-//    quantized product, fp32 accumulation in j order.
+//  * salient_add_kernel: y = fp16_rn(y + sum_j x[:, idx_j] W_S[j, :]) after the
+//    quantized product, fp32 accumulation (eight interleaved slices of j,
+//    added in slice order).
 #include "awq_common.h"
 #include "awq_internal.h"
 
@@ -122,8 +124,8 @@ __global__ __launch_bounds__(256) void gather_channels_kernel(
     int32_t count, uint16_t* __restrict__ w_s) {
   const int64_t total = n * count;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t row = e / count;
-    const int j = (int)(e - row * count);
+    const int j = (int)(e / n);
+    const int64_t row = e - (int64_t)j * n;
     w_s[e] = w[row * k + idx[j]];
   }
 }
@@ -138,40 +140,54 @@ __global__ __launch_bounds__(256) void mask_rows_kernel(const uint16_t* __restri
     out[e] = keep[e % k] == 0 ? (uint16_t)0 : x[e];
 }
 
-// Tiles of 256 columns x kAddTok tokens; the tile's protected activations are
-// staged in LDS as float ([kAddTok][count]); thread = one column, its
-// protected weights read in j order.
+// Tiles of 64 columns x kAddTok tokens, 512 threads: thread (column c =
+// tid % 64, slice q = tid / 64) sums channels j = q, q + 8, ... of the
+// protected set (coalesced loads of w_s[j][col], 8 in flight); the eight
+// slice sums meet in LDS and slice 0 adds them in slice order.  The tile's protected activations
+// are staged in LDS as float [kAddTok][count].
 constexpr int kAddTok = 16;
-constexpr int kAddMaxCount = 1024;
+constexpr int kAddSlices = 8;
 
-__global__ __launch_bounds__(256) void salient_add_kernel(
+__global__ __launch_bounds__(64 * kAddSlices) void salient_add_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ idx, int32_t count,
     const uint16_t* __restrict__ w_s, int64_t m, int64_t n, int64_t k, uint16_t* __restrict__ y) {
   extern __shared__ float xs[];                          // [kAddTok][count]
-  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float part[kAddSlices - 1][kAddTok][64];
+  const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 64 + c;
   const int64_t t0 = (int64_t)blockIdx.y * kAddTok;
   const int tt_n = (m - t0) < kAddTok ? (int)(m - t0) : kAddTok;
-  for (int e = threadIdx.x; e < tt_n * count; e += 256) {
+  for (int e = threadIdx.x; e < tt_n * count; e += 64 * kAddSlices) {
     const int tt = e / count, j = e - tt * count;
     xs[e] = h2f(x[(t0 + tt) * k + idx[j]]);
   }
   __syncthreads();
-  if (col >= n) return;
+  const int64_t cc = col < n ? col : n - 1;
   float acc[kAddTok];
 #pragma unroll
   for (int tt = 0; tt < kAddTok; ++tt) acc[tt] = 0.0f;
-  const uint16_t* __restrict__ wr = w_s + col * count;
-  for (int j = 0; j < count; ++j) {
-    const float wv = h2f(wr[j]);
+#pragma unroll 8
+  for (int j = q; j < count; j += kAddSlices) {
+    const float wv = h2f(w_s[(int64_t)j * n + cc]);
 #pragma unroll
     for (int tt = 0; tt < kAddTok; ++tt)
       if (tt < tt_n) acc[tt] = __builtin_fmaf(xs[tt * count + j], wv, acc[tt]);
   }
+  if (q > 0) {
 #pragma unroll
-  for (int tt = 0; tt < kAddTok; ++tt) {
-    if (tt < tt_n) {
-      uint16_t* yp = y + (t0 + tt) * n + col;
-      *yp = f2h_rn(h2f(*yp) + acc[tt]);
+    for (int tt = 0; tt < kAddTok; ++tt) part[q - 1][tt][c] = acc[tt];
+  }
+  __syncthreads();
+  if (q == 0 && col < n) {
+#pragma unroll
+    for (int tt = 0; tt < kAddTok; ++tt) {
+      if (tt < tt_n) {
+        float v = acc[tt];
+#pragma unroll
+        for (int qq = 0; qq < kAddSlices - 1; ++qq) v += part[qq][tt][c];
+        uint16_t* yp = y + (t0 + tt) * n + col;
+        *yp = f2h_rn(h2f(*yp) + v);
+      }
     }
   }
 }
@@ -221,9 +237,16 @@ hipError_t launch_salient_add(const uint16_t* x, const int32_t* idx, int32_t cou
                               hipStream_t stream) {
   if (count == 0 || m == 0) return hipSuccess;
   const int64_t ty = (m + kAddTok - 1) / kAddTok;
-  const dim3 grid((unsigned)((n + 255) / 256), (unsigned)ty);
+  const dim3 grid((unsigned)((n + 63) / 64), (unsigned)ty);
   const size_t lds = (size_t)kAddTok * count * 4;
-  hipLaunchKernelGGL(salient_add_kernel, grid, dim3(256), lds, stream, x, idx, count, w_s, m, n, k, y);
+  const size_t lds_static = (size_t)(kAddSlices - 1) * kAddTok * 64 * 4;
+  if (lds + lds_static > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&salient_add_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(salient_add_kernel, grid, dim3(64 * kAddSlices), lds, stream, x, idx, count, w_s, m, n,
+                     k, y);
   return hipGetLastError();
 }
 
