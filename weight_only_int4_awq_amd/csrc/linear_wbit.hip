@@ -223,8 +223,17 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
 //    keeps exact counts of the loads in flight instead of waiting for all.
 //  * At a block's end each wave leaves its fp32 partial tile in LDS; after
 //    the last block the partial tiles are summed in wave order.
-constexpr int kWbPF = 4;
-constexpr int kWbMaxBlk = 4;
+#ifndef AWQ_WB_PF
+#define AWQ_WB_PF 2
+#endif
+#ifndef AWQ_WB_MAXBLK
+#define AWQ_WB_MAXBLK 4
+#endif
+#ifndef AWQ_WB_SZPRE
+#define AWQ_WB_SZPRE 2
+#endif
+constexpr int kWbPF = AWQ_WB_PF;
+constexpr int kWbMaxBlk = AWQ_WB_MAXBLK;
 
 // dynamic LDS of the staged decode kernel
 // (x_tilde [m][k] | table [nb][ng][17] words | 16-byte aligned partial tiles [nb][w][64])
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_decode_kernel(
   const uint32_t kc = (uint32_t)(k / 8), xchunks = (uint32_t)m * kc;
   const uint16_t* __restrict__ sbase = has_inv ? inv_s : x;    // a valid address either way
   const int szn = my_blocks * 16 * ng;                         // table entries
-  constexpr int XPRE = 2, SZPRE = 2;
+  constexpr int XPRE = 2, SZPRE = AWQ_WB_SZPRE;
   uint4 xp[XPRE], sp[XPRE];
 #pragma unroll
   for (int i = 0; i < XPRE; ++i) {
