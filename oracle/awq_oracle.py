@@ -299,6 +299,24 @@ def fold_inv_scale(v16: np.ndarray, s16: np.ndarray) -> np.ndarray:
                        np.asarray(s16, np.float16).astype(np.float64))
 
 
+def fold_inv_scale_rows(w16: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """The same fold when the operation producing a linear's input is itself a
+    linear whose output channel j feeds input channel j (in a decoder block
+    the up projection, whose output multiplies the activated gate output and
+    is the down projection's input): row j of its weight [N, K] becomes
+    fp16_rn(W_jk / s_j), each the float64 quotient of two fp16 values rounded
+    once.  The downstream linear then runs with inv_s16 = None.
+
+    Pinned by: s = 1 (identity), s a power of two (exact scaling), the exact
+    rational quotient rounded once for random pairs, and rows equal to
+    fold_inv_scale of each row with its s_j repeated (tests/test_oracle_pins.py).
+    """
+    w = np.asarray(w16, np.float16).astype(np.float64)
+    s = np.asarray(s16, np.float16).astype(np.float64)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        return fp16_rn(w / s[:, None])
+
+
 # ----------------------------------------------------------------------------
 # a5: real quantization and packing (layout v1)  ([csdn] 量化流程优化)
 

@@ -368,6 +368,27 @@ def test_fold_inv_scale_exact_quotient():
         assert float(h) == want or (np.isinf(want) and np.isinf(float(h))), (a, b, float(h), want)
 
 
+def test_fold_inv_scale_rows():
+    r = _rng(97)
+    w = (r.standard_normal((40, 24)) * 10.0 ** r.integers(-3, 2, (40, 24))).astype(np.float16)
+    s = O.scale_candidate(np.abs(r.standard_normal(40)) * 10.0 ** r.integers(-2, 3, 40), 0.6)
+    got = O.fold_inv_scale_rows(w, s)
+    # identity and exact power-of-two scaling
+    assert np.array_equal(O.fold_inv_scale_rows(w, np.ones(40, np.float16)).view(np.uint16), w.view(np.uint16))
+    p2 = np.full(40, 0.25, np.float16)
+    assert np.array_equal(O.fold_inv_scale_rows(w, p2).view(np.uint16),
+                          O.fp16_rn(w.astype(np.float64) * 4.0).view(np.uint16))
+    # every element the exact rational quotient rounded once
+    for j in range(0, 40, 7):
+        for c in range(24):
+            want = X.f16_round_exact(X.frac_of_f16(w[j, c]) / X.frac_of_f16(s[j]))
+            assert float(got[j, c]) == want or (np.isinf(want) and np.isinf(float(got[j, c])))
+    # row j is the per-channel fold of that row with s_j repeated
+    for j in range(40):
+        assert np.array_equal(got[j].view(np.uint16),
+                              O.fold_inv_scale(w[j], np.full(24, s[j], np.float16)).view(np.uint16))
+
+
 def test_joint_loss_is_sum_of_stacked_projections():
     # q, k, v read one input: with one s for all three, the loss of their
     # stacked weights is the sum of their own losses, for every alpha
