@@ -11,8 +11,9 @@ One step is one pass of the whole path over one batch of synthetic input:
             down; 128 calls, replayed as one HIP graph each) at M = 1, 8, 32
             and 128 tokens with g = 128, and at M = 1 and 32 with g = 64;
   shared s  the same stack at M = 1 with one s for q/k/v and one for gate/up
-            (searched on their weights stacked along N), each pair packed and
-            run as one linear on activations that already carry 1/s;
+            (searched on their weights stacked along N), each packed and run
+            as one linear on activations that already carry 1/s, and down's
+            s folded into the rows of up (down also runs without 1/s);
   prefill   the 7 linears of layer L at M = 2048 tokens (GEMM), grouped as
             in the decode (4 calls, each one activation-prep launch and one
             GEMM launch over the tiles of its linears);
@@ -230,39 +231,51 @@ def main():
     # the stack with one shared s for q/k/v and one for gate/up (searched on
     # their weights stacked along N, 128 calibration tokens), packed as one
     # linear each and run on activations that already carry 1/s (folded into
-    # the producing operation's weight): inv_s16 absent for those two
-    fused = []
-    for layer in range(L):
-        row = []
-        for grp_names in (("q", "k", "v"), ("gate", "up")):
-            idx = [li for li, (nm, n, k) in enumerate(shapes) if nm in grp_names]
-            wst = torch.cat([W[layer][li] for li in idx], 0)
-            inp = S.INPUT_OF[grp_names[0]]
-            xc = XC[layer][inp][:128].contiguous()
-            ws = torch.empty(P.awq_search_workspace_size(wst.shape[0], wst.shape[1], 128, 128, n_grid),
-                             dtype=torch.uint8, device=dev)
-            _, s16f, _, _ = P.awq_search_scale(wst, xc, P.awq_calib_stats(xc), g=128, n_grid=n_grid,
-                                               workspace=ws)
-            qwf, scf, qzf, _ = P.awq_pack_int4(wst, s16f, g=128)
-            row.append((inp, qwf, scf, qzf))
-            del wst, ws
-        fused.append(row)
-    torch.cuda.synchronize()
-    YF = [[torch.empty((1, 6144), dtype=torch.float16, device=dev),
-           torch.empty((1, 28672), dtype=torch.float16, device=dev)] for _ in range(L)]
+    # the producing operation's weight): inv_s16 absent for those two.  The
+    # down projection's s is searched first and folded into the rows of the up
+    # projection (awq_fold_inv_scale_rows) before the gate/up search, so down
+    # runs without inv_s16 too; o keeps its inv_s16 (v's outputs feed several
+    # of o's input channels under grouped-query attention)
+    def shared_search(wst, xc):
+        ws = torch.empty(P.awq_search_workspace_size(wst.shape[0], wst.shape[1], 128, 128, n_grid),
+                         dtype=torch.uint8, device=dev)
+        return P.awq_search_scale(wst, xc, P.awq_calib_stats(xc), g=128, n_grid=n_grid, workspace=ws)[1]
+
     li_o = [li for li, (nm, n, k) in enumerate(shapes) if nm == "o"][0]
     li_d = [li for li, (nm, n, k) in enumerate(shapes) if nm == "down"][0]
+    li_u = [li for li, (nm, n, k) in enumerate(shapes) if nm == "up"][0]
+    fused = []
+    for layer in range(L):
+        xd = XC[layer][S.INPUT_OF["down"]][:128].contiguous()
+        s16d = shared_search(W[layer][li_d], xd)
+        w_up_f = P.awq_fold_inv_scale_rows(W[layer][li_u], s16d)
+        row = []
+        for grp_names in (("q", "k", "v"), ("gate", "up")):
+            wst = torch.cat([w_up_f if li == li_u else W[layer][li]
+                             for li, (nm, n, k) in enumerate(shapes) if nm in grp_names], 0)
+            inp = S.INPUT_OF[grp_names[0]]
+            s16f = shared_search(wst, XC[layer][inp][:128].contiguous())
+            qwf, scf, qzf, _ = P.awq_pack_int4(wst, s16f, g=128)
+            row.append((inp, qwf, scf, qzf))
+            del wst
+        qwd, scd, qzd, _ = P.awq_pack_int4(W[layer][li_d], s16d, g=128)
+        row.append((S.INPUT_OF["down"], qwd, scd, qzd))
+        fused.append(row)
+        del w_up_f
+    torch.cuda.synchronize()
+    YF = [[torch.empty((1, 6144), dtype=torch.float16, device=dev),
+           torch.empty((1, 28672), dtype=torch.float16, device=dev),
+           YR[1][layer][li_d]] for layer in range(L)]
 
     def decode_fused():
         st = stacks[128]
         for layer in range(L):
             for fi, (inp, qwf, scf, qzf) in enumerate(fused[layer]):
                 P.awq_linear_w4a16(XR[1][layer][inp], qwf, scf, qzf, None, g=128, out=YF[layer][fi])
-                li = li_o if fi == 0 else li_d
-                nm = shapes[li][0]
-                qw, sc, qz, _ = st[layer][li]
-                P.awq_linear_w4a16(XR[1][layer][S.INPUT_OF[nm]], qw, sc, qz, st[layer][li + len(shapes)][2],
-                                   g=128, out=YR[1][layer][li])
+                if fi == 0:
+                    qw, sc, qz, _ = st[layer][li_o]
+                    P.awq_linear_w4a16(XR[1][layer][S.INPUT_OF["o"]], qw, sc, qz,
+                                       st[layer][li_o + len(shapes)][2], g=128, out=YR[1][layer][li_o])
 
     decode_cases = [(128, 1), (128, 8), (128, 32), (128, 128), (64, 1), (64, 32)]
     for g, m in decode_cases:        # eager run first: allocates the library scratch
@@ -534,7 +547,7 @@ def main():
                                      "frac_hbm_peak": bytes_by[(g, m)] / t / 1e9 / HBM_PEAK_GBS}
     t_f = acc["decode_fused"] / K
     by_f = L * (gemv_bytes(1, 6144, 4096, 128, inv=False) + gemv_bytes(1, 28672, 4096, 128, inv=False)
-                + gemv_bytes(1, 4096, 4096, 128) + gemv_bytes(1, 4096, 14336, 128))
+                + gemv_bytes(1, 4096, 4096, 128) + gemv_bytes(1, 4096, 14336, 128, inv=False))
     rows["decode_shared_s_g128_m1"] = {"us_per_stack": t_f * 1e6, "GBps": by_f / t_f / 1e9,
                                        "frac_hbm_peak": by_f / t_f / 1e9 / HBM_PEAK_GBS,
                                        "launches_per_stack": 4 * L}

@@ -164,6 +164,25 @@ awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k,
                               uint16_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_fold_inv_scale_rows -- the fold of awq_fold_inv_scale when the input of
+ * the linear is produced by another linear whose output channel j is its
+ * input channel j (in a decoder block the up projection, whose output,
+ * multiplied by the activated gate output, is the down projection's input):
+ * row j of that linear's fp16 weight is divided by s_j.
+ * Passage: as awq_fold_inv_scale.  The producing linear is then searched and
+ * packed from the folded weight, and the consuming linear runs with
+ * inv_s16 = NULL.  (Under grouped-query attention an output channel of the v
+ * projection feeds several channels of the o projection's input, which would
+ * need equal s on them; that fold is not offered.)
+ *
+ *   out[j][c] = fp16_rn(w[j][c] / s16[j]): the exact quotient rounded once.
+ *   w, out [n][k] fp16 (device; out may alias w); s16 [n] fp16 (device).
+ *   Errors: NULL pointers, n < 1 or k < 1, pointers not 2-byte aligned.
+ * ------------------------------------------------------------------------- */
+awq_status awq_fold_inv_scale_rows(const uint16_t* w, const uint16_t* s16, int64_t n,
+                                   int64_t k, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Mixed-precision baseline: awq_salient_channels, awq_channel_mask,
  * awq_gather_channels, awq_mixed_loss, awq_linear_mixed.
  * Passage: jsqmd.com page, section 二.1 (1) (a small share, 0.1 - 1 %, of the

@@ -37,7 +37,7 @@ def test_header_declares_the_path():
                  "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
                  "awq_salient_channels", "awq_channel_mask", "awq_gather_channels",
                  "awq_mixed_loss_workspace_size", "awq_mixed_loss", "awq_linear_mixed",
-                 "awq_last_error", "awq_abi_version"):
+                 "awq_fold_inv_scale_rows", "awq_last_error", "awq_abi_version"):
         assert want in names, names
 
 
@@ -107,6 +107,14 @@ def test_fold_argument_errors(lib):
     assert _status(lib, "awq_fold_inv_scale", FAKE, FAKE, 16, None, None)[0] == 1
     assert _status(lib, "awq_fold_inv_scale", FAKE, FAKE, 0, FAKE, None)[0] == 2
     st, msg = _status(lib, "awq_fold_inv_scale", FAKE + 1, FAKE, 16, FAKE, None)
+    assert st == 3 and "aligned" in msg
+
+
+def test_fold_rows_argument_errors(lib):
+    assert _status(lib, "awq_fold_inv_scale_rows", None, FAKE, 4, 16, FAKE, None)[0] == 1
+    assert _status(lib, "awq_fold_inv_scale_rows", FAKE, FAKE, 0, 16, FAKE, None)[0] == 2
+    assert _status(lib, "awq_fold_inv_scale_rows", FAKE, FAKE, 4, 0, FAKE, None)[0] == 2
+    st, msg = _status(lib, "awq_fold_inv_scale_rows", FAKE, FAKE + 1, 4, 16, FAKE, None)
     assert st == 3 and "aligned" in msg
 
 

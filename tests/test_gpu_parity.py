@@ -572,3 +572,41 @@ def test_shared_scale_stacked_qkv_full_size(P):
     # the packed rows of the stack are the oracle's pack at the shared s
     oq, osc, oz = O.pack_int4(wst[rows[::8]], s16h, 128)[:3]
     assert np.array_equal(host_u32(qw[torch.from_numpy(rows[::8]).to(DEV)]), oq)
+
+
+def test_fold_inv_scale_rows_bit_exact(P):
+    r = np.random.Generator(np.random.PCG64(810))
+    n, k = 37, 1031
+    w = (r.standard_normal((n, k)) * 10.0 ** r.integers(-5, 4, (n, k))).astype(np.float16)
+    w[0, :5] = np.array([0.0, -0.0, 65504.0, 6e-8, -3e-5], np.float16)
+    s16 = O.scale_candidate(np.abs(r.standard_normal(n)) * 10.0 ** r.integers(-4, 4, n), 0.8)
+    s16[:3] = np.array([2.0 ** -14, 1.0, 300.0], np.float16)
+    want = O.fold_inv_scale_rows(w, s16)
+    wd, sd = dev(w), dev(s16)
+    got = P.awq_fold_inv_scale_rows(wd, sd)
+    P.awq_fold_inv_scale_rows(wd, sd, out=wd)          # in place
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    assert np.array_equal(wd.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+def test_fold_rows_up_for_down_full_size(P):
+    # the down projection's s (its input has 14336 channels) folded into the
+    # rows of the Llama-3-8B up projection (14336 x 4096): bit-exact on every
+    # element, and the folded up projection's pack is the oracle's pack of the
+    # folded weight on sampled rows
+    _, x_cal, _, _ = S.config_layer(2, "down", 4096, 14336, 128, 0, 0.02, 0.01, 20.0)
+    w_up = S.config_layer(2, "up", 14336, 4096, 8, 0, 0.02, 0.01, 20.0)[0]
+    s16 = O.scale_candidate(O.calib_stats(x_cal), 0.45)
+    got = P.awq_fold_inv_scale_rows(dev(w_up), dev(s16))
+    torch.cuda.synchronize()
+    want = O.fold_inv_scale_rows(w_up, s16)
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    qw, sc, qz, _ = P.awq_pack_int4(got, None, g=128)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.Generator(np.random.PCG64(811)).choice(14336, 64, replace=False))
+    ri = torch.from_numpy(rows).to(DEV)
+    oq, osc, oz = O.pack_int4(want[rows], None, 128)[:3]
+    assert np.array_equal(host_u32(qw[ri]), oq)
+    assert np.array_equal(sc[ri].cpu().numpy().view(np.uint16), osc.view(np.uint16))
+    assert np.array_equal(host_u32(qz[ri]), oz)

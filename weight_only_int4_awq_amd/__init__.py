@@ -22,7 +22,7 @@ __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "
            "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit", "packed_shapes",
            "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
            "awq_salient_channels", "awq_channel_mask", "awq_gather_channels", "awq_mixed_loss",
-           "awq_linear_mixed",
+           "awq_linear_mixed", "awq_fold_inv_scale_rows",
            "AWQError", "load"]
 
 
@@ -148,6 +148,23 @@ def awq_fold_inv_scale(v, s16, out=None):
     st = _lib.load().awq_fold_inv_scale(_ptr(v), _ptr(s16), k, _ptr(out), _stream())
     _lib.check("awq_fold_inv_scale", st)
     return out
+
+
+def awq_fold_inv_scale_rows(w, s16, out=None):
+    """fp16_rn(w[j, :] / s16[j]) (w fp16 [n, k], s16 fp16 [n]): the weight of the
+    linear producing another linear's input with that linear's 1/s folded
+    into its output rows.  Returns the fp16 [n, k] tensor."""
+    torch = _torch()
+    _dev_tensor(w, torch.float16, "w", 2)
+    _dev_tensor(s16, torch.float16, "s16", 1)
+    n, k = w.shape
+    if s16.shape[0] != n:
+        raise ValueError("s16 must have one entry per row of w")
+    o = out if out is not None else torch.empty((n, k), dtype=torch.float16, device=w.device)
+    _out_tensor(o, torch.float16, (n, k), "out")
+    st = _lib.load().awq_fold_inv_scale_rows(_ptr(w), _ptr(s16), n, k, _ptr(o), _stream())
+    _lib.check("awq_fold_inv_scale_rows", st)
+    return o
 
 
 def awq_pack_int4(w, s16=None, g=128, out=None):

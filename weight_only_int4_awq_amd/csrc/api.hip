@@ -167,6 +167,18 @@ awq_status awq_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n, int6
                    nonfinite_groups, stream);
 }
 
+awq_status awq_fold_inv_scale_rows(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
+                                   uint16_t* out, void* stream) {
+  g_err[0] = 0;
+  if (!w || !s16 || !out) return fail(AWQ_ERR_NULL, "awq_fold_inv_scale_rows: null pointer");
+  if (n < 1 || k < 1) return fail(AWQ_ERR_SHAPE, "awq_fold_inv_scale_rows: n=%lld, k=%lld must be >= 1", n, k);
+  if (!aligned(w, 2) || !aligned(s16, 2) || !aligned(out, 2))
+    return fail(AWQ_ERR_ALIGN, "awq_fold_inv_scale_rows: misaligned pointer");
+  hipError_t e = awq::launch_fold_inv_scale_rows(w, s16, n, k, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "awq_fold_inv_scale_rows launch");
+  return AWQ_OK;
+}
+
 awq_status awq_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
                               void* stream) {
   g_err[0] = 0;

@@ -27,6 +27,8 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
                          int32_t w_bit, int32_t* best_idx, uint16_t* s16, uint16_t* inv_s16,
                          double* losses, void* workspace, hipStream_t stream);
 
+hipError_t launch_fold_inv_scale_rows(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
+                                      uint16_t* out, hipStream_t stream);
 hipError_t launch_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
                                  hipStream_t stream);
 

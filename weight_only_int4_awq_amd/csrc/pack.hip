@@ -253,6 +253,26 @@ __global__ __launch_bounds__(256) void fold_inv_scale_kernel(const uint16_t* __r
     out[i] = f64_to_f16_rn((double)h2f(v[i]) / (double)h2f(s16[i]));
 }
 
+// the same fold into the output rows of a linear [n][k] that produces the
+// input: out_jc = fp16_rn(w_jc / s_j)
+__global__ __launch_bounds__(256) void fold_inv_scale_rows_kernel(const uint16_t* __restrict__ w,
+                                                                  const uint16_t* __restrict__ s16,
+                                                                  int64_t n, int64_t k,
+                                                                  uint16_t* __restrict__ out) {
+  const int64_t total = n * k;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
+    out[e] = f64_to_f16_rn((double)h2f(w[e]) / (double)h2f(s16[e / k]));
+}
+
+hipError_t launch_fold_inv_scale_rows(const uint16_t* w, const uint16_t* s16, int64_t n, int64_t k,
+                                      uint16_t* out, hipStream_t stream) {
+  const int64_t total = n * k;
+  const int64_t blocks = (total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096;
+  hipLaunchKernelGGL(fold_inv_scale_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, s16, n,
+                     k, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fold_inv_scale(const uint16_t* v, const uint16_t* s16, int64_t k, uint16_t* out,
                                  hipStream_t stream) {
   const int64_t blocks = (k + 255) / 256 < 1024 ? (k + 255) / 256 : 1024;
