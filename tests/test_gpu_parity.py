@@ -269,8 +269,10 @@ def test_linear_ragged(P, n, k):
 
 
 @pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 8, 24])
 def test_linear_decode_full_size(P, name, n, k, m):
+    # m = 24: the fused two-chunk kernel for q, k, v and o, the grouped GEMM
+    # (64-row tiles, split along K) for gate, up and down
     w, x_cal, x_run, _ = S.config_layer(2, name, n, k, 128, m, 0.02, 0.01, 20.0)
     s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
     _check_linear(P, w, x_run, s16, 128)
@@ -289,7 +291,7 @@ def test_linear_70b_shapes_sampled(P, name, n, k):
     w = S.weights(n, k, 0.015, S.seed_of(4, 0, S.SLOTS[name], 0))
     ch = S.outlier_channels(k, 0.005, S.seed_of(4, 0, S.SLOTS[name], 3))
     cols = np.sort(np.random.Generator(np.random.PCG64(n + 2)).choice(n, 256, replace=False))
-    for m in (1, 16):
+    for m in (1, 16, 24):
         x = S.activations(m, k, S.seed_of(4, 0, S.SLOTS[name], 2), ch, 30.0)
         _check_linear(P, w, x, None, 128, cols=cols)
 
@@ -476,7 +478,8 @@ def _check_group(P, items, meta, k, g, cols_per=None):
 @pytest.mark.parametrize("m", [1, 8, 24, 40, 300])
 @pytest.mark.parametrize("g", [128, 64])
 def test_linear_group_matches_single_and_oracle(P, m, g):
-    # m = 1 and 8: one grouped decode launch; m = 24: one launch per linear;
+    # m = 1, 8 and 24: one grouped decode launch (at 24 the fused kernel with
+    # two token chunks);
     # m = 40 and 300 (two row tiles, the second ragged): one activation-prep
     # launch and one GEMM launch over the tiles of every linear
     specs = [(1000, 0.5, 460), (256, 0.3, 470), (264, None, 480), (16, 0.4, 490)]
@@ -499,8 +502,8 @@ def test_linear_group_llama3_8b_full_size_sampled(P, m):
 def test_linear_group_mixed_plan(P, m):
     # m = 8: the group takes two column blocks per work-group (group-major
     # kernel), the small linears alone take one (block-major kernel); above 16
-    # tokens a group of more than 16 MiB of packed weights runs linear by
-    # linear, and the small linear in it still takes its own (fused) plan
+    # tokens the linear of more than 16 MiB of packed weights runs the grouped
+    # GEMM and the small linears each take their own (fused) plan
     specs = [(14336, 0.5, 570), (1024, 0.4, 580), (264, None, 590)]
     items, meta = _group_case(P, m, 4096, 128, specs, 600 + m)
     _check_group(P, items, meta, 4096, 128, cols_per=128)

@@ -2059,7 +2059,7 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
 // than 16 MiB of packed weights) and that is wide (at least 12288 columns)
 // takes the GEMM.  A property of the linear alone, as every plan choice.
 static bool skinny_wide(const LinItem& it, int64_t m, int64_t k) {
-  return m > 16 && m <= 32 && it.n >= 12288 && it.n * k / 2 > ((int64_t)16 << 20);
+  return m > 16 && m <= 32 && it.n * k / 2 > ((int64_t)16 << 20);
 }
 
 // The prefill GEMM of a group (m > 32): x_tilde of every linear into a
@@ -2288,10 +2288,11 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
       return hipGetLastError();
     }
   }
-  // 17 <= m <= 32: wide linears that do not take the fused kernel run as one
-  // grouped GEMM launch (64-row tiles, split along K), which streams their
-  // weights faster than the staged skinny pair (measured: gate/up 67 -> 40 us,
-  // 70B-shaped gate/up 93 -> 70 us at 32 tokens); the others as calls alone
+  // 17 <= m <= 32: linears of more than 16 MiB of packed weights that do not
+  // take the fused kernel run as one grouped GEMM launch (64-row tiles, split
+  // along K), which streams their weights faster than the staged skinny pair
+  // (measured at 32 tokens: gate/up 67 -> 37 us, down 34 -> 30 us, 70B-shaped
+  // gate/up 93 -> 62 us, down 97 -> 80 us); the others as calls alone
   if (m > 16 && m <= 32) {
     LinItem wide[kGroupMax], rest[kGroupMax];
     int nw = 0, nr = 0;
