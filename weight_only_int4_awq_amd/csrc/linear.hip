@@ -1536,7 +1536,12 @@ static int64_t gemm_row_chunk(int64_t k) {
 static int gemm_bm(int64_t m) { return m <= AWQ_GEMM_SMALL_M ? 64 : kGemmBM; }
 
 // Slices of K per tile for a linear whose tiles alone leave CUs idle: enough
-// slices for one work-group per CU, at least two K-steps each, at most 16.
+// slices for one work-group per CU (two for 64-row tiles where K >= 8192: a
+// long tile K loop runs one K-step ahead and stalls on its loads, and a
+// second resident work-group per CU hides that; measured at 24-128 tokens,
+// down 30 -> 25.5 us, 70B-shaped down 79 -> 58 us, while at K = 4096 and with
+// 256-row tiles the extra partial tiles cost more), at least two K-steps
+// each, at most 16.
 // With 64-row tiles (m <= 128) whenever the linear has fewer tiles than CUs;
 // with 256-row tiles up to 512 tokens and 64 tiles, or 128 tiles where K >=
 // 8192 makes a tile's K loop long (beyond that the partial tiles' round trip
@@ -1549,7 +1554,8 @@ static int gemm_split_occupancy(int64_t m, int64_t n, int64_t k) {
   if (m > gemm_row_chunk(k) || tiles >= AWQ_GEMM_SPLIT_TARGET) return 1;
   if (bm != 64 && (m > 512 || tiles > 128 || (tiles > 64 && k < 8192))) return 1;
   const int64_t nk = k / kGemmBK;
-  int64_t sk = (AWQ_GEMM_SPLIT_TARGET + tiles - 1) / tiles;
+  const int64_t target = (bm == 64 && k >= 8192) ? 2 * AWQ_GEMM_SPLIT_TARGET : AWQ_GEMM_SPLIT_TARGET;
+  int64_t sk = (target + tiles - 1) / tiles;
   const int64_t smax = nk / 2 < 16 ? nk / 2 : 16;
   sk = sk < smax ? sk : smax;
   return sk > 1 ? (int)sk : 1;
