@@ -46,9 +46,43 @@ __device__ __forceinline__ void wb_run_codes(const uint32_t (&cw)[NW], int i, ui
       const uint64_t v = ((uint64_t)cw[0] | ((uint64_t)cw[1] << 32)) >> (sh + 24u * (uint32_t)i);
       c24 = (uint32_t)v & 0xFFFFFFu;
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      hq[e] = ((c24 >> (6 * e)) & 7u) | (((c24 >> (6 * e + 3)) & 7u) << 16) | 0x64006400u;
+    // codes e (bits 3e .. 3e+2 of c24) in the pair order (e0, e4), (e1, e5),
+    // (e2, e6), (e3, e7): the two codes of a pair lie 12 bits apart, so one
+    // shift places both inside the mantissas of the two halves, at bit a of
+    // the low and b of the high half; a half whose exponent is 2^(10 - a)
+    // then holds 2^(10 - a) + q exactly (a, b = 4/0, 7/3, 6/2, 4/0)
+    const uint32_t x4 = c24 << 4, x5 = c24 >> 5;
+    hq[0] = (x4 & 0x00070070u) | 0x64005400u;       // 64 + e0, 1024 + e4
+    hq[1] = (x4 & 0x00380380u) | 0x58004800u;       // 8 + e1, 128 + e5
+    hq[2] = (c24 & 0x001C01C0u) | 0x5C004C00u;      // 16 + e2, 256 + e6
+    hq[3] = (x5 & 0x00070070u) | 0x64005400u;       // 64 + e3, 1024 + e7
+  }
+}
+
+// The offsets that turn the halves of wb_run_codes into q - z, from
+// oz = (-1024 - z, -1024 - z): at 8 bits every pair is 1024 + q; at 3 bits
+// the bases of the pairs above (every sum exact in fp16)
+template <int BITS>
+__device__ __forceinline__ void wb_offsets(half2_t oz, half2_t (&o)[4]) {
+  if constexpr (BITS == 8) {
+    o[0] = oz; o[1] = oz; o[2] = oz; o[3] = oz;
+  } else {
+    o[0] = oz + half2_t{(half_t)960.0f, (half_t)0.0f};
+    o[1] = oz + half2_t{(half_t)1016.0f, (half_t)896.0f};
+    o[2] = oz + half2_t{(half_t)1008.0f, (half_t)768.0f};
+    o[3] = o[0];
+  }
+}
+
+// 8 activation channels (k0 .. k7, two per word) into the 3-bit pair order
+// (k0, k4), (k1, k5), (k2, k6), (k3, k7); the 8-bit order is the natural one
+template <int BITS>
+__device__ __forceinline__ uint4 wb_act_order(uint4 v) {
+  if constexpr (BITS == 8) {
+    return v;
+  } else {
+    return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                      __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
   }
 }
 
@@ -123,11 +157,14 @@ struct WbLane {
 // (grid y strides over the chunks); the waves split the groups of K into W
 // contiguous ranges.  Sub-step i < G/32 of a group is one
 // v_mfma_f32_16x16x32_f16 whose k-block of lane c is its i-th run of 8
-// channels; A (x_tilde of token t0 + r) and B follow the same order, so every
-// channel meets its weight once.  Weights become fp16_rn((q - z) D): the
-// codes sit in the mantissa of 1024, 1024 + z is subtracted exactly, and the
-// product with D rounds once.  Activations become fp16_rn(x inv_s).  The
-// waves' fp32 partial tiles are summed in wave order through LDS.
+// channels (at 3 bits in the pair order (k0, k4), (k1, k5), (k2, k6), (k3, k7)
+// of the code extraction); A (x_tilde of token t0 + r) and B follow the same
+// order, so every channel meets its weight once.  Weights become
+// fp16_rn((q - z) D): the codes sit in the mantissa of a power of two
+// (1024 at 8 bits, 8 .. 1024 by position at 3 bits), base + z is subtracted
+// exactly, and the product with D rounds once.  Activations become
+// fp16_rn(x inv_s).  The waves' fp32 partial tiles are summed in wave order
+// through LDS.
 template <int G, int BITS, int W>
 __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
@@ -165,6 +202,8 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
       const uint32_t db = srow[j];
       const half2_t dd = __builtin_bit_cast(half2_t, db | (db << 16));
       const half2_t oz = {(half_t)(-1024.0f - z), (half_t)(-1024.0f - z)};
+      half2_t oe[4];
+      wb_offsets<BITS>(oz, oe);
 #pragma unroll
       for (int i = 0; i < SUB; ++i) {
         const int64_t kb = (int64_t)j * G + lg.chan(i);
@@ -173,7 +212,7 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
         uint32_t bw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          bw[e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, hq[e]) + oz) * dd);
+          bw[e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, hq[e]) + oe[e]) * dd);
         const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
         const uint4 xv = tok_ok ? *reinterpret_cast<const uint4*>(xrow + kb)
                                 : make_uint4(0u, 0u, 0u, 0u);
@@ -185,7 +224,8 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
         for (int e = 0; e < 4; ++e)
           aw[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xw[e]) *
                                                    __builtin_bit_cast(half2_t, sw[e]));
-        const half8_t aop = __builtin_bit_cast(half8_t, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+        const half8_t aop =
+            __builtin_bit_cast(half8_t, wb_act_order<BITS>(make_uint4(aw[0], aw[1], aw[2], aw[3])));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc, 0, 0, 0);
       }
     }
@@ -212,9 +252,9 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
 // 16-column blocks b, b + grid, ... (at most kWbMaxBlk).
 //  * Prologue: the staging loads (x, inv_s, scales, zeros: cache-resident and
 //    shared by all work-groups) are issued first, then the first kWbPF weight
-//    loads of every wave; x_tilde = fp16_rn(x inv_s) of all m tokens and the
-//    blocks' (D, -1024 - z) pairs go to LDS, so weights are the only global
-//    loads of the main loop.
+//    loads of every wave; x_tilde = fp16_rn(x inv_s) of all m tokens (each
+//    8-channel run in the code order) and the blocks' (D, -1024 - z) pairs
+//    go to LDS, so weights are the only global loads of the main loop.
 //  * Main loop: each wave owns a contiguous range of groups along K and walks
 //    the sequence (block, group) with its weight loads in two halves of kWbPF
 //    items, one in flight while the other is multiplied, across block
@@ -232,7 +272,13 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
 #ifndef AWQ_WB_SZPRE
 #define AWQ_WB_SZPRE 2
 #endif
-constexpr int kWbPF = AWQ_WB_PF;
+#ifndef AWQ_WB_PF3
+#define AWQ_WB_PF3 2
+#endif
+// items per prefetch half: a 3-bit item is 768 bytes per wave (at g = 128),
+// an 8-bit one 2 KiB
+template <int BITS>
+constexpr int wb_pf() { return BITS == 3 ? AWQ_WB_PF3 : AWQ_WB_PF; }
 constexpr int kWbMaxBlk = AWQ_WB_MAXBLK;
 
 // dynamic LDS of the staged decode kernel
@@ -308,6 +354,7 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_decode_kernel(
   }
 
   // ---- 2. the first half of the weight loads
+  constexpr int kWbPF = wb_pf<BITS>();
   uint32_t wq[2 * kWbPF][NW];
   int i_blk = 0, i_j = jb, i_left = total;    // issue cursor (wave-uniform)
   auto issue = [&](int slot) {
@@ -333,7 +380,7 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_decode_kernel(
     v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
     v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
     v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.w) * __builtin_bit_cast(half2_t, sv.w));
-    *reinterpret_cast<uint4*>(xs_l + (size_t)q * 8) = v;
+    *reinterpret_cast<uint4*>(xs_l + (size_t)q * 8) = wb_act_order<BITS>(v);
   };
   auto stage_sz = [&](int q, uint32_t d, uint32_t zw) {
     const int bi = q / (16 * ng), rest = q - bi * 16 * ng;
@@ -376,6 +423,8 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_decode_kernel(
       const uint32_t dl = t & 0xFFFFu, zl = t >> 16;
       const half2_t dd = __builtin_bit_cast(half2_t, dl | (dl << 16));
       const half2_t oz = __builtin_bit_cast(half2_t, zl | (zl << 16));
+      half2_t oe[4];
+      wb_offsets<BITS>(oz, oe);
 #pragma unroll
       for (int i = 0; i < SUB; ++i) {
         uint32_t hq[4];
@@ -383,7 +432,7 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_decode_kernel(
         uint32_t bw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          bw[e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, hq[e]) + oz) * dd);
+          bw[e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, hq[e]) + oe[e]) * dd);
         const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
         const half8_t aop = tok_ok ? *reinterpret_cast<const half8_t*>(xa + j * G + lg.chan(i))
                                    : half8_t{};
