@@ -434,8 +434,8 @@ __global__ __launch_bounds__(W * 64) void linear_wbit_decode_kernel(
         for (int e = 0; e < 4; ++e)
           bw[e] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2_t, hq[e]) + oe[e]) * dd);
         const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
-        const half8_t aop = tok_ok ? *reinterpret_cast<const half8_t*>(xa + j * G + lg.chan(i))
-                                   : half8_t{};
+        // rows r >= m read token 0: they only reach output rows that are not stored
+        const half8_t aop = *reinterpret_cast<const half8_t*>(xa + j * G + lg.chan(i));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, acc, 0, 0, 0);
       }
       --c_left;
