@@ -839,7 +839,9 @@ static int wbit_split(int64_t m, int64_t n, int64_t k, int32_t g) {
   if (m > 512 || tiles > 128 || m > wbit_row_chunk(k)) return 1;
   const int64_t unit = g / kWbBK > 1 ? g / kWbBK : 1;
   const int64_t nu = k / kWbBK / unit;
-  int64_t sk = (256 + tiles - 1) / tiles;
+  // two work-groups per CU for 64-row tiles with a long K loop (as the 4-bit GEMM)
+  const int64_t target = (bm == 64 && k >= 8192) ? 512 : 256;
+  int64_t sk = (target + tiles - 1) / tiles;
   const int64_t smax = nu / 2 < 16 ? nu / 2 : 16;
   sk = sk < smax ? sk : smax;
   return sk > 1 ? (int)sk : 1;
