@@ -280,9 +280,9 @@ awq_status awq_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n,
  *
  *   y[t][n] = fp16_rn( sum_k x_tilde_tk (q_nk - z_nj) D_nj ), as
  *   awq_linear_w4a16, within the same 5e-3 bound.  w_bit = 4 runs
- *   awq_linear_w4a16 (and takes its limits).  w_bit 3 and 8: up to 32
+ *   awq_linear_w4a16 (and takes its limits).  w_bit 3 and 8: up to 16
  *   tokens one MFMA kernel that streams the weights per 16-token chunk; from
- *   33 tokens a tiled GEMM (x * inv_s16 is first staged in the library's
+ *   17 tokens a tiled GEMM (x * inv_s16 is first staged in the library's
  *   per-device scratch buffer, as for awq_linear_w4a16; calls that overlap on
  *   one device from different host threads must be serialised).
  *   x [m][k] fp16, qweight and inv_s16 [k] fp16 (or NULL) 16-byte aligned;

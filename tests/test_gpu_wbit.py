@@ -222,7 +222,7 @@ def _check_linear(P, w, x, s16, g, w_bit, cols=None):
 
 @pytest.mark.parametrize("w_bit", [3, 8])
 @pytest.mark.parametrize("g", [32, 64, 128])
-@pytest.mark.parametrize("m", [1, 5, 16, 17, 33, 300])
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 33, 300])
 def test_linear_wbit_small(P, w_bit, g, m):
     n, k = 50, 640
     w = S.weights(n, k, 0.02, 1400 + m)
