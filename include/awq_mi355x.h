@@ -36,7 +36,16 @@
  *     fixed order.
  *   - Outputs must not alias inputs.
  *   - Non-finite data cannot be seen on the host without a synchronisation;
- *     it is reported through device-side values as stated per entry point.
+ *     it is reported through device-side values as stated per entry point
+ *     (AWQ_ERR_NONFINITE is reserved for that condition and is never
+ *     returned: no entry point waits for the device).
+ *   - The library allocates no device memory and keeps no device state.
+ *     Device scratch comes from the caller as a workspace whose size a query
+ *     function returns; the query runs the call's own launch plan without
+ *     launching, so the size is exactly what that call uses (0 when its
+ *     kernels need none, and then the workspace may be NULL).  Calls that
+ *     run at the same time, on any streams, need workspaces that do not
+ *     overlap; a workspace may be reused by calls ordered on one stream.
  */
 #ifndef AWQ_MI355X_H
 #define AWQ_MI355X_H
@@ -54,6 +63,7 @@ typedef enum {
   AWQ_ERR_SHAPE = 2,       /* a size or group size is out of range                */
   AWQ_ERR_ALIGN = 3,       /* a pointer is not aligned as required                 */
   AWQ_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required           */
+  AWQ_ERR_NONFINITE = 5,   /* reserved: non-finite data is reported on the device  */
   AWQ_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed           */
   AWQ_ERR_UNSUPPORTED = 7  /* not supported on this device                         */
 } awq_status;
@@ -212,8 +222,10 @@ awq_status awq_fold_inv_scale_rows(const uint16_t* w, const uint16_t* s16, int64
  *   interleaved slices of j, added in slice order; the quantized part is
  *   rounded to fp16 first).  Within 5e-3 *
  *   max(|y_ref|, rms of the row of y_ref) of the float64 value.  qweight,
- *   scales, qzeros: the RTN pack of W (layout v1).  Limits: those of
- *   awq_linear_w4a16; 0 <= count <= min(k, 1024); m <= 1048560.
+ *   scales, qzeros: the RTN pack of W (layout v1).  keep16 16-byte aligned.
+ *   Workspace: awq_linear_workspace_size(m, n, k, g) bytes (the quantized
+ *   part is awq_linear_w4a16).  Limits: those of awq_linear_w4a16;
+ *   0 <= count <= min(k, 1024); m <= 1048560.
  * Errors: NULL pointers, shapes and alignment as stated, before any launch.
  * ------------------------------------------------------------------------- */
 awq_status awq_salient_channels(const double* mean_abs, int64_t k, int32_t count,
@@ -231,7 +243,8 @@ awq_status awq_linear_mixed(const uint16_t* x, const uint32_t* qweight,
                             const uint16_t* scales, const uint32_t* qzeros,
                             const uint16_t* keep16, const uint16_t* w_s,
                             const int32_t* idx, int32_t count, int64_t m, int64_t n,
-                            int64_t k, int32_t g, uint16_t* y, void* stream);
+                            int64_t k, int32_t g, uint16_t* y, void* workspace,
+                            size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_search_scale_wbit -- awq_search_scale for 3-, 4- or 8-bit codes.
@@ -282,19 +295,22 @@ awq_status awq_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n,
  *   awq_linear_w4a16, within the same 5e-3 bound.  w_bit = 4 runs
  *   awq_linear_w4a16 (and takes its limits).  w_bit 3 and 8: up to 16
  *   tokens one MFMA kernel that streams the weights per 16-token chunk; from
- *   17 tokens a tiled GEMM (x * inv_s16 is first staged in the library's
- *   per-device scratch buffer, as for awq_linear_w4a16; calls that overlap on
- *   one device from different host threads must be serialised).
+ *   17 tokens a tiled GEMM (x * inv_s16 staged in the workspace, and fp32
+ *   partial tiles there where the linear is split along K).
  *   x [m][k] fp16, qweight and inv_s16 [k] fp16 (or NULL) 16-byte aligned;
  *   qzeros 4-byte aligned, scales 2-byte aligned; y [m][n] fp16 out.
+ *   workspace: awq_linear_wbit_workspace_size(m, n, k, g, w_bit,
+ *            inv_s16 != NULL) bytes, 256-byte aligned (NULL if that is 0).
  *   Limits: g in {32, 64, 128}; k % g == 0; k % 64 == 0; 1 <= m, n
  *           <= 2^31 - 1; w_bit in {3, 4, 8}.
  * ------------------------------------------------------------------------- */
+size_t awq_linear_wbit_workspace_size(int64_t m, int64_t n, int64_t k, int32_t g,
+                                      int32_t w_bit, int32_t has_inv_s16);
 awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight,
                            const uint16_t* scales, const uint32_t* qzeros,
                            const uint16_t* inv_s16, int64_t m, int64_t n,
                            int64_t k, int32_t g, int32_t w_bit, uint16_t* y,
-                           void* stream);
+                           void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_linear_w4a16 -- y = x_tilde W_deq^T with 4-bit weights and fp16
@@ -308,25 +324,31 @@ awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight,
  *   x_tilde = x * inv_s16 (per channel) or x when inv_s16 is NULL.
  *   Accumulation is fp32; against the float64 value the result is within
  *   5e-3 * max(|y_ref|, rms of the row of y_ref) per output.
- *   x        [m][k] fp16, 16-byte aligned;  inv_s16 [k] fp16 or NULL;
- *   qweight/scales/qzeros in layout v1 (awq_pack_int4);  y [m][n] fp16 out.
- *   m = 1 runs the decode GEMV; 2 <= m <= 16 one fused skinny kernel;
- *   17 <= m <= 32 a small activation-staging kernel and a skinny kernel
- *   (GEMV mode); m > 32 the prefill GEMM.  Shapes whose activations or
- *   scale rows do not fit LDS for these take a staged two-kernel decode
- *   path.  Every path dequantizes in-kernel.
- *   The library keeps one device scratch buffer per device for the staged
- *   activations (grown on demand with hipMalloc, never freed); calls that
- *   overlap on one device from different host threads must be serialised
- *   by the caller.
- *   Limits: g in {32, 64, 128}; k % g == 0; k % 64 == 0; m >= 1; n >= 1;
- *           x and qweight 16-byte aligned.  |x_tilde| must stay within the
- *           fp16 range (larger values give a non-finite y).
+ *   x        [m][k] fp16, 16-byte aligned;  inv_s16 [k] fp16 or NULL,
+ *            16-byte aligned;  qweight/scales/qzeros in layout v1
+ *            (awq_pack_int4), qweight 16-byte aligned;  y [m][n] fp16 out.
+ *   workspace: device scratch of awq_linear_workspace_size(m, n, k, g)
+ *            bytes, 256-byte aligned, owned by the caller (NULL when the
+ *            size is 0); contents on entry are ignored.
+ *   m = 1 runs the decode GEMV and 2 <= m <= 16 one fused skinny kernel,
+ *   both without scratch; 17 <= m <= 32 a fused kernel with two token
+ *   chunks, or for linears above 16 MiB of packed weights the tiled GEMM
+ *   (GEMV mode); m > 32 the prefill GEMM (x * inv_s16 staged in the
+ *   workspace, and fp32 partial tiles there where the linear is split along
+ *   K).  Shapes whose activations or scale rows do not fit LDS for these take
+ *   a staged two-kernel decode path (activations staged in the workspace).
+ *   Every path dequantizes in-kernel.
+ *   Limits: g in {32, 64, 128}; k % g == 0; k % 64 == 0 (the kernels step
+ *           through K in 64-channel steps); m >= 1; n >= 1; n * k / 2 below
+ *           4 GiB.  |x_tilde| must stay within the fp16 range (larger values
+ *           give a non-finite y).
  * ------------------------------------------------------------------------- */
+size_t awq_linear_workspace_size(int64_t m, int64_t n, int64_t k, int32_t g);
 awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight,
                             const uint16_t* scales, const uint32_t* qzeros,
                             const uint16_t* inv_s16, int64_t m, int64_t n,
-                            int64_t k, int32_t g, uint16_t* y, void* stream);
+                            int64_t k, int32_t g, uint16_t* y, void* workspace,
+                            size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_linear_w4a16_group -- independent linears of one decode step in one
@@ -347,7 +369,12 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight,
  *   alone (the arithmetic of a column block does not depend on the launch).
  *   m = 1 and 2 <= m <= 16 run the whole group in one launch of the decode
  *   GEMV or of the fused skinny kernel when their shared-memory plans fit
- *   the k; otherwise the linears run one after another on the stream.
+ *   the k; m > 32 one activation-prep launch and one GEMM launch over the
+ *   tiles of every linear; otherwise the linears run one after another on
+ *   the stream, reusing the workspace in stream order.
+ *   workspace: awq_linear_group_workspace_size(n, count, m, k, g) bytes for
+ *            the outputs' widths n[0..count-1], 256-byte aligned (NULL if
+ *            that is 0).
  *   Limits: those of awq_linear_w4a16 for every linear; 1 <= count <= 4.
  * ------------------------------------------------------------------------- */
 typedef struct {
@@ -360,8 +387,11 @@ typedef struct {
   int64_t n;
 } awq_linear_item;
 
+size_t awq_linear_group_workspace_size(const int64_t* n, int32_t count, int64_t m,
+                                       int64_t k, int32_t g);
 awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count,
-                                  int64_t m, int64_t k, int32_t g, void* stream);
+                                  int64_t m, int64_t k, int32_t g, void* workspace,
+                                  size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * awq_linear_w4a16_bf16, awq_linear_w4a16_group_bf16 -- the 4-bit linear and
@@ -376,15 +406,18 @@ awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count,
  *   is rounded once from the fp32 accumulation to bf16 (nearest, ties to even)
  *   instead of fp16.  Within 5e-3 * max(|y_ref|, rms of the row of y_ref) of
  *   the float64 value for x in that range.  inv_s16, qweight, scales, qzeros:
- *   as awq_linear_w4a16 (fp16 scales and inv_s16).  Arguments, limits, scratch
- *   and errors: those of awq_linear_w4a16 and awq_linear_w4a16_group.
+ *   as awq_linear_w4a16 (fp16 scales and inv_s16).  Arguments, limits,
+ *   workspace sizes and errors: those of awq_linear_w4a16 and
+ *   awq_linear_w4a16_group.
  * ------------------------------------------------------------------------- */
 awq_status awq_linear_w4a16_bf16(const uint16_t* x, const uint32_t* qweight,
                                  const uint16_t* scales, const uint32_t* qzeros,
                                  const uint16_t* inv_s16, int64_t m, int64_t n,
-                                 int64_t k, int32_t g, uint16_t* y, void* stream);
+                                 int64_t k, int32_t g, uint16_t* y, void* workspace,
+                                 size_t ws_bytes, void* stream);
 awq_status awq_linear_w4a16_group_bf16(const awq_linear_item* items, int32_t count,
-                                       int64_t m, int64_t k, int32_t g, void* stream);
+                                       int64_t m, int64_t k, int32_t g, void* workspace,
+                                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

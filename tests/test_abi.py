@@ -37,7 +37,9 @@ def test_header_declares_the_path():
                  "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
                  "awq_salient_channels", "awq_channel_mask", "awq_gather_channels",
                  "awq_mixed_loss_workspace_size", "awq_mixed_loss", "awq_linear_mixed",
-                 "awq_fold_inv_scale_rows", "awq_last_error", "awq_abi_version"):
+                 "awq_fold_inv_scale_rows", "awq_last_error", "awq_abi_version",
+                 "awq_linear_workspace_size", "awq_linear_group_workspace_size",
+                 "awq_linear_wbit_workspace_size"):
         assert want in names, names
 
 
@@ -50,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in exported, name
         assert hasattr(lib, name)
         assert name in _lib.SIGNATURES, name
-    assert lib.awq_abi_version() == 1
+    assert lib.awq_abi_version() == 2
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
@@ -139,11 +141,11 @@ def test_pack_argument_errors(lib):
 
 
 def test_linear_argument_errors(lib):
-    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, FAKE, None]
+    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, FAKE, None, 0, None]
 
     def call(**kw):
         a = list(base)
-        names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "y", "st"]
+        names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "y", "ws", "wsb", "st"]
         for key, v in kw.items():
             a[names.index(key)] = v
         return _status(lib, "awq_linear_w4a16", *a)[0]
@@ -156,6 +158,48 @@ def test_linear_argument_errors(lib):
     assert call(n=0) == 2
     assert call(x=MISALIGNED) == 3
     assert call(qw=FAKE + 4) == 3
+    # inv_s16 is read with 16-byte loads
+    assert call(inv=FAKE + 2) == 3
+    assert call(inv=FAKE + 8) == 3
+    # 64 tokens run the prefill GEMM, which stages x * inv_s16 in the workspace
+    need = lib.awq_linear_workspace_size(64, 64, 256, 128)
+    assert need > 0
+    assert call(m=64, ws=None) == 4
+    assert call(m=64, ws=FAKE, wsb=need - 1) == 4
+    assert call(m=64, ws=FAKE + 16, wsb=need) == 3
+
+
+def test_linear_workspace_sizes(lib):
+    """The size queries run the call's launch plan without launching (CPU only):
+    no scratch for the decode GEMV and the fused skinny kernels, x_tilde slots
+    and split-K partial tiles for the GEMM, 0 for invalid shapes."""
+    C = __import__("ctypes")
+    for m in (1, 2, 8, 16):
+        for n, k in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)):
+            assert lib.awq_linear_workspace_size(m, n, k, 128) == 0, (m, n, k)
+            assert lib.awq_linear_workspace_size(m, n, k, 64) == 0, (m, n, k)
+    # m = 2048: one x_tilde slot of m * k halves per linear, no split
+    assert lib.awq_linear_workspace_size(2048, 4096, 4096, 128) == 2048 * 4096 * 2
+    assert lib.awq_linear_workspace_size(2048, 4096, 14336, 128) == 2048 * 14336 * 2
+    ns = (C.c_int64 * 3)(4096, 1024, 1024)
+    assert lib.awq_linear_group_workspace_size(ns, 3, 2048, 4096, 128) == 3 * 2048 * 4096 * 2
+    assert lib.awq_linear_group_workspace_size(ns, 3, 1, 4096, 128) == 0
+    # 33 tokens: 64-row tiles split along K, partial tiles after the x_tilde slot
+    assert lib.awq_linear_workspace_size(33, 4096, 4096, 128) > 33 * 4096 * 2
+    # 17-32 tokens: linears above 16 MiB of packed weights run the GEMM
+    assert lib.awq_linear_workspace_size(32, 14336, 4096, 128) > 0
+    assert lib.awq_linear_workspace_size(32, 4096, 4096, 128) == 0
+    # invalid shapes
+    assert lib.awq_linear_workspace_size(0, 64, 256, 128) == 0
+    assert lib.awq_linear_workspace_size(64, 64, 96, 32) == 0
+    assert lib.awq_linear_group_workspace_size(None, 1, 64, 256, 128) == 0
+    assert lib.awq_linear_group_workspace_size(ns, 5, 64, 4096, 128) == 0
+    # 3/8-bit: scratch only from 17 tokens (x * inv_s16, and partial tiles)
+    assert lib.awq_linear_wbit_workspace_size(16, 14336, 4096, 128, 3, 1) == 0
+    assert lib.awq_linear_wbit_workspace_size(2048, 4096, 4096, 128, 8, 1) == 2048 * 4096 * 2
+    assert lib.awq_linear_wbit_workspace_size(2048, 4096, 4096, 128, 8, 0) == 0
+    assert (lib.awq_linear_wbit_workspace_size(64, 4096, 4096, 128, 4, 1)
+            == lib.awq_linear_workspace_size(64, 4096, 4096, 128))
 
 
 def test_search_wbit_argument_errors(lib):
@@ -206,8 +250,8 @@ def test_pack_wbit_argument_errors(lib):
 
 
 def test_linear_wbit_argument_errors(lib):
-    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, 3, FAKE, None]
-    names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "wb", "y", "st"]
+    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, 3, FAKE, None, 0, None]
+    names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "wb", "y", "ws", "wsb", "st"]
 
     def call(**kw):
         a = list(base)
@@ -231,6 +275,8 @@ def test_linear_wbit_argument_errors(lib):
     # w_bit 4 takes the 4-bit entry's checks (qweight 16-byte aligned there)
     st, msg = call(wb=4, qw=FAKE + 4)
     assert st == 3 and "awq_linear_w4a16" in msg, msg
+    # from 17 tokens the tiled GEMM stages x * inv_s16 in the workspace
+    assert call(wb=3, m=64, inv=FAKE)[0] == 4
 
 
 def test_packed_shapes():
@@ -242,8 +288,8 @@ def test_packed_shapes():
 
 
 def test_linear_bf16_argument_errors(lib):
-    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, FAKE, None]
-    names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "y", "st"]
+    base = [FAKE, FAKE, FAKE, FAKE, None, 1, 64, 256, 128, FAKE, None, 0, None]
+    names = ["x", "qw", "sc", "qz", "inv", "m", "n", "k", "g", "y", "ws", "wsb", "st"]
 
     def call(**kw):
         a = list(base)
@@ -257,8 +303,8 @@ def test_linear_bf16_argument_errors(lib):
     assert call(k=96, g=32)[0] == 2
     assert call(m=0)[0] == 2
     assert call(x=MISALIGNED)[0] == 3
-    assert _status(lib, "awq_linear_w4a16_group_bf16", None, 1, 1, 256, 128, None)[0] == 1
-    st, msg = _status(lib, "awq_linear_w4a16_group_bf16", _items(2), 5, 1, 256, 128, None)
+    assert _status(lib, "awq_linear_w4a16_group_bf16", None, 1, 1, 256, 128, None, 0, None)[0] == 1
+    st, msg = _status(lib, "awq_linear_w4a16_group_bf16", _items(2), 5, 1, 256, 128, None, 0, None)
     assert st == 2 and msg.startswith("awq_linear_w4a16_group_bf16"), msg
 
 
@@ -289,8 +335,9 @@ def test_mixed_argument_errors(lib):
     assert call(m=9000) == 2
     assert call(x=MISALIGNED) == 3
     assert call(wsb=ws - 1) == 4
-    lbase = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 64, 256, 128, FAKE, None]
-    lnames = ["x", "qw", "sc", "qz", "keep", "ws", "idx", "cnt", "m", "n", "k", "g", "y", "st"]
+    lbase = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 64, 256, 128, FAKE, None, 0, None]
+    lnames = ["x", "qw", "sc", "qz", "keep", "ws", "idx", "cnt", "m", "n", "k", "g", "y", "wk", "wkb",
+              "st"]
 
     def lcall(**kw):
         a = list(lbase)
@@ -304,6 +351,8 @@ def test_mixed_argument_errors(lib):
     st, msg = lcall(g=48)
     assert st == 2 and msg.startswith("awq_linear_mixed"), msg
     assert lcall(x=MISALIGNED)[0] == 3
+    assert lcall(keep=FAKE + 2)[0] == 3          # keep16 is read as inv_s16: 16-byte loads
+    assert lcall(m=64, cnt=0)[0] == 4            # the quantized part's GEMM needs the workspace
 
 
 def test_python_binding_has_the_c_names():
@@ -339,12 +388,18 @@ def _items(count, **over):
 
 
 def test_linear_group_argument_errors(lib):
-    assert _status(lib, "awq_linear_w4a16_group", None, 1, 1, 256, 128, None)[0] == 1
-    assert _status(lib, "awq_linear_w4a16_group", _items(1), 0, 1, 256, 128, None)[0] == 2
-    assert _status(lib, "awq_linear_w4a16_group", _items(5), 5, 1, 256, 128, None)[0] == 2
-    assert _status(lib, "awq_linear_w4a16_group", _items(2, y=None), 2, 1, 256, 128, None)[0] == 1
-    assert _status(lib, "awq_linear_w4a16_group", _items(2, n=0), 2, 1, 256, 128, None)[0] == 2
-    assert _status(lib, "awq_linear_w4a16_group", _items(2), 2, 1, 200, 128, None)[0] == 2
-    assert _status(lib, "awq_linear_w4a16_group", _items(2), 2, 0, 256, 128, None)[0] == 2
-    st, msg = _status(lib, "awq_linear_w4a16_group", _items(2, x=MISALIGNED), 2, 1, 256, 128, None)
+    def call(*a):
+        return _status(lib, "awq_linear_w4a16_group", *a, None, 0, None)
+
+    assert call(None, 1, 1, 256, 128)[0] == 1
+    assert call(_items(1), 0, 1, 256, 128)[0] == 2
+    assert call(_items(5), 5, 1, 256, 128)[0] == 2
+    assert call(_items(2, y=None), 2, 1, 256, 128)[0] == 1
+    assert call(_items(2, n=0), 2, 1, 256, 128)[0] == 2
+    assert call(_items(2), 2, 1, 200, 128)[0] == 2
+    assert call(_items(2), 2, 0, 256, 128)[0] == 2
+    st, msg = call(_items(2, x=MISALIGNED), 2, 1, 256, 128)
     assert st == 3 and "awq_linear_w4a16_group" in msg
+    assert call(_items(2, inv_s16=FAKE + 4), 2, 1, 256, 128)[0] == 3
+    st, msg = call(_items(2), 2, 64, 256, 128)
+    assert st == 4 and "workspace" in msg, msg

@@ -11,6 +11,10 @@ the library's HIP kernels; there is no fallback.
     awq_pack_int4(w, s16, g)                    -> (qweight, scales, qzeros, nonfinite int32 [1])
     awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16, g) -> y fp16 [m, n]
     awq_linear_w4a16_group([(x, qweight, scales, qzeros, inv_s16, out), ...], g) -> [y, ...]
+
+The linear calls take an optional ``workspace`` (a uint8 device tensor of at
+least the size the library's query returns); without one the binding
+allocates it with torch for the call.  The library itself allocates nothing.
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ from . import _lib
 from ._lib import AWQError  # noqa: F401
 
 __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "awq_fold_inv_scale",
+           "awq_linear_workspace_size", "awq_linear_group_workspace_size", "awq_linear_wbit_workspace_size",
            "awq_pack_int4", "awq_linear_w4a16", "awq_linear_w4a16_group",
            "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit", "packed_shapes",
            "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
@@ -63,6 +68,35 @@ def _dev_tensor(t, dtype, name, ndim=None):
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
     return t
+
+
+def _workspace(need, device, workspace):
+    """(pointer, bytes) of the call's workspace: the caller's uint8 tensor, or
+    one allocated with torch when none is given (None when need is 0)."""
+    torch = _torch()
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _dev_tensor(workspace, torch.uint8, "workspace")
+    return workspace.data_ptr(), workspace.numel()
+
+
+def awq_linear_workspace_size(m, n, k, g=128):
+    """Device scratch bytes awq_linear_w4a16 (and its bf16 and mixed forms)
+    needs for this shape (0 for the decode GEMV and the fused skinny kernels)."""
+    return int(_lib.load().awq_linear_workspace_size(m, n, k, g))
+
+
+def awq_linear_group_workspace_size(ns, m, k, g=128):
+    """Device scratch bytes of awq_linear_w4a16_group for linears of widths ns."""
+    import ctypes as C
+    arr = (C.c_int64 * len(ns))(*ns)
+    return int(_lib.load().awq_linear_group_workspace_size(arr, len(ns), m, k, g))
+
+
+def awq_linear_wbit_workspace_size(m, n, k, g=128, w_bit=4, has_inv_s16=True):
+    return int(_lib.load().awq_linear_wbit_workspace_size(m, n, k, g, w_bit, 1 if has_inv_s16 else 0))
 
 
 def awq_calib_stats(x, out=None):
@@ -242,7 +276,7 @@ def awq_pack_wbit(w, s16=None, g=128, w_bit=4, out=None):
     return qw, sc, qz, bad
 
 
-def awq_linear_wbit(x, qweight, scales, qzeros, inv_s16=None, g=128, w_bit=4, out=None):
+def awq_linear_wbit(x, qweight, scales, qzeros, inv_s16=None, g=128, w_bit=4, out=None, workspace=None):
     """awq_linear_w4a16 for the layouts of awq_pack_wbit: x fp16 [m, k] -> y fp16 [m, n]."""
     torch = _torch()
     _dev_tensor(x, torch.float16, "x", 2)
@@ -262,24 +296,26 @@ def awq_linear_wbit(x, qweight, scales, qzeros, inv_s16=None, g=128, w_bit=4, ou
             raise ValueError("inv_s16 must have k entries")
     y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
     _out_tensor(y, torch.float16, (m, n), "y")
+    wp, wb = _workspace(awq_linear_wbit_workspace_size(m, n, k, g, w_bit, inv_s16 is not None), x.device,
+                        workspace)
     st = _lib.load().awq_linear_wbit(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
-                                     _ptr(inv_s16), m, n, k, g, w_bit, _ptr(y), _stream())
+                                     _ptr(inv_s16), m, n, k, g, w_bit, _ptr(y), wp, wb, _stream())
     _lib.check("awq_linear_wbit", st)
     return y
 
 
-def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
+def awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None, workspace=None):
     """y = (x * inv_s16) @ dequant(W)^T in fp16: x fp16 [m, k] -> y fp16 [m, n]."""
-    return _linear(x, qweight, scales, qzeros, inv_s16, g, out, False)
+    return _linear(x, qweight, scales, qzeros, inv_s16, g, out, False, workspace)
 
 
-def awq_linear_w4a16_bf16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None):
+def awq_linear_w4a16_bf16(x, qweight, scales, qzeros, inv_s16=None, g=128, out=None, workspace=None):
     """awq_linear_w4a16 with bf16 activations: x bf16 [m, k] -> y bf16 [m, n]
     (inv_s16 and the packed tensors as for fp16)."""
-    return _linear(x, qweight, scales, qzeros, inv_s16, g, out, True)
+    return _linear(x, qweight, scales, qzeros, inv_s16, g, out, True, workspace)
 
 
-def _linear(x, qweight, scales, qzeros, inv_s16, g, out, bf):
+def _linear(x, qweight, scales, qzeros, inv_s16, g, out, bf, workspace):
     torch = _torch()
     adt = torch.bfloat16 if bf else torch.float16
     _dev_tensor(x, adt, "x", 2)
@@ -297,26 +333,27 @@ def _linear(x, qweight, scales, qzeros, inv_s16, g, out, bf):
     y = out if out is not None else torch.empty((m, n), dtype=adt, device=x.device)
     _out_tensor(y, adt, (m, n), "y")
     fn = "awq_linear_w4a16_bf16" if bf else "awq_linear_w4a16"
+    wp, wb = _workspace(awq_linear_workspace_size(m, n, k, g), x.device, workspace)
     st = getattr(_lib.load(), fn)(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros),
-                                  _ptr(inv_s16), m, n, k, g, _ptr(y), _stream())
+                                  _ptr(inv_s16), m, n, k, g, _ptr(y), wp, wb, _stream())
     _lib.check(fn, st)
     return y
 
 
-def awq_linear_w4a16_group(items, g=128):
+def awq_linear_w4a16_group(items, g=128, workspace=None):
     """Independent linears with the same m and k (q, k, v of a layer; gate and
     up) in one call.  ``items`` holds up to four tuples (x, qweight, scales,
     qzeros, inv_s16, out) with x fp16 [m, k] and out fp16 [m, n] or None.
     Returns the list of outputs; each equals awq_linear_w4a16 of that linear."""
-    return _linear_group(items, g, False)
+    return _linear_group(items, g, False, workspace)
 
 
-def awq_linear_w4a16_group_bf16(items, g=128):
+def awq_linear_w4a16_group_bf16(items, g=128, workspace=None):
     """awq_linear_w4a16_group with bf16 activations (x and out bf16)."""
-    return _linear_group(items, g, True)
+    return _linear_group(items, g, True, workspace)
 
 
-def _linear_group(items, g, bf):
+def _linear_group(items, g, bf, workspace):
     torch = _torch()
     adt = torch.bfloat16 if bf else torch.float16
     if not 1 <= len(items) <= 4:
@@ -348,7 +385,9 @@ def _linear_group(items, g, bf):
         a.scales, a.qzeros, a.y, a.n = _ptr(scales), _ptr(qzeros), _ptr(y), n
         outs.append(y)
     fn = "awq_linear_w4a16_group_bf16" if bf else "awq_linear_w4a16_group"
-    st = getattr(_lib.load(), fn)(arr, len(items), m, k, g, _stream())
+    wp, wb = _workspace(awq_linear_group_workspace_size([int(a.n) for a in arr], m, k, g), outs[0].device,
+                        workspace)
+    st = getattr(_lib.load(), fn)(arr, len(items), m, k, g, wp, wb, _stream())
     _lib.check(fn, st)
     return outs
 
@@ -418,7 +457,7 @@ def awq_mixed_loss(w, x, keep16, g=128, workspace=None, out=None):
     return loss
 
 
-def awq_linear_mixed(x, qweight, scales, qzeros, keep16, w_s, idx, g=128, out=None):
+def awq_linear_mixed(x, qweight, scales, qzeros, keep16, w_s, idx, g=128, out=None, workspace=None):
     """y = x Wm^T (fp16 [m, n]) for the RTN pack of W with the channels idx kept
     in fp16 (w_s [count, n], keep16 the matching mask)."""
     torch = _torch()
@@ -439,9 +478,10 @@ def awq_linear_mixed(x, qweight, scales, qzeros, keep16, w_s, idx, g=128, out=No
         raise ValueError("packed tensors or keep16 do not match x")
     y = out if out is not None else torch.empty((m, n), dtype=torch.float16, device=x.device)
     _out_tensor(y, torch.float16, (m, n), "y")
+    wp, wb = _workspace(awq_linear_workspace_size(m, n, k, g), x.device, workspace)
     st = _lib.load().awq_linear_mixed(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(keep16),
                                       _ptr(w_s) if cnt > 0 else None, _ptr(idx) if cnt > 0 else None,
-                                      cnt, m, n, k, g, _ptr(y), _stream())
+                                      cnt, m, n, k, g, _ptr(y), wp, wb, _stream())
     _lib.check("awq_linear_mixed", st)
     return y
 

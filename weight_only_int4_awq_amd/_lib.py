@@ -11,7 +11,7 @@ import pathlib
 LIB_PATH = pathlib.Path(__file__).resolve().parent / "libawq_mi355x.so"
 
 STATUS = {0: "AWQ_OK", 1: "AWQ_ERR_NULL", 2: "AWQ_ERR_SHAPE", 3: "AWQ_ERR_ALIGN",
-          4: "AWQ_ERR_WORKSPACE", 6: "AWQ_ERR_HIP", 7: "AWQ_ERR_UNSUPPORTED"}
+          4: "AWQ_ERR_WORKSPACE", 5: "AWQ_ERR_NONFINITE", 6: "AWQ_ERR_HIP", 7: "AWQ_ERR_UNSUPPORTED"}
 
 # name -> (restype, argtypes)
 SIGNATURES = {
@@ -24,9 +24,14 @@ SIGNATURES = {
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "awq_pack_int4": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "awq_linear_workspace_size": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32]),
+    "awq_linear_group_workspace_size": (C.c_size_t, [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                                     C.c_int32]),
+    "awq_linear_wbit_workspace_size": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int64, C.c_int32,
+                                                    C.c_int32, C.c_int32]),
     "awq_linear_w4a16": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.c_void_p,
-                                   C.c_void_p]),
+                                   C.c_void_p, C.c_size_t, C.c_void_p]),
     "awq_fold_inv_scale": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]),
     "awq_fold_inv_scale_rows": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p,
                                           C.c_void_p]),
@@ -38,7 +43,7 @@ SIGNATURES = {
                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "awq_linear_wbit": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
-                                  C.c_void_p, C.c_void_p]),
+                                  C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
 }
 
 
@@ -51,7 +56,7 @@ class LinearItem(C.Structure):
 
 
 SIGNATURES["awq_linear_w4a16_group"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
-                                                  C.c_int32, C.c_void_p])
+                                                  C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p])
 SIGNATURES["awq_linear_w4a16_bf16"] = SIGNATURES["awq_linear_w4a16"]
 SIGNATURES["awq_salient_channels"] = (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p])
 SIGNATURES["awq_channel_mask"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p])
@@ -63,7 +68,8 @@ SIGNATURES["awq_mixed_loss"] = (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.
                                           C.c_void_p])
 SIGNATURES["awq_linear_mixed"] = (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                             C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
-                                            C.c_int64, C.c_int32, C.c_void_p, C.c_void_p])
+                                            C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,
+                                            C.c_void_p])
 SIGNATURES["awq_linear_w4a16_group_bf16"] = SIGNATURES["awq_linear_w4a16_group"]
 
 _lib = None

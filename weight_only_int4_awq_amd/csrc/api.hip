@@ -3,8 +3,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "../../include/awq_mi355x.h"
 #include "awq_common.h"
 #include "awq_internal.h"
@@ -26,40 +24,11 @@ awq_status hip_fail(hipError_t e, const char* where) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool group_ok(int32_t g) { return g == 32 || g == 64 || g == 128; }
 
-// One grow-only device scratch buffer per device for the staged activations
-// of the decode kernels.
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch[kMaxDevices] = {};
-size_t g_scratch_bytes[kMaxDevices] = {};
-
-awq_status get_scratch(size_t bytes, void** out) {
-  *out = nullptr;
-  if (bytes == 0) return AWQ_OK;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(AWQ_ERR_UNSUPPORTED, "device index %lld out of range", dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (g_scratch_bytes[dev] < bytes) {
-    size_t want = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
-    void* p = nullptr;
-    e = hipMalloc(&p, want);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(linear scratch)");
-    // the previous buffer may still be in use by queued kernels: keep it
-    // alive (grown buffers are rare and small)
-    g_scratch[dev] = p;
-    g_scratch_bytes[dev] = want;
-  }
-  *out = g_scratch[dev];
-  return AWQ_OK;
-}
-
 }  // namespace
 
 extern "C" {
 
-int32_t awq_abi_version(void) { return 1; }
+int32_t awq_abi_version(void) { return 2; }
 
 const char* awq_last_error(void) { return g_err; }
 
@@ -221,11 +190,12 @@ awq_status check_linear_args(const char* fn, const uint16_t* x, const uint32_t* 
     snprintf(g_err, sizeof(g_err), "%s: n=%lld out of range", fn, (long long)n);
     return AWQ_ERR_SHAPE;
   }
-  if (!aligned(x, 16) || !aligned(qweight, 16)) {
-    snprintf(g_err, sizeof(g_err), "%s: x and qweight must be 16-byte aligned", fn);
+  // x, inv_s16 and qweight are read with 16-byte loads and direct-to-LDS copies
+  if (!aligned(x, 16) || !aligned(qweight, 16) || (inv_s16 && !aligned(inv_s16, 16))) {
+    snprintf(g_err, sizeof(g_err), "%s: x, inv_s16 and qweight must be 16-byte aligned", fn);
     return AWQ_ERR_ALIGN;
   }
-  if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2) || (inv_s16 && !aligned(inv_s16, 2))) {
+  if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2)) {
     snprintf(g_err, sizeof(g_err), "%s: misaligned pointer", fn);
     return AWQ_ERR_ALIGN;
   }
@@ -237,25 +207,48 @@ awq_status check_linear_args(const char* fn, const uint16_t* x, const uint32_t* 
   return AWQ_OK;
 }
 
+// the caller's workspace against what the call's plan needs
+awq_status check_workspace(const char* fn, size_t need, const void* workspace, size_t ws_bytes) {
+  if (need == 0) return AWQ_OK;
+  if (!workspace || ws_bytes < need) {
+    snprintf(g_err, sizeof(g_err), "%s: workspace of %llu bytes < %llu needed", fn,
+             (unsigned long long)(workspace ? ws_bytes : 0), (unsigned long long)need);
+    return AWQ_ERR_WORKSPACE;
+  }
+  if (!aligned(workspace, 256)) {
+    snprintf(g_err, sizeof(g_err), "%s: workspace must be 256-byte aligned", fn);
+    return AWQ_ERR_ALIGN;
+  }
+  return AWQ_OK;
+}
+
+awq_status run_linear_group(const char* fn, const awq::LinItem* li, int32_t count, int64_t m, int64_t k,
+                            int32_t g, void* workspace, size_t ws_bytes, void* stream) {
+  const size_t need = awq::linear_group_scratch_bytes(li, count, m, k, g);
+  awq_status st = check_workspace(fn, need, workspace, ws_bytes);
+  if (st != AWQ_OK) return st;
+  awq::Scratch scr;
+  scr.base = static_cast<char*>(workspace);
+  hipError_t e = awq::launch_linear_group(li, count, m, k, g, scr, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return AWQ_OK;
+}
+
 awq_status linear_impl(const char* fn, const uint16_t* x, const uint32_t* qweight,
                        const uint16_t* scales, const uint32_t* qzeros, const uint16_t* inv_s16,
                        int64_t m, int64_t n, int64_t k, int32_t g, uint16_t* y, int32_t bf,
-                       void* stream) {
+                       void* workspace, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   awq_status st0 = check_linear_args(fn, x, qweight, scales, qzeros, inv_s16, m, n, k, g, y);
   if (st0 != AWQ_OK) return st0;
   awq::LinItem it{x, inv_s16, qweight, scales, qzeros, y, n};
   it.bf = bf;
-  void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_group_scratch_bytes(&it, 1, m, k, g), &scratch);
-  if (st != AWQ_OK) return st;
-  hipError_t e = awq::launch_linear_group(&it, 1, m, k, g, scratch, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, fn);
-  return AWQ_OK;
+  return run_linear_group(fn, &it, 1, m, k, g, workspace, ws_bytes, stream);
 }
 
 awq_status linear_group_impl(const char* fn, const awq_linear_item* items, int32_t count, int64_t m,
-                             int64_t k, int32_t g, int32_t bf, void* stream) {
+                             int64_t k, int32_t g, int32_t bf, void* workspace, size_t ws_bytes,
+                             void* stream) {
   g_err[0] = 0;
   if (!items) {
     snprintf(g_err, sizeof(g_err), "%s: null items", fn);
@@ -275,48 +268,79 @@ awq_status linear_group_impl(const char* fn, const awq_linear_item* items, int32
     li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
     li[i].bf = bf;
   }
-  void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_group_scratch_bytes(li, count, m, k, g), &scratch);
-  if (st != AWQ_OK) return st;
-  hipError_t e = awq::launch_linear_group(li, count, m, k, g, scratch, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, fn);
-  return AWQ_OK;
+  return run_linear_group(fn, li, count, m, k, g, workspace, ws_bytes, stream);
+}
+
+bool linear_shape_ok(int64_t m, int64_t n, int64_t k, int32_t g) {
+  return group_ok(g) && k >= 64 && k % g == 0 && k % 64 == 0 && m >= 1 && m <= 0x7FFFFFFF && n >= 1 &&
+         n <= 0x7FFFFFFF;
 }
 
 }  // namespace
 
 extern "C" {
 
+size_t awq_linear_workspace_size(int64_t m, int64_t n, int64_t k, int32_t g) {
+  if (!linear_shape_ok(m, n, k, g)) return 0;
+  awq::LinItem it{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, n};
+  return awq::linear_group_scratch_bytes(&it, 1, m, k, g);
+}
+
+size_t awq_linear_group_workspace_size(const int64_t* n, int32_t count, int64_t m, int64_t k,
+                                       int32_t g) {
+  if (!n || count < 1 || count > awq::kGroupMax) return 0;
+  awq::LinItem li[awq::kGroupMax];
+  for (int32_t i = 0; i < count; ++i) {
+    if (!linear_shape_ok(m, n[i], k, g)) return 0;
+    li[i] = awq::LinItem{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, n[i]};
+  }
+  return awq::linear_group_scratch_bytes(li, count, m, k, g);
+}
+
 awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                             const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
-                            int64_t k, int32_t g, uint16_t* y, void* stream) {
+                            int64_t k, int32_t g, uint16_t* y, void* workspace, size_t ws_bytes,
+                            void* stream) {
   return linear_impl("awq_linear_w4a16", x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, 0,
-                     stream);
+                     workspace, ws_bytes, stream);
 }
 
 awq_status awq_linear_w4a16_bf16(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                                  const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m,
-                                 int64_t n, int64_t k, int32_t g, uint16_t* y, void* stream) {
+                                 int64_t n, int64_t k, int32_t g, uint16_t* y, void* workspace,
+                                 size_t ws_bytes, void* stream) {
   return linear_impl("awq_linear_w4a16_bf16", x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, 1,
-                     stream);
+                     workspace, ws_bytes, stream);
 }
 
 awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count, int64_t m, int64_t k,
-                                  int32_t g, void* stream) {
-  return linear_group_impl("awq_linear_w4a16_group", items, count, m, k, g, 0, stream);
+                                  int32_t g, void* workspace, size_t ws_bytes, void* stream) {
+  return linear_group_impl("awq_linear_w4a16_group", items, count, m, k, g, 0, workspace, ws_bytes,
+                           stream);
 }
 
 awq_status awq_linear_w4a16_group_bf16(const awq_linear_item* items, int32_t count, int64_t m,
-                                       int64_t k, int32_t g, void* stream) {
-  return linear_group_impl("awq_linear_w4a16_group_bf16", items, count, m, k, g, 1, stream);
+                                       int64_t k, int32_t g, void* workspace, size_t ws_bytes,
+                                       void* stream) {
+  return linear_group_impl("awq_linear_w4a16_group_bf16", items, count, m, k, g, 1, workspace,
+                           ws_bytes, stream);
+}
+
+size_t awq_linear_wbit_workspace_size(int64_t m, int64_t n, int64_t k, int32_t g, int32_t w_bit,
+                                      int32_t has_inv_s16) {
+  if (w_bit == 4) return awq_linear_workspace_size(m, n, k, g);
+  if ((w_bit != 3 && w_bit != 8) || !linear_shape_ok(m, n, k, g)) return 0;
+  return awq::linear_wbit_scratch_bytes(m, n, k, g, has_inv_s16 != 0);
 }
 
 awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                            const uint32_t* qzeros, const uint16_t* inv_s16, int64_t m, int64_t n,
-                           int64_t k, int32_t g, int32_t w_bit, uint16_t* y, void* stream) {
+                           int64_t k, int32_t g, int32_t w_bit, uint16_t* y, void* workspace,
+                           size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (w_bit == 4) {
-    awq_status st = awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, stream);
+    awq_status st = awq_linear_w4a16(x, qweight, scales, qzeros, inv_s16, m, n, k, g, y, workspace,
+                                     ws_bytes, stream);
     if (st != AWQ_OK) {
       char msg[512];
       snprintf(msg, sizeof(msg), "awq_linear_wbit (w_bit 4) -> %s", g_err);
@@ -335,11 +359,11 @@ awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight, const uin
     return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: x, qweight and inv_s16 must be 16-byte aligned");
   if (!aligned(qzeros, 4) || !aligned(scales, 2) || !aligned(y, 2))
     return fail(AWQ_ERR_ALIGN, "awq_linear_wbit: misaligned pointer");
-  void* scratch = nullptr;
-  awq_status st = get_scratch(awq::linear_wbit_scratch_bytes(m, n, k, g, inv_s16 != nullptr), &scratch);
+  const size_t need = awq::linear_wbit_scratch_bytes(m, n, k, g, inv_s16 != nullptr);
+  awq_status st = check_workspace("awq_linear_wbit", need, workspace, ws_bytes);
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_linear_wbit(x, qweight, scales, qzeros, inv_s16, m, n, k, g, w_bit, y,
-                                         scratch, (hipStream_t)stream);
+                                         workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_wbit launch");
   return AWQ_OK;
 }
@@ -411,16 +435,16 @@ awq_status awq_mixed_loss(const uint16_t* w, const uint16_t* x, const uint16_t* 
 awq_status awq_linear_mixed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                             const uint32_t* qzeros, const uint16_t* keep16, const uint16_t* w_s,
                             const int32_t* idx, int32_t count, int64_t m, int64_t n, int64_t k,
-                            int32_t g, uint16_t* y, void* stream) {
+                            int32_t g, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (!keep16 || ((!w_s || !idx) && count > 0)) return fail(AWQ_ERR_NULL, "awq_linear_mixed: null pointer");
   if (count < 0 || count > k || count > awq::kMixedMaxCount)
     return fail(AWQ_ERR_SHAPE, "awq_linear_mixed: count=%lld outside 0..min(k, %lld)", count, awq::kMixedMaxCount);
   if (m > (int64_t)65535 * 16) return fail(AWQ_ERR_SHAPE, "awq_linear_mixed: m=%lld too large", m);
-  if (!aligned(keep16, 2) || (w_s && !aligned(w_s, 2)) || (idx && !aligned(idx, 4)))
-    return fail(AWQ_ERR_ALIGN, "awq_linear_mixed: misaligned pointer");
+  if (!aligned(keep16, 16) || (w_s && !aligned(w_s, 2)) || (idx && !aligned(idx, 4)))
+    return fail(AWQ_ERR_ALIGN, "awq_linear_mixed: misaligned pointer (keep16 must be 16-byte aligned)");
   awq_status st = linear_impl("awq_linear_mixed", x, qweight, scales, qzeros, keep16, m, n, k, g, y, 0,
-                              stream);
+                              workspace, ws_bytes, stream);
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_salient_add(x, idx, count, w_s, m, n, k, y, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_mixed launch");

@@ -57,19 +57,30 @@ struct LinItem {
   int32_t bf = 0;          // 1: x and y hold bf16 patterns (the same for every item of a call)
 };
 
-// Scratch bytes a call of count linears (same m, k, g) needs for the staged
-// activations (and, for m > 32, the scaled activations of every linear and the
-// fp32 partial tiles of the linears split along K).
-size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g, int count);
-size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k,
-                                  int32_t g);
+// Device scratch of one linear call: the caller's workspace (base), or a
+// plan-only pass (dry) in which the launch code records the bytes its plan
+// would use (need) and launches nothing.  One code path decides the plan for
+// both, so the size the library asks for is exactly what the launches touch.
+struct Scratch {
+  char* base = nullptr;
+  size_t need = 0;
+  bool dry = false;
+  // the scratch bytes [off, off + bytes) of this call (nullptr in a dry pass)
+  char* at(size_t off, size_t bytes) {
+    if (off + bytes > need) need = off + bytes;
+    return base ? base + off : nullptr;
+  }
+};
 
 // 1..kGroupMax independent linears of the same m, k and g: one launch for the
 // kernels that take groups (decode GEMV, fused skinny, prefill GEMM),
-// consecutive launches otherwise.  Each y
-// holds the bits launch_linear writes for that linear alone.
+// consecutive launches otherwise.  Each y holds the bits a call of that
+// linear alone writes.  Scratch: linear_group_scratch_bytes bytes,
+// 256-byte aligned (0 for the decode GEMV and the fused skinny kernels).
 hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
-                               void* scratch, hipStream_t stream);
+                               Scratch& scr, hipStream_t stream);
+size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k,
+                                  int32_t g);
 
 // mixed-precision baseline (mixed.hip)
 hipError_t launch_salient_select(const double* a, int64_t k, int32_t count, int32_t* idx,

@@ -39,40 +39,6 @@ static int64_t gemm_row_chunk(int64_t k);
 
 static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k, int32_t g);
 
-static bool skinny_wide(const LinItem& it, int64_t m, int64_t k);
-
-size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k,
-                                  int32_t g) {
-  size_t total = linear_scratch_bytes(m, k, g, count);
-  if (m > 32) {
-    for (int l = 0; l < count; ++l) total += gemm_part_bytes(m, items[l].n, k, g);
-  } else if (m > 16) {
-    // wide linears run the GEMM: x_tilde slots and partial tiles
-    size_t gemm = 0;
-    int nw = 0;
-    for (int l = 0; l < count; ++l)
-      if (skinny_wide(items[l], m, k)) {
-        gemm += gemm_part_bytes(m, items[l].n, k, g);
-        ++nw;
-      }
-    gemm += (size_t)nw * align256((size_t)m * (size_t)k * 2);
-    total = total > gemm ? total : gemm;
-  }
-  return total;
-}
-
-size_t linear_scratch_bytes(int64_t m, int64_t k, int32_t g, int count) {
-  if (m > 32) {                 // scaled, permuted activations: one slot per linear
-    const size_t slot = align256((size_t)m * (size_t)k * 2);
-    return m <= gemm_row_chunk(k) ? (size_t)count * slot : slot;
-  }
-  const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
-  const int64_t ng = k / g;
-  size_t a = (size_t)tc * (size_t)k * 16 * 2;          // [tc][ng][4][16][g/4] halves
-  size_t tu = (size_t)tc * (size_t)ng * 16 * 8;        // [tc][ng][16] float2
-  return align256(a) + align256(tu);
-}
-
 // slot s (0..7) of an 8-channel word in unpack order -> nibble index
 __device__ __forceinline__ int slot_nibble(int s) { return (s >> 1) + 4 * (s & 1); }
 
@@ -1977,7 +1943,7 @@ static bool scales_octets(const LinItem* items, int count, int64_t ng) {
 }
 
 template <int G>
-static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, void* scratch,
+static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, Scratch& scr,
                                     hipStream_t stream) {
   const uint16_t* x = it.x;
   const uint32_t* qweight = it.qw;
@@ -2007,9 +1973,12 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
       const int nb = (int)((nblk + grid - 1) / grid);
       const size_t lds = skinny16_lds_bytes(k, G, nb, tcs);
       const bool szv = (ng_all % 8 == 0) && (reinterpret_cast<uintptr_t>(scales) % 16 == 0);
-      char* sp16 = static_cast<char*>(scratch);
+      // x_tilde [2][ng][4][16][g/4] halves, then T, U [2][ng][16] float2
+      const size_t a_bytes = align256((size_t)tcs * (size_t)k * 16 * 2);
+      char* sp16 = scr.at(0, a_bytes + (size_t)tcs * (size_t)ng_all * 16 * 8);
+      if (scr.dry) return hipSuccess;
       uint16_t* a16 = reinterpret_cast<uint16_t*>(sp16);
-      float2* tu16 = reinterpret_cast<float2*>(sp16 + align256((size_t)tcs * (size_t)k * 16 * 2));
+      float2* tu16 = reinterpret_cast<float2*>(sp16 + a_bytes);
       const int64_t n_pairs = tcs * ng_all;
       hipLaunchKernelGGL(linear_prep16_kernel<G>, dim3((unsigned)((n_pairs + 3) / 4)), dim3(256), 0,
                          stream, x, inv_s16, m, k, n_pairs, a16, tu16, bf);
@@ -2032,9 +2001,12 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, voi
   // the staged two-kernel decode path (any m <= 32 whose plans above do not fit)
   const int64_t tc = (m + kSkinnyTok - 1) / kSkinnyTok;
   const int64_t ng = k / G;
-  char* sp = static_cast<char*>(scratch);
+  // x_tilde [tc][ng][4][16][g/4] halves, then T, U [tc][ng][16] float2
+  const size_t a_bytes = align256((size_t)tc * (size_t)k * 16 * 2);
+  char* sp = scr.at(0, a_bytes + (size_t)tc * (size_t)ng * 16 * 8);
+  if (scr.dry) return hipSuccess;
   uint16_t* a_st = reinterpret_cast<uint16_t*>(sp);
-  float2* tu = reinterpret_cast<float2*>(sp + align256((size_t)tc * (size_t)k * 16 * 2));
+  float2* tu = reinterpret_cast<float2*>(sp + a_bytes);
   const int64_t n_pairs = tc * ng;
   hipLaunchKernelGGL(linear_prep_kernel<G>, dim3((unsigned)((n_pairs + 3) / 4)), dim3(256), 0,
                      stream, x, inv_s16, m, k, n_pairs, a_st, tu, bf);
@@ -2075,7 +2047,7 @@ static bool skinny_wide(const LinItem& it, int64_t m, int64_t k) {
 // linear, in row chunks, through scratch slot 0.
 template <int G>
 static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, int64_t k,
-                                    void* scratch, hipStream_t stream) {
+                                    Scratch& scr, hipStream_t stream) {
   const int bm = gemm_bm(m);
   const int64_t chunk = gemm_row_chunk(k);
   const bool whole = m <= chunk;
@@ -2093,11 +2065,19 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
   const void* fn = bm == 64 ? reinterpret_cast<const void*>(&linear_gemm_kernel<G, 64>)
                             : reinterpret_cast<const void*>(&linear_gemm_kernel<G, kGemmBM>);
   if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
+  // scratch: one x_tilde slot per linear and the fp32 partial tiles of the
+  // split linears (whole m in one launch), else slot 0 reused linear by linear
+  const size_t slot_bytes = align256((size_t)m * (size_t)k * 2);
+  size_t scratch_bytes = whole ? (size_t)count * slot_bytes : slot_bytes;
+  if (whole)
+    for (int l = 0; l < count; ++l)
+      if (sks[l] > 1) scratch_bytes += gemm_part_bytes(m, items[l].n, k, G);
+  char* const scratch = scr.at(0, scratch_bytes);
+  if (scr.dry) return hipSuccess;
   if (lds + lds_static > 65536) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const size_t slot_bytes = align256((size_t)m * (size_t)k * 2);
   const int n_batch = whole ? 1 : count;
   for (int bt = 0; bt < n_batch; ++bt) {
     const LinItem* its = whole ? items : items + bt;
@@ -2106,7 +2086,7 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
     for (int l = 0; l < cnt; ++l) {
       xg.x[l] = its[l].x;
       xg.inv[l] = its[l].inv;
-      xg.y[l] = reinterpret_cast<uint16_t*>(static_cast<char*>(scratch) + (size_t)l * slot_bytes);
+      xg.y[l] = reinterpret_cast<uint16_t*>(scratch + (size_t)l * slot_bytes);
     }
     xg.count = cnt;
     xg.bf = its[0].bf;
@@ -2120,7 +2100,7 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
       LinGroup gg = {};
       int total = 0;
       bool split = false;
-      char* part = static_cast<char*>(scratch) + (size_t)cnt * slot_bytes;
+      char* part = scratch + (size_t)cnt * slot_bytes;
       for (int l = 0; l < cnt; ++l) {
         const int64_t n = its[l].n;
         gg.x[l] = xg.y[l] + r0 * k;
@@ -2167,10 +2147,10 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
 
 template <int G>
 static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t m, int64_t k,
-                                        void* scratch, hipStream_t stream) {
+                                        Scratch& scr, hipStream_t stream) {
   // fused skinny plan above 16 tokens: groups of at most this many packed bytes
   constexpr int64_t kFusedMax = (int64_t)16 << 20;
-  if (m > 32) return launch_gemm_group<G>(items, count, m, k, scratch, stream);
+  if (m > 32) return launch_gemm_group<G>(items, count, m, k, scr, stream);
   // the decode GEMV (m = 1): at most kGemvMaxBlk column blocks per
   // work-group, whose scale/zero octets fit the prologue (kGemvSzRounds per
   // thread) and whose LDS plan fits 160 KiB
@@ -2203,6 +2183,7 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
       const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
       const size_t lds = gemv_lds_bytes(k, G, nb, waves);
       const bool szv = scales_octets(items, count, ng_all);
+      if (scr.dry) return hipSuccess;               // the decode GEMV takes no scratch
       const void* fn =
           waves == 16 ? (szv ? reinterpret_cast<const void*>(&linear_gemv_kernel<G, true, 16>)
                              : reinterpret_cast<const void*>(&linear_gemv_kernel<G, false, 16>))
@@ -2249,6 +2230,7 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
       const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
       const size_t lds = skinny_fused_lds_bytes(k, G, nb, tcs);
       const bool szv = scales_octets(items, count, ng_all);
+      if (scr.dry) return hipSuccess;               // the fused skinny kernels take no scratch
       const dim3 gd((unsigned)gp.wg0[count]), bd(kSk16Threads);
 #define AWQ_SKF(TCC, SZ, PFF)                                                                  \
   {                                                                                            \
@@ -2307,10 +2289,10 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
       else rest[nr++] = items[l];
     }
     if (nw > 0) {
-      hipError_t e = launch_gemm_group<G>(wide, nw, m, k, scratch, stream);
+      hipError_t e = launch_gemm_group<G>(wide, nw, m, k, scr, stream);
       if (e != hipSuccess) return e;
       for (int l = 0; l < nr; ++l) {
-        e = launch_linear_group_g<G>(rest + l, 1, m, k, scratch, stream);
+        e = launch_linear_group_g<G>(rest + l, 1, m, k, scr, stream);
         if (e != hipSuccess) return e;
       }
       return hipSuccess;
@@ -2319,24 +2301,31 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
   // every other case: one linear after another on the stream, each planned as
   // a call of it alone (the staged kernels share the scratch buffer, in
   // stream order)
-  if (count == 1) return launch_linear_one<G>(items[0], m, k, scratch, stream);
+  if (count == 1) return launch_linear_one<G>(items[0], m, k, scr, stream);
   for (int l = 0; l < count; ++l) {
-    hipError_t e = launch_linear_group_g<G>(items + l, 1, m, k, scratch, stream);
+    hipError_t e = launch_linear_group_g<G>(items + l, 1, m, k, scr, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_linear_group(const LinItem* items, int count, int64_t m, int64_t k, int32_t g,
-                               void* scratch, hipStream_t stream) {
+                               Scratch& scr, hipStream_t stream) {
   switch (g) {
     case 32:
-      return launch_linear_group_g<32>(items, count, m, k, scratch, stream);
+      return launch_linear_group_g<32>(items, count, m, k, scr, stream);
     case 64:
-      return launch_linear_group_g<64>(items, count, m, k, scratch, stream);
+      return launch_linear_group_g<64>(items, count, m, k, scr, stream);
     default:
-      return launch_linear_group_g<128>(items, count, m, k, scratch, stream);
+      return launch_linear_group_g<128>(items, count, m, k, scr, stream);
   }
+}
+
+size_t linear_group_scratch_bytes(const LinItem* items, int count, int64_t m, int64_t k, int32_t g) {
+  Scratch scr;
+  scr.dry = true;
+  (void)launch_linear_group(items, count, m, k, g, scr, nullptr);
+  return scr.need;
 }
 
 }  // namespace awq
