@@ -45,21 +45,22 @@ def u32(t):
 
 
 def _pack(P, w, s16, g):
-    qw, sc, qz, _ = P.awq_pack_int4(dev(w), None if s16 is None else dev(s16), g=g)
-    return qw, sc, qz
+    """The oracle's pack of w at s16, uploaded (linear tests never feed the
+    oracle a GPU result)."""
+    hq, hs, hz, _ = O.pack_int4(w, s16, g)
+    return dev(hq.view(np.int32)), dev(hs), dev(hz.view(np.int32)), (hq, hs, hz)
 
 
 def _check(P, w, xb, s16, g, cols=None):
     """bf16 linear against the oracle; returns (y bf16 as float64, packed tensors, inv)."""
     inv = None if s16 is None else O.fp16_rn(1.0 / s16.astype(np.float64))
-    qw, sc, qz = _pack(P, w, s16, g)
+    qw, sc, qz, (hq, hs, hz) = _pack(P, w, s16, g)
     y = P.awq_linear_w4a16_bf16(dev_bf16(xb), qw, sc, qz, None if inv is None else dev(inv), g=g)
     torch.cuda.synchronize()
     assert y.dtype == torch.bfloat16
     k = w.shape[1]
     x = O.bf16_to_f64(xb)
     yh = host_bf16(y)
-    hq, hs, hz = u32(qw), sc.cpu().numpy(), u32(qz)
     if cols is None:
         yr = O.linear_ref(x, hq, hs, hz, inv, k, g)
         ok, worst, raw = O.check_linear(yh, yr)
@@ -152,7 +153,7 @@ def test_linear_bf16_group_matches_single(P, m):
     inv = dev(O.fp16_rn(1.0 / O.scale_candidate(
         O.calib_stats(S.activations(64, k, 2452, S.outlier_channels(k, 0.01, 2451), 20.0)), 0.3)
         .astype(np.float64)))
-    packs = [_pack(P, S.weights(n, k, 0.02, 2453 + i), None, g) for i, n in enumerate(ns)]
+    packs = [_pack(P, S.weights(n, k, 0.02, 2453 + i), None, g)[:3] for i, n in enumerate(ns)]
     singles = [P.awq_linear_w4a16_bf16(xb, qw, sc, qz, inv, g=g) for qw, sc, qz in packs]
     outs = P.awq_linear_w4a16_group_bf16([(xb, qw, sc, qz, inv, None) for qw, sc, qz in packs], g=g)
     torch.cuda.synchronize()
@@ -163,7 +164,7 @@ def test_linear_bf16_group_matches_single(P, m):
 
 def test_linear_bf16_deterministic(P):
     w = S.weights(512, 2048, 0.02, 2461)
-    qw, sc, qz = _pack(P, w, None, 128)
+    qw, sc, qz, _ = _pack(P, w, None, 128)
     for m in (1, 8, 32, 300):
         xb = dev_bf16(S.activations_bf16(m, 2048, 2462 + m))
         a = P.awq_linear_w4a16_bf16(xb, qw, sc, qz, None, g=128)

@@ -132,13 +132,13 @@ def test_mixed_loss_full_k_sampled_rows(P):
 
 def _check_mixed_linear(P, w, x, idx, g, cols=None):
     k = w.shape[1]
-    qw, sc, qz, _ = P.awq_pack_int4(dev(w), None, g=g)
+    hq, hs, hz, _ = O.pack_int4(w, None, g)          # the oracle's RTN pack, uploaded
+    qw, sc, qz = dev(hq.view(np.int32)), dev(hs), dev(hz.view(np.int32))
     di = dev(idx)
     keep = P.awq_channel_mask(di, k)
     ws = P.awq_gather_channels(dev(w), di)
     y = P.awq_linear_mixed(dev(x), qw, sc, qz, keep, ws, di, g=g)
     torch.cuda.synchronize()
-    hq, hs, hz = u32(qw), sc.cpu().numpy(), u32(qz)
     yh = y.cpu().numpy()
     if cols is None:
         yr = O.linear_mixed_ref(x, hq, hs, hz, w, idx, k, g)

@@ -13,6 +13,8 @@ import pytest
 import synthetic as S
 from oracle import awq_oracle as O
 
+from tests import search_bound as SB
+
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
@@ -133,30 +135,22 @@ def test_pack_full_size_sampled_rows(P, name, n, k):
 # ----------------------------------------------------------------- search
 
 
-def _check_search(P, w, x, g, n_grid, expect_best=None):
+def _check_search(P, w, x, g, n_grid, expect_best=None, label=None):
+    """GPU search against the oracle: alpha index, s16 and inv_s16 bit for bit,
+    every loss within the bound derived from the kernel's arithmetic
+    (tests/search_bound.py).  Prints the oracle's best-vs-second gap and its
+    margin over the two losses' bounds (margin > 1: the index cannot flip)."""
     a_dev = P.awq_calib_stats(dev(x))
     best, s16, inv, losses = P.awq_search_scale(dev(w), dev(x), a_dev, g=g, n_grid=n_grid)
     torch.cuda.synchronize()
     a = O.calib_stats(x)
     ob, os16, oinv, olosses = O.search_scale(w, x, a, g=g, n_grid=n_grid)
-    gl = losses.cpu().numpy()
-    fin = np.isfinite(olosses)
-    assert np.array_equal(np.isfinite(gl), fin)
-    # The kernel's loss carries the fp32 accumulation error of E = dW X^T plus the
-    # 2^-22 residue of the fp16 hi+lo split of dW.  Both are bounded per output by
-    # gamma * sum_k |dW X| with gamma far below 1e-5, so with
-    # S = sum_{t,n} (sum_k |dW_nk X_tk|)^2:  |L_gpu - L| <= 2 gamma sqrt(L S) + gamma^2 S.
-    gamma = 1e-5
-    xa = np.abs(x.astype(np.float64))
-    for i in np.flatnonzero(fin):
-        s_i = O.scale_candidate(a, i / n_grid)
-        dw = O.fake_quantize(w, s_i, g)[5] / s_i.astype(np.float64)[None, :] - w.astype(np.float64)
-        sabs = float(np.sum((np.abs(dw) @ xa.T) ** 2))
-        bound = 2 * gamma * np.sqrt(olosses[i] * sabs) + gamma * gamma * sabs
-        assert abs(gl[i] - olosses[i]) <= bound, (i, gl[i], olosses[i], bound)
-    srt = np.sort(olosses[fin])
-    gap = (srt[1] - srt[0]) / srt[0] if len(srt) > 1 and srt[0] > 0 else np.inf
-    assert int(best.item()) == ob, (int(best.item()), ob, gap)
+    dnorm = SB.loss_bounds(w, x, a, g, n_grid)
+    worst = SB.check_losses(losses.cpu().numpy(), olosses, dnorm)
+    b, second, gap, margin = SB.gap_report(olosses, dnorm)
+    print(f"search gap [{label or (w.shape, x.shape[0], g)}]: best {ob} second {second} "
+          f"gap {gap:.3e} margin {margin:.3g} max rel loss err {worst:.2e}")
+    assert int(best.item()) == ob, (int(best.item()), ob, gap, margin)
     assert np.array_equal(s16.cpu().numpy().view(np.uint16), os16.view(np.uint16))
     assert np.array_equal(inv.cpu().numpy().view(np.uint16), oinv.view(np.uint16))
     if expect_best is not None:
@@ -230,13 +224,20 @@ def test_search_deterministic(P):
 # ----------------------------------------------------------------- linear
 
 
+def oracle_pack(w, s16, g):
+    """The oracle's pack of w at s16 (CPU), uploaded: (qweight, scales, qzeros) on
+    the device and as host arrays.  Linear tests take their packed weights from
+    the oracle, never from the GPU pack."""
+    hq, hs, hz, _ = O.pack_int4(w, s16, g)
+    return (dev(hq.view(np.int32)), dev(hs), dev(hz.view(np.int32))), (hq, hs, hz)
+
+
 def _check_linear(P, w, x, s16, g, cols=None):
     inv = None if s16 is None else O.fp16_rn(1.0 / s16.astype(np.float64))
-    qw, sc, qz, _ = P.awq_pack_int4(dev(w), None if s16 is None else dev(s16), g=g)
+    (qw, sc, qz), (hq, hs, hz) = oracle_pack(w, s16, g)
     y = P.awq_linear_w4a16(dev(x), qw, sc, qz, None if inv is None else dev(inv), g=g)
     torch.cuda.synchronize()
     k = w.shape[1]
-    hq, hs, hz = host_u32(qw), sc.cpu().numpy(), host_u32(qz)
     yh = host16(y)
     if cols is None:
         yr = O.linear_ref(x, hq, hs, hz, inv, k, g)
@@ -268,14 +269,27 @@ def test_linear_ragged(P, n, k):
         _check_linear(P, w, x, None, 64)
 
 
+@pytest.mark.parametrize("g", [128, 64])
 @pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
-@pytest.mark.parametrize("m", [1, 8, 24])
-def test_linear_decode_full_size(P, name, n, k, m):
-    # m = 24: the fused two-chunk kernel for q, k, v and o, the grouped GEMM
-    # (64-row tiles, split along K) for gate, up and down
-    w, x_cal, x_run, _ = S.config_layer(2, name, n, k, 128, m, 0.02, 0.01, 20.0)
+def test_linear_decode_full_size(P, name, n, k, g):
+    # every output of the Llama-3-8B-shaped linears at the decode sizes, with
+    # group sizes 128 and 64 (the stack's two variants): m = 1 the decode GEMV,
+    # 8 the fused skinny kernel (group-major where blocks are shared), 24 and 32
+    # the fused two-chunk kernel for q, k, v and o and the grouped GEMM (64-row
+    # tiles, split along K) for gate, up and down
+    w, x_cal, _, _ = S.config_layer(2, name, n, k, 128, 0, 0.02, 0.01, 20.0)
     s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
-    _check_linear(P, w, x_run, s16, 128)
+    inv = O.fp16_rn(1.0 / s16.astype(np.float64))
+    (qw, sc, qz), (hq, hs, hz) = oracle_pack(w, s16, g)
+    del w
+    ch = S.outlier_channels(k, 0.01, S.seed_of(2, 0, S.SLOTS.get(S.INPUT_OF[name], 0), 3))
+    for m in ((1, 8, 24, 32) if g == 128 else (1, 8, 32)):
+        x = S.activations(m, k, S.seed_of(2, 0, S.SLOTS[name], 2) + m, ch, 20.0)
+        y = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=g)
+        torch.cuda.synchronize()
+        yr = O.linear_ref(x, hq, hs, hz, inv, k, g)
+        ok, worst, raw = O.check_linear(host16(y), yr)
+        assert ok, (m, worst, raw)
 
 
 @pytest.mark.parametrize("name,n,k", S.LLAMA3_8B_LINEARS)
@@ -365,7 +379,7 @@ def test_linear_packed_weights_at_4gib(P):
 def test_linear_split_k_full_size_sampled(P, m):
     # between the skinny kernels and a full prefill the GEMM's tiles alone
     # leave CUs idle: 64-row tiles up to 64 tokens, and each tile's K-steps
-    # split over several work-groups (fp32 partial tiles in scratch, summed in
+    # split over several work-groups (fp32 partial tiles in the workspace, summed in
     # slice order by a second launch).  Full Llama-3-8B shapes, sampled
     # columns against the oracle, and a second call bit for bit equal.
     rng = np.random.Generator(np.random.PCG64(700 + m))
@@ -374,7 +388,7 @@ def test_linear_split_k_full_size_sampled(P, m):
         xc = S.activations(64, k, 702 + k, S.outlier_channels(k, 0.01, 703), 20.0)
         s16 = O.scale_candidate(O.calib_stats(xc), alpha)
         inv = O.fp16_rn(1.0 / s16.astype(np.float64))
-        qw, sc, qz, _ = P.awq_pack_int4(dev(w), dev(s16), g=128)
+        (qw, sc, qz), (hq, hs, hz) = oracle_pack(w, s16, 128)
         del w
         x = S.activations(m, k, 704 + m + k, S.outlier_channels(k, 0.01, 703), 20.0)
         y = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=128)
@@ -382,7 +396,7 @@ def test_linear_split_k_full_size_sampled(P, m):
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
         cols = np.unique(np.concatenate([rng.choice(n, 96, replace=False), np.arange(n - 8, n)]))
-        yr = O.linear_ref_rows(x, host_u32(qw), sc.cpu().numpy(), host_u32(qz), inv, k, 128, cols)
+        yr = O.linear_ref_rows(x, hq, hs, hz, inv, k, 128, cols)
         ok, worst, raw = O.check_linear(host16(y)[:, cols], yr)
         assert ok, (m, n, k, worst, raw)
 
@@ -401,15 +415,18 @@ def test_linear_gemm_long_k_small_groups(P, m, k, g):
 
 
 def test_linear_split_k_graph_replays(P):
-    # a captured split-K call (GEMM launch + slice-sum launch over scratch
+    # a captured split-K call (GEMM launch + slice-sum launch over workspace
     # partials) replayed several times, with eager calls of other sizes in
-    # between that reuse the same scratch: every replay matches the eager result
+    # between that reuse the same workspace: every replay matches the eager result
     k, n, m = 4096, 1024, 64
     w = S.weights(n, k, 0.02, 710)
     qw, sc, qz, _ = P.awq_pack_int4(dev(w), None, g=128)
     x = dev(S.activations(m, k, 711, S.outlier_channels(k, 0.01, 712), 20.0))
     x_other = dev(S.activations(40, k, 713, S.outlier_channels(k, 0.01, 712), 20.0))
-    y_eager = P.awq_linear_w4a16(x, qw, sc, qz, None, g=128)
+    need = max(P.awq_linear_workspace_size(m, n, k, 128), P.awq_linear_workspace_size(40, n, k, 128))
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    y_eager = P.awq_linear_w4a16(x, qw, sc, qz, None, g=128, workspace=ws)
     torch.cuda.synchronize()
     out = torch.empty_like(y_eager)
     stream = torch.cuda.Stream()
@@ -417,7 +434,7 @@ def test_linear_split_k_graph_replays(P):
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(gr, stream=stream):
-            P.awq_linear_w4a16(x, qw, sc, qz, None, g=128, out=out)
+            P.awq_linear_w4a16(x, qw, sc, qz, None, g=128, out=out, workspace=ws)
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     for i in range(4):
@@ -425,7 +442,7 @@ def test_linear_split_k_graph_replays(P):
         gr.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), y_eager.view(torch.int16)), i
-        y_mid = P.awq_linear_w4a16(x_other, qw, sc, qz, None, g=128)
+        y_mid = P.awq_linear_w4a16(x_other, qw, sc, qz, None, g=128, workspace=ws)
         torch.cuda.synchronize()
         assert bool(torch.isfinite(y_mid).all())
 
@@ -448,23 +465,23 @@ def _group_case(P, m, k, g, specs, seed):
             xc = S.activations(64, k, sd + 1, S.outlier_channels(k, 0.01, sd + 2), 20.0)
             s16 = O.scale_candidate(O.calib_stats(xc), alpha)
             inv = O.fp16_rn(1.0 / s16.astype(np.float64))
-        qw, sc, qz, _ = P.awq_pack_int4(dev(w), None if s16 is None else dev(s16), g=g)
+        (qw, sc, qz), host = oracle_pack(w, s16, g)
         del w
         x_d, x_h = xs[i % 2]
         inv_d = None if inv is None else dev(inv)
         items.append((x_d, qw, sc, qz, inv_d, None))
-        meta.append((x_d, x_h, qw, sc, qz, inv, inv_d))
+        meta.append((x_d, x_h, qw, sc, qz, inv, inv_d, host))
     return items, meta
 
 
 def _check_group(P, items, meta, k, g, cols_per=None):
     ys = P.awq_linear_w4a16_group(items, g=g)
-    for y, (x_d, x_h, qw, sc, qz, inv, inv_d) in zip(ys, meta):
+    for y, (x_d, x_h, qw, sc, qz, inv, inv_d, host) in zip(ys, meta):
         y1 = P.awq_linear_w4a16(x_d, qw, sc, qz, inv_d, g=g)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
         n = qw.shape[0]
-        hq, hs, hz = host_u32(qw), sc.cpu().numpy(), host_u32(qz)
+        hq, hs, hz = host
         if cols_per is None or n <= cols_per:
             yr = O.linear_ref(x_h, hq, hs, hz, inv, k, g)
             ok, worst, raw = O.check_linear(host16(y), yr)
@@ -563,18 +580,22 @@ def test_shared_scale_stacked_qkv_full_size(P):
     gfold = P.awq_fold_inv_scale(dev(gamma), s16)
     torch.cuda.synchronize()
     assert np.array_equal(gfold.cpu().numpy().view(np.uint16), O.fold_inv_scale(gamma, s16h).view(np.uint16))
-    x_tilde = O.fp16_rn(x_run.astype(np.float64) * gfold.cpu().numpy().astype(np.float64)[None, :])
-    qw, sc, qz, _ = P.awq_pack_int4(wd, s16, g=128)
+    # the linear runs on the oracle's fold and the oracle's pack of the stack
+    x_tilde = O.fp16_rn(x_run.astype(np.float64) *
+                        O.fold_inv_scale(gamma, s16_want).astype(np.float64)[None, :])
+    (qw, sc, qz), (hq, hs, hz) = oracle_pack(wst, s16_want, 128)
     y = P.awq_linear_w4a16(dev(x_tilde), qw, sc, qz, None, g=128)
     torch.cuda.synchronize()
     cols = np.unique(np.concatenate([r.choice(6144, 192, replace=False), np.arange(4090, 4100), np.arange(6136, 6144)]))
-    ci = torch.from_numpy(cols).to(DEV)
-    yr = O.linear_ref(x_tilde, host_u32(qw[ci]), sc[ci].cpu().numpy(), host_u32(qz[ci]), None, 4096, 128)
-    ok, worst, raw = O.check_linear(host16(y[:, ci]), yr)
+    yr = O.linear_ref(x_tilde, hq[cols], hs[cols], hz[cols], None, 4096, 128)
+    ok, worst, raw = O.check_linear(host16(y)[:, cols], yr)
     assert ok, (worst, raw)
-    # the packed rows of the stack are the oracle's pack at the shared s
-    oq, osc, oz = O.pack_int4(wst[rows[::8]], s16h, 128)[:3]
-    assert np.array_equal(host_u32(qw[torch.from_numpy(rows[::8]).to(DEV)]), oq)
+    # the GPU pack of the stack at the shared s is the oracle's pack
+    gq, gs, gz, _ = P.awq_pack_int4(wd, s16, g=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u32(gq), hq)
+    assert np.array_equal(gs.cpu().numpy().view(np.uint16), hs.view(np.uint16))
+    assert np.array_equal(host_u32(gz), hz)
 
 
 def test_fold_inv_scale_rows_bit_exact(P):

@@ -11,6 +11,7 @@ import pytest
 
 import synthetic as S
 from oracle import awq_oracle as O
+from tests import search_bound as SB
 
 pytestmark = pytest.mark.gpu
 
@@ -128,28 +129,19 @@ def test_pack_wbit_4_is_pack_int4(P):
 
 
 def _check_search(P, w, x, g, n_grid, w_bit):
-    max_int = (1 << w_bit) - 1
     a_dev = P.awq_calib_stats(dev(x))
     best, s16, inv, losses = P.awq_search_scale_wbit(dev(w), dev(x), a_dev, g=g, n_grid=n_grid,
                                                      w_bit=w_bit)
     torch.cuda.synchronize()
     a = O.calib_stats(x)
     ob, os16, oinv, olosses = O.search_scale(w, x, a, g=g, n_grid=n_grid, w_bit=w_bit)
-    gl = losses.cpu().numpy()
-    fin = np.isfinite(olosses)
-    assert np.array_equal(np.isfinite(gl), fin)
-    # the same accumulation bound as the 4-bit search: per output the kernel's
-    # error is at most gamma * sum_k |dW X| with gamma below 1e-5
-    gamma = 1e-5
-    xa = np.abs(x.astype(np.float64))
-    for i in np.flatnonzero(fin):
-        s_i = O.scale_candidate(a, i / n_grid)
-        deq = O.fake_quantize(w, s_i, g, max_int)[5]
-        dw = deq / s_i.astype(np.float64)[None, :] - w.astype(np.float64)
-        sabs = float(np.sum((np.abs(dw) @ xa.T) ** 2))
-        bound = 2 * gamma * np.sqrt(olosses[i] * sabs) + gamma * gamma * sabs
-        assert abs(gl[i] - olosses[i]) <= bound, (i, gl[i], olosses[i], bound)
-    assert int(best.item()) == ob
+    # the bound of the 4-bit search (the same kernel; tests/search_bound.py)
+    dnorm = SB.loss_bounds(w, x, a, g, n_grid, w_bit)
+    worst = SB.check_losses(losses.cpu().numpy(), olosses, dnorm)
+    b, second, gap, margin = SB.gap_report(olosses, dnorm)
+    print(f"search gap [w_bit {w_bit} {w.shape} m={x.shape[0]} g={g}]: best {ob} second {second} "
+          f"gap {gap:.3e} margin {margin:.3g} max rel loss err {worst:.2e}")
+    assert int(best.item()) == ob, (int(best.item()), ob, gap, margin)
     assert np.array_equal(u16(s16), os16.view(np.uint16))
     assert np.array_equal(u16(inv), oinv.view(np.uint16))
     return ob
@@ -203,12 +195,13 @@ def test_search_wbit_fewer_bits_lose_more(P):
 
 
 def _check_linear(P, w, x, s16, g, w_bit, cols=None):
+    """GPU linear on the oracle's pack (uploaded) against the oracle."""
     inv = None if s16 is None else O.fp16_rn(1.0 / s16.astype(np.float64))
-    qw, sc, qz, _ = P.awq_pack_wbit(dev(w), None if s16 is None else dev(s16), g=g, w_bit=w_bit)
+    hq, hs, hz, _ = O.pack_weights(w, s16, g, w_bit)
+    qw, sc, qz = dev(hq.view(np.int32)), dev(hs), dev(hz.view(np.int32))
     y = P.awq_linear_wbit(dev(x), qw, sc, qz, None if inv is None else dev(inv), g=g, w_bit=w_bit)
     torch.cuda.synchronize()
     k = w.shape[1]
-    hq, hs, hz = u32(qw), sc.cpu().numpy(), u32(qz)
     yh = y.cpu().numpy().astype(np.float16)
     if cols is None:
         yr = O.linear_ref(x, hq, hs, hz, inv, k, g, w_bit)
@@ -248,6 +241,30 @@ def test_linear_wbit_decode_full_size(P, w_bit, name, n, k):
     w, x_cal, x_run, _ = S.config_layer(2, name, n, k, 128, 1, 0.02, 0.01, 20.0)
     s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
     _check_linear(P, w, x_run, s16, 128, w_bit)
+
+
+@pytest.mark.parametrize("w_bit", [3, 8])
+@pytest.mark.parametrize("name,n,k", [("gate", 14336, 4096), ("down", 4096, 14336)])
+def test_linear_wbit_32_tokens_full_size_sampled(P, w_bit, name, n, k):
+    # 17-32 tokens run the tiled GEMM with 64-row tiles, split along K (two
+    # work-groups per CU of K slices for down, K >= 8192): full Llama-3-8B
+    # gate and down shapes at 24 and 32 tokens on sampled columns
+    w, x_cal, _, _ = S.config_layer(2, name, n, k, 128, 0, 0.02, 0.01, 20.0)
+    s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
+    inv = O.fp16_rn(1.0 / s16.astype(np.float64))
+    hq, hs, hz, _ = O.pack_weights(w, s16, 128, w_bit)
+    del w
+    qw, sc, qz = dev(hq.view(np.int32)), dev(hs), dev(hz.view(np.int32))
+    rng = np.random.Generator(np.random.PCG64(1480 + n + w_bit))
+    cols = np.unique(np.concatenate([rng.choice(n, 128, replace=False), np.arange(n - 8, n)]))
+    ch = S.outlier_channels(k, 0.01, S.seed_of(2, 0, S.SLOTS[S.INPUT_OF[name]], 3))
+    for m in (24, 32):
+        x = S.activations(m, k, 1481 + m, ch, 20.0)
+        y = P.awq_linear_wbit(dev(x), qw, sc, qz, dev(inv), g=128, w_bit=w_bit)
+        torch.cuda.synchronize()
+        yr = O.linear_ref_rows(x, hq, hs, hz, inv, k, 128, cols, w_bit)
+        ok, worst, raw = O.check_linear(y.cpu().numpy()[:, cols], yr)
+        assert ok, (m, worst, raw)
 
 
 @pytest.mark.parametrize("w_bit", [3, 8])
