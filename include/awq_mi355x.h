@@ -394,6 +394,30 @@ awq_status awq_linear_w4a16_group(const awq_linear_item* items, int32_t count,
                                   size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * awq_linear_w4a16_group_noalloc -- awq_linear_w4a16_group without a
+ * workspace and without any allocation, for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses that
+ * forbid allocation.
+ *
+ *   Arguments, results (bit for bit), limits and errors: those of
+ *   awq_linear_w4a16_group, with the scratch taken from a device array of the
+ *   library, awq_linear_noalloc_scratch_bytes() = 64 MiB per GPU, held by each
+ *   GPU the library runs on until the process ends.  A call whose plan needs
+ *   more (awq_linear_group_workspace_size) returns AWQ_ERR_WORKSPACE before
+ *   any launch: decode calls (m <= 32) need little or none, prefill of the
+ *   Llama-3-8B-shaped groups fits; larger prefill calls take the workspace
+ *   form.  The first call on a device takes the array's device address
+ *   (hipGetSymbolAddress), which allocates nothing.
+ *   Every call on one GPU uses the same array and leaves its contents behind
+ *   (nothing in it needs to start at zero): calls that overlap on one GPU
+ *   (concurrent streams, or host threads) race on it and must be serialised
+ *   by the caller.
+ * ------------------------------------------------------------------------- */
+size_t awq_linear_noalloc_scratch_bytes(void);
+awq_status awq_linear_w4a16_group_noalloc(const awq_linear_item* items, int32_t count,
+                                          int64_t m, int64_t k, int32_t g, void* stream);
+
+/* ---------------------------------------------------------------------------
  * awq_linear_w4a16_bf16, awq_linear_w4a16_group_bf16 -- the 4-bit linear and
  * its group call with bf16 activations: x and y hold bf16 bit patterns.
  * Passage: jsqmd.com page, section 二.1 (3) and bjdmk.com.cn page, section

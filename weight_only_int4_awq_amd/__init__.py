@@ -27,7 +27,7 @@ __all__ = ["awq_calib_stats", "awq_search_workspace_size", "awq_search_scale", "
            "awq_search_scale_wbit", "awq_pack_wbit", "awq_linear_wbit", "packed_shapes",
            "awq_linear_w4a16_bf16", "awq_linear_w4a16_group_bf16",
            "awq_salient_channels", "awq_channel_mask", "awq_gather_channels", "awq_mixed_loss",
-           "awq_linear_mixed", "awq_fold_inv_scale_rows",
+           "awq_linear_mixed", "awq_fold_inv_scale_rows", "awq_linear_w4a16_group_noalloc",
            "AWQError", "load"]
 
 
@@ -390,6 +390,35 @@ def _linear_group(items, g, bf, workspace):
     st = getattr(_lib.load(), fn)(arr, len(items), m, k, g, wp, wb, _stream())
     _lib.check(fn, st)
     return outs
+
+
+def awq_linear_w4a16_group_noalloc(items, g=128):
+    """awq_linear_w4a16_group without a workspace: the library's static device
+    scratch (awq_linear_noalloc_scratch_bytes() per GPU) serves the call, and
+    nothing is allocated by the library or here (the outputs must be given).
+    Calls that overlap on one GPU share that scratch and must be serialised."""
+    torch = _torch()
+    if not 1 <= len(items) <= 4:
+        raise ValueError("a group holds 1 to 4 linears")
+    arr = (_lib.LinearItem * len(items))()
+    m = k = None
+    for i, (x, qweight, scales, qzeros, inv_s16, out) in enumerate(items):
+        _dev_tensor(x, torch.float16, "x", 2)
+        if out is None:
+            raise ValueError("the no-allocation call needs every output given")
+        mi, ki = x.shape
+        if m is None:
+            m, k = mi, ki
+        elif (mi, ki) != (m, k):
+            raise ValueError("the linears of a group must share m and k")
+        n = qweight.shape[0]
+        _out_tensor(out, torch.float16, (m, n), "y")
+        a = arr[i]
+        a.x, a.inv_s16, a.qweight = _ptr(x), _ptr(inv_s16), _ptr(qweight)
+        a.scales, a.qzeros, a.y, a.n = _ptr(scales), _ptr(qzeros), _ptr(out), n
+    st = _lib.load().awq_linear_w4a16_group_noalloc(arr, len(items), m, k, g, _stream())
+    _lib.check("awq_linear_w4a16_group_noalloc", st)
+    return [it[5] for it in items]
 
 
 # ---------------------------------------------------------------- mixed-precision baseline

@@ -71,6 +71,9 @@ SIGNATURES["awq_linear_mixed"] = (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, 
                                             C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,
                                             C.c_void_p])
 SIGNATURES["awq_linear_w4a16_group_bf16"] = SIGNATURES["awq_linear_w4a16_group"]
+SIGNATURES["awq_linear_noalloc_scratch_bytes"] = (C.c_size_t, [])
+SIGNATURES["awq_linear_w4a16_group_noalloc"] = (C.c_int, [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                                          C.c_int32, C.c_void_p])
 
 _lib = None
 

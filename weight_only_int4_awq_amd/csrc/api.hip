@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/awq_mi355x.h"
 #include "awq_common.h"
 #include "awq_internal.h"
@@ -448,6 +450,84 @@ awq_status awq_linear_mixed(const uint16_t* x, const uint32_t* qweight, const ui
   if (st != AWQ_OK) return st;
   hipError_t e = awq::launch_salient_add(x, idx, count, w_s, m, n, k, y, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "awq_linear_mixed launch");
+  return AWQ_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no allocation
+// awq_linear_w4a16_group_noalloc: the group call with its device scratch in a
+// file-scope device array instead of a caller workspace, for callers that
+// cannot allocate (code under graph capture, tight serving loops, harnesses
+// that forbid allocation).  Each GPU the library runs on holds its own copy of
+// the array until the process ends.  In host code the array's name is only a
+// host-side stand-in: its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept per device; that
+// address, never the name, is what the kernels receive.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// the device address of `scratch` on the current device
+awq_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(AWQ_ERR_UNSUPPORTED, "awq_linear_w4a16_group_noalloc: device index %lld out of range", dev);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "awq_linear_w4a16_group_noalloc: hipGetSymbolAddress");
+    if (ptr == nullptr)
+      return fail(AWQ_ERR_HIP, "awq_linear_w4a16_group_noalloc: no device address for the scratch array");
+    g_noalloc_ptr[dev] = ptr;
+  }
+  *out = g_noalloc_ptr[dev];
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t awq_linear_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+awq_status awq_linear_w4a16_group_noalloc(const awq_linear_item* items, int32_t count, int64_t m,
+                                          int64_t k, int32_t g, void* stream) {
+  const char* fn = "awq_linear_w4a16_group_noalloc";
+  g_err[0] = 0;
+  if (!items) return fail(AWQ_ERR_NULL, "awq_linear_w4a16_group_noalloc: null items");
+  if (count < 1 || count > awq::kGroupMax)
+    return fail(AWQ_ERR_SHAPE, "awq_linear_w4a16_group_noalloc: count=%lld outside 1..%lld", count,
+                awq::kGroupMax);
+  awq::LinItem li[awq::kGroupMax];
+  for (int32_t i = 0; i < count; ++i) {
+    const awq_linear_item& it = items[i];
+    awq_status st = check_linear_args(fn, it.x, it.qweight, it.scales, it.qzeros, it.inv_s16, m, it.n,
+                                      k, g, it.y);
+    if (st != AWQ_OK) return st;
+    li[i] = awq::LinItem{it.x, it.inv_s16, it.qweight, it.scales, it.qzeros, it.y, it.n};
+  }
+  const size_t need = awq::linear_group_scratch_bytes(li, count, m, k, g);
+  if (need > kNoallocScratchBytes)
+    return fail(AWQ_ERR_WORKSPACE,
+                "awq_linear_w4a16_group_noalloc: the call needs %lld scratch bytes, beyond the %lld of the "
+                "static scratch (use awq_linear_w4a16_group with a workspace)",
+                (long long)need, (long long)kNoallocScratchBytes);
+  void* ptr = nullptr;
+  awq_status st = noalloc_scratch(&ptr);
+  if (st != AWQ_OK) return st;
+  awq::Scratch scr;
+  scr.base = static_cast<char*>(ptr);
+  hipError_t e = awq::launch_linear_group(li, count, m, k, g, scr, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
   return AWQ_OK;
 }
 
