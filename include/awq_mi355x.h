@@ -298,7 +298,7 @@ awq_status awq_pack_wbit(const uint16_t* w, const uint16_t* s16, int64_t n,
  *   17 tokens a tiled GEMM (x * inv_s16 staged in the workspace, and fp32
  *   partial tiles there where the linear is split along K).
  *   x [m][k] fp16, qweight and inv_s16 [k] fp16 (or NULL) 16-byte aligned;
- *   qzeros 4-byte aligned, scales 2-byte aligned; y [m][n] fp16 out.
+ *   scales and qzeros 4-byte aligned; y [m][n] fp16 out.
  *   workspace: awq_linear_wbit_workspace_size(m, n, k, g, w_bit,
  *            inv_s16 != NULL) bytes, 256-byte aligned (NULL if that is 0).
  *   Limits: g in {32, 64, 128}; k % g == 0; k % 64 == 0; 1 <= m, n
@@ -326,7 +326,8 @@ awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight,
  *   5e-3 * max(|y_ref|, rms of the row of y_ref) per output.
  *   x        [m][k] fp16, 16-byte aligned;  inv_s16 [k] fp16 or NULL,
  *            16-byte aligned;  qweight/scales/qzeros in layout v1
- *            (awq_pack_int4), qweight 16-byte aligned;  y [m][n] fp16 out.
+ *            (awq_pack_int4), qweight 16-byte aligned, scales and qzeros
+ *            4-byte aligned;  y [m][n] fp16 out.
  *   workspace: device scratch of awq_linear_workspace_size(m, n, k, g)
  *            bytes, 256-byte aligned, owned by the caller (NULL when the
  *            size is 0); contents on entry are ignored.

@@ -158,6 +158,8 @@ def test_linear_argument_errors(lib):
     assert call(n=0) == 2
     assert call(x=MISALIGNED) == 3
     assert call(qw=FAKE + 4) == 3
+    # scales are read as 32-bit words of two groups
+    assert call(sc=FAKE + 2) == 3
     # inv_s16 is read with 16-byte loads
     assert call(inv=FAKE + 2) == 3
     assert call(inv=FAKE + 8) == 3

@@ -197,7 +197,8 @@ awq_status check_linear_args(const char* fn, const uint16_t* x, const uint32_t* 
     snprintf(g_err, sizeof(g_err), "%s: x, inv_s16 and qweight must be 16-byte aligned", fn);
     return AWQ_ERR_ALIGN;
   }
-  if (!aligned(scales, 2) || !aligned(qzeros, 4) || !aligned(y, 2)) {
+  // scales are read as 32-bit words of two groups by the prefill GEMM
+  if (!aligned(scales, 4) || !aligned(qzeros, 4) || !aligned(y, 2)) {
     snprintf(g_err, sizeof(g_err), "%s: misaligned pointer", fn);
     return AWQ_ERR_ALIGN;
   }

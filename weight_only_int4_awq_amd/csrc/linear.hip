@@ -1444,16 +1444,16 @@ size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
          (size_t)nb * tc * 64 * 16;
 }
 
-// ---------------------------------------------------------------- prefill GEMM
-// Work-group tile 256 tokens x 128 output columns, K-step 64, 4 waves in a
-// 2 x 2 arrangement, each wave 128 x 64 = 4 x 2 blocks of
-// v_mfma_f32_32x32x16_f16 (fp32 accumulators); for few tokens a 64 x 128
-// tile, 4 waves side by side along N, each 64 x 32 = 2 x 1 blocks.
+// ---------------------------------------------------------------- prefill GEMM, 33-128 tokens
+// Work-group tile 64 tokens x 128 output columns, K-step 64, 4 waves side by
+// side along N, each 64 x 32 = 2 x 1 blocks of v_mfma_f32_32x32x16_f16 (fp32
+// accumulators).  Also taken beyond 128 tokens where a column has an odd
+// number of groups (the 128-row kernel below copies scales in pairs).
 //  * A (activations): linear_xprep first writes x_tilde = fp16(x * inv_s)
 //    once per call, every 8-channel chunk permuted into the nibble-unpack
-//    slot order.  Each K-step the work-group copies its 256 x 64 tile straight
+//    slot order.  Each K-step the work-group copies its 64 x 64 tile straight
 //    from global memory into one of two LDS stages (global_load_lds, 16 bytes
-//    per lane; 16-byte chunks XOR-swizzled by row, so the 16 lanes served per
+//    per lane; 16-byte chunks XOR-swizzled by row, so the lanes served per
 //    LDS cycle hit distinct banks).
 //  * B (weights) never touches LDS: lane (column j, half c) of a wave loads
 //    the 4 qweight words of its column for the K-step directly (one 16-byte
@@ -1466,7 +1466,7 @@ size_t skinny_fused_lds_bytes(int64_t k, int32_t g, int nb, int tc) {
 //  * Scales and zero words of the work-group's 128 columns are staged in LDS
 //    once.  The next K-step's global loads are in flight while the current
 //    one is multiplied.
-constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 64;
+constexpr int kGemmBM = 64, kGemmBN = 128, kGemmBK = 64;
 constexpr int kGemmSRow = kGemmBN + 2, kGemmZRow = kGemmBN + 1;   // padded LDS rows
 
 // dynamic LDS of the GEMM (the two activation stages are static): the
@@ -1484,12 +1484,20 @@ static int gemm_slice_groups(int64_t k, int32_t g, int ks) {
   const int64_t steps = (nk + ks - 1) / ks;
   return (int)((steps * kGemmBK + g - 1) / g + 1);
 }
-static size_t gemm_static_lds(int bm) { return (size_t)2 * bm * kGemmBK * 2; }
+// the 128-row kernel: tile, stages of its copy ring and their bytes (x_tilde,
+// packed words, scale and zero words)
+constexpr int kG2BM = 128, kG2BN = 256, kG2Stages = 3;
+constexpr int kG2AStage = kG2BM * kGemmBK * 2;
+constexpr int kG2BStage = kG2BN * 32;
+constexpr int kG2Stage = kG2AStage + kG2BStage + 2 * kG2BN * 4;
+static size_t gemm_static_lds(int bm) {
+  return bm == 64 ? (size_t)2 * bm * kGemmBK * 2 : (size_t)kG2Stages * kG2Stage;
+}
 
 // rows of one GEMM launch: its x_tilde stays below 2^31 bytes
 static int64_t gemm_row_chunk(int64_t k) {
-  const int64_t c = (((int64_t)1 << 31) / (k * 2)) / kGemmBM * kGemmBM;
-  return c > 0 ? c : kGemmBM;
+  const int64_t c = (((int64_t)1 << 31) / (k * 2)) / kG2BM * kG2BM;
+  return c > 0 ? c : kG2BM;
 }
 
 #ifndef AWQ_GEMM_SMALL_M
@@ -1498,25 +1506,30 @@ static int64_t gemm_row_chunk(int64_t k) {
 #ifndef AWQ_GEMM_SPLIT_TARGET
 #define AWQ_GEMM_SPLIT_TARGET 256
 #endif
-// tile rows: 64 for few tokens (the 256-row tile would be mostly padding)
-static int gemm_bm(int64_t m) { return m <= AWQ_GEMM_SMALL_M ? 64 : kGemmBM; }
+// tile rows: 64 for few tokens (64 x 128 tiles), else 128 (128 x 256 tiles;
+// the 128-row kernel copies the scales as 32-bit words of two groups, so it
+// needs an even number of groups per column)
+static int gemm_bm(int64_t m, int64_t k, int32_t g) {
+  return (m <= AWQ_GEMM_SMALL_M || (k / g) % 2 != 0) ? 64 : kG2BM;
+}
+static int gemm_bn(int bm) { return bm == 64 ? kGemmBN : kG2BN; }
 
 // Slices of K per tile for a linear whose tiles alone leave CUs idle: enough
 // slices for one work-group per CU (two for 64-row tiles where K >= 8192: a
 // long tile K loop runs one K-step ahead and stalls on its loads, and a
 // second resident work-group per CU hides that; measured at 24-128 tokens,
 // down 30 -> 25.5 us, 70B-shaped down 79 -> 58 us, while at K = 4096 and with
-// 256-row tiles the extra partial tiles cost more), at least two K-steps
+// 128 x 256 tiles the extra partial tiles cost more), at least two K-steps
 // each, at most 16.
 // With 64-row tiles (m <= 128) whenever the linear has fewer tiles than CUs;
-// with 256-row tiles up to 512 tokens and 64 tiles, or 128 tiles where K >=
-// 8192 makes a tile's K loop long (beyond that the partial tiles' round trip
-// costs more than the idle CUs: measured on the Llama-shaped linears).  A
-// property of the linear alone, so a group call computes every linear exactly
-// as a call of it alone.
-static int gemm_split_occupancy(int64_t m, int64_t n, int64_t k) {
-  const int bm = gemm_bm(m);
-  const int64_t tiles = ((m + bm - 1) / bm) * ((n + kGemmBN - 1) / kGemmBN);
+// with 128 x 256 tiles up to 512 tokens and 64 tiles, or 128 tiles where
+// K >= 8192 makes a tile's K loop long (beyond that the partial tiles' round
+// trip costs more than the idle CUs: measured on the Llama-shaped linears with
+// tiles of the same area, 256 x 128).  A property of the linear alone, so a
+// group call computes every linear exactly as a call of it alone.
+static int gemm_split_occupancy(int64_t m, int64_t n, int64_t k, int32_t g) {
+  const int bm = gemm_bm(m, k, g), bn = gemm_bn(bm);
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
   if (m > gemm_row_chunk(k) || tiles >= AWQ_GEMM_SPLIT_TARGET) return 1;
   if (bm != 64 && (m > 512 || tiles > 128 || (tiles > 64 && k < 8192))) return 1;
   const int64_t nk = k / kGemmBK;
@@ -1526,26 +1539,28 @@ static int gemm_split_occupancy(int64_t m, int64_t n, int64_t k) {
   sk = sk < smax ? sk : smax;
   return sk > 1 ? (int)sk : 1;
 }
-// Also split where the scales and zero words of a tile's whole K range would
-// not fit LDS (long K with small groups: K / g beyond about 300); 0 when that
-// would need a split and the call's activations are too large for one launch.
+// With 64-row tiles also split where the scales and zero words of a tile's
+// whole K range would not fit LDS (long K with small groups: K / g beyond
+// about 300; the 128-row kernel keeps them in registers); 0 when that would
+// need a split and the call's activations are too large for one launch.
 static int gemm_split(int64_t m, int64_t n, int64_t k, int32_t g) {
-  int sk = gemm_split_occupancy(m, n, k);
+  int sk = gemm_split_occupancy(m, n, k, g);
   const int64_t nk = k / kGemmBK;
-  const size_t budget = (size_t)160 * 1024 - gemm_static_lds(gemm_bm(m));
-  while (gemm_lds_bytes(gemm_slice_groups(k, g, sk)) > budget && sk < nk) ++sk;
+  const int bm = gemm_bm(m, k, g);
+  const size_t budget = (size_t)160 * 1024 - gemm_static_lds(bm);
+  while (bm == 64 && gemm_lds_bytes(gemm_slice_groups(k, g, sk)) > budget && sk < nk) ++sk;
   if (sk > 1 && m > gemm_row_chunk(k)) return 0;
   return sk;
 }
 
-// fp32 partial tiles of a split linear: [tile][slice][min(m, 256) rows][128]
+// fp32 partial tiles of a split linear: [tile][slice][min(m, BM) rows][BN]
 static size_t gemm_part_bytes(int64_t m, int64_t n, int64_t k, int32_t g) {
   const int sk = gemm_split(m, n, k, g);
   if (sk <= 1) return 0;
-  const int bm = gemm_bm(m);
-  const int64_t tiles = ((m + bm - 1) / bm) * ((n + kGemmBN - 1) / kGemmBN);
+  const int bm = gemm_bm(m, k, g), bn = gemm_bn(bm);
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
   const int64_t rows_t = m < bm ? m : bm;
-  return align256((size_t)sk * (size_t)tiles * (size_t)rows_t * kGemmBN * 4);
+  return align256((size_t)sk * (size_t)tiles * (size_t)rows_t * bn * 4);
 }
 #ifndef AWQ_GEMM_SWZ_SHIFT
 #define AWQ_GEMM_SWZ_SHIFT 1
@@ -1590,17 +1605,16 @@ __global__ __launch_bounds__(256) void linear_xprep_kernel(const LinGroup gp, in
   }
 }
 
-template <int G, int BM>
+template <int G>
 __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, int64_t m,
                                                              int64_t k, int tiles_m) {
-  // BM = 256: waves 2 (M) x 2 (N), each 128 x 64 = 4 x 2 blocks of 32 x 32;
-  // BM = 64 (few tokens): waves 1 x 4, each 64 x 32 = 2 x 1 blocks
-  constexpr int WM = BM == 256 ? 2 : 1;
+  // waves 1 (M) x 4 (N), each 64 x 32 = 2 x 1 blocks of 32 x 32
+  constexpr int BM = kGemmBM;
+  constexpr int WM = 1;
   constexpr int WN = 4 / WM;
   constexpr int RW = BM / WM, CW = kGemmBN / WN;    // rows and columns per wave
   constexpr int BMB = RW / 32, BNB = CW / 32;       // 32 x 32 blocks per wave
   constexpr int AR = BM / 32;                       // A copy instructions per wave (8 rows each)
-  static_assert(BM == 256 || BM == 64, "tile rows");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // two distinct stage objects: the compiler can see that the copies into one
   // stage never alias the fragment reads of the other, so it does not wait for
@@ -1829,11 +1843,386 @@ __global__ __launch_bounds__(256, 2) void linear_gemm_kernel(const LinGroup gp, 
       }
 }
 
+// ---------------------------------------------------------------- prefill GEMM, m > 128
+// Work-group tile 128 tokens x 256 output columns, K-step 64, 4 waves side by
+// side along N, each wave 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_f16.
+// Against a 256 x 128 tile in a 2 x 2 wave arrangement the same MFMA work
+// reads 26 instead of 40 KB per K-step (16 KB of activations, 8 KB of packed
+// weights loaded once, 2 KB of scales and zero words) and every column is
+// dequantized by one wave only.
+//  * Every global load of the K loop is a 16- or 4-byte global -> LDS copy
+//    into a ring of three stages, issued two K-steps ahead, so that a copy has
+//    two K-steps of MFMA work to land.  A stage holds the x_tilde tile (rows
+//    of 64 channels, chunks XOR-swizzled by row as in the 64-row kernel), the
+//    packed words of the 256 columns (two 16-byte chunks per column, swapped
+//    on every other column quad so that 8 lanes reading 8 columns hit 32
+//    distinct banks), and per column the 32-bit word holding the step's fp16
+//    scale (with its neighbour group) and the zero word.
+//  * The copies are inline asm: the compiler neither sees nor waits for them.
+//    Per K-step one explicit wait and one barrier: the wave's own copies of
+//    the step have landed (those of the next step stay in flight), then every
+//    wave's copies are visible and no wave still reads the stage the next
+//    copies overwrite.  Every K-step issues the same copies (past the last
+//    step they repeat it), so the wait count is a constant.
+//  * Dequantization as in the 64-row kernel, the scale and zero point formed
+//    as fp16 pairs straight from their bits.
+// Needs 4-byte aligned scales and an even number of groups per column (the
+// scale words); the host takes the 64-row kernel otherwise.
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// lane i copies 16 (resp. 4) bytes from sbase + voff (sbase wave-uniform, in
+// SGPRs; voff the lane's 32-bit byte offset) to LDS bytes lds_base + 16 i
+// (resp. 4 i); no output register, the caller waits with an explicit vmcnt
+__device__ __forceinline__ void g2_copy16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void g2_copy4(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+#define AWQ_G2_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory")
+// A work-group barrier without the memory fence of __syncthreads (which
+// waits for every outstanding global load, the look-ahead included); the
+// empty statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void g2_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int G, int KG>
+__global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void linear_gemm2_kernel(const LinGroup gp, int64_t m,
+                                                                                 int64_t k, int tiles_m) {
+  constexpr int BM = kG2BM, BN = kG2BN, BK = kGemmBK;
+  constexpr int BMB = BM / 32, BNB = 2;               // 32 x 32 blocks per wave
+  constexpr int AR = BM / 32;                         // A copies per wave and step (8 rows each)
+  constexpr int kCopiesPerStep = AR + 2 + 2;          // + 2 KB of packed words, scale and zero words
+  static_assert(kG2Stages == 3 && BN == 4 * 64, "three stages, four waves of 64 columns");
+  static_assert(KG == 1 || KG == 2, "one or two K groups");
+  // stage s, K group g: bytes (s KG + g) kG2Stage ..
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kG2Stages * KG * kG2Stage];
+  const int ng = (int)(k / G), nzw = (ng + 7) / 8;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kgrp = wave >> 2, wv = wave & 3;          // K group, wave within the group
+  // XCD-aware tile order (as in the 64-row kernel): M fastest within an XCD
+  const int total = gp.wg0[gp.count];
+  const int bid = blockIdx.x;
+  const int per = total / 8, rem = total % 8;
+  const int xcd = bid % 8, slot = bid / 8;
+  const int tile = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const LinPick L = pick_linear_at(gp, tile);
+  uint16_t* __restrict__ y = L.y;
+  const int64_t n = L.n;
+  const int ks = L.ks;
+  const int tl = L.bid / ks, sl = L.bid - tl * ks;
+  const int tm = tl % tiles_m, tn = tl / tiles_m;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t kw_row = k / 8;
+  const int nk = (int)(k / BK);
+  const int kt0 = (int)((int64_t)sl * nk / ks), kt1 = (int)((int64_t)(sl + 1) * nk / ks);
+  // round P: K group g multiplies K-step kt0 + KG P + g
+  const int nr = (kt1 - kt0 + KG - 1) / KG;
+
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(&ring[0]) + (uint32_t)(kgrp * kG2Stage);
+  const unsigned char* ring_g = ring + kgrp * kG2Stage;
+  // ---- copy sources: a wave-uniform base per K-step (SGPRs) plus the lane's
+  // fixed 32-bit byte offset (x_tilde of one launch and the packed tensors of
+  // one linear stay below 2^31 resp. 2^32 bytes).
+  // A: wave w of a K group copies rows 32 w .. 32 w + 31 of the tile, lane
+  // (row r = 8 i + lane / 8, slot p = lane % 8) the logical chunk
+  // p ^ swizzle(r), so that lane i fills LDS slot i.
+  const int a_lr = lane >> 3, a_p = lane & 7;
+  uint32_t a_voff[AR];
+#pragma unroll
+  for (int i = 0; i < AR; ++i) {
+    const int lrow = wv * (BM / 4) + 8 * i + a_lr;
+    int64_t row = m0 + lrow;
+    row = row < m ? row : m - 1;
+    a_voff[i] = (uint32_t)((row * k + (a_p ^ ((lrow >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 8) * 2);
+  }
+  // B: wave w copies the 32-byte K-step slices of columns 64 w .. 64 w + 63,
+  // two per copy instruction: lane i fills slot i of column 32 h + i / 2,
+  // taking chunk (i % 2) ^ (bit 2 of the column)
+  uint32_t b_voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lcol = wv * 64 + 32 * h + (lane >> 1);
+    int64_t col = n0 + lcol;
+    col = col < n ? col : n - 1;
+    b_voff[h] = (uint32_t)(col * kw_row * 4 + (((lane & 1) ^ ((lcol >> 2) & 1)) * 16));
+  }
+  // scale and zero words: lane i of wave w, column 64 w + i
+  int64_t sz_col = n0 + wv * 64 + lane;
+  sz_col = sz_col < n ? sz_col : n - 1;
+  const uint32_t s_voff = (uint32_t)(sz_col * ng * 2), z_voff = (uint32_t)(sz_col * nzw * 4);
+  const char* xb = reinterpret_cast<const char*>(L.x);
+  const char* qb = reinterpret_cast<const char*>(L.qw);
+  const char* sb = reinterpret_cast<const char*>(L.sc);
+  const char* zb = reinterpret_cast<const char*>(L.qz);
+  // the copies of the K group's K-step of round P (clamped to the slice's
+  // last step) into stage ST
+#define AWQ_G2_LOAD(P, ST)                                                               \
+  {                                                                                     \
+    int kt_ = kt0 + KG * (P) + kgrp;                                                    \
+    kt_ = kt_ < kt1 ? kt_ : kt1 - 1;                                                    \
+    const uint32_t st_ = ring_lds + (uint32_t)((ST) * KG * kG2Stage);                   \
+    const char* xk_ = xb + (int64_t)kt_ * BK * 2;                                       \
+    _Pragma("unroll") for (int i = 0; i < AR; ++i)                                      \
+      g2_copy16(a_voff[i], xk_, st_ + (uint32_t)((wv * (BM / 4) + 8 * i) * 128));       \
+    const char* qk_ = qb + (int64_t)kt_ * 32;                                           \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h)                                       \
+      g2_copy16(b_voff[h], qk_, st_ + (uint32_t)(kG2AStage + (wv * 64 + 32 * h) * 32));  \
+    const int g0_ = (kt_ * BK) / G;                                                     \
+    g2_copy4(s_voff, sb + (int64_t)(g0_ & ~1) * 2,                                      \
+             st_ + (uint32_t)(kG2AStage + kG2BStage + wv * 256));                       \
+    g2_copy4(z_voff, zb + (int64_t)(g0_ >> 3) * 4,                                      \
+             st_ + (uint32_t)(kG2AStage + kG2BStage + BN * 4 + wv * 256));              \
+  }
+
+  floatx16_t acc[BMB][BNB];
+#pragma unroll
+  for (int i = 0; i < BMB; ++i)
+#pragma unroll
+    for (int jj = 0; jj < BNB; ++jj) acc[i][jj] = floatx16_t{};
+  const UnpackConsts uc = unpack_consts();
+  // ---- fragment reads.  A: byte offset of lane's fragment of row block bm at
+  // sub-step 0 (row bm 32 + lane % 32, logical chunk 4 (lane / 32) + s stored
+  // at chunk ^ swizzle(row); s flips chunk bits 0-1 only)
+  const int bj = lane & 31, bc = lane >> 5;
+  uint32_t a_base[BMB];
+#pragma unroll
+  for (int bm = 0; bm < BMB; ++bm) {
+    const int row = bm * 32 + bj;
+    a_base[bm] = (uint32_t)(row * 128 + ((4 * bc) ^ ((row >> AWQ_GEMM_SWZ_SHIFT) & 7)) * 16);
+  }
+  // B: lane (column j, half c) of block bn reads the 4 words 4c .. 4c + 3 of
+  // column 64 w + 32 bn + j; scale and zero words of that column
+  uint32_t b_off[BNB], s_off[BNB], z_off[BNB];
+#pragma unroll
+  for (int bn = 0; bn < BNB; ++bn) {
+    const int lcol = wv * 64 + bn * 32 + bj;
+    b_off[bn] = (uint32_t)(kG2AStage + lcol * 32 + ((bc ^ ((lcol >> 2) & 1)) * 16));
+    s_off[bn] = (uint32_t)(kG2AStage + kG2BStage + lcol * 4);
+    z_off[bn] = (uint32_t)(kG2AStage + kG2BStage + BN * 4 + lcol * 4);
+  }
+
+  // The operands a wave copied itself (the packed words, scale and zero words
+  // of its own 64 columns) need only its own wait, not the barrier: they are
+  // read from LDS, and the step's scale and zero point formed as fp16 pairs
+  // (d, d), (-1024 - z) and (-64 - z) straight from their bits, at the end of
+  // the previous round, so that after the barrier only the shared activation
+  // fragments stand between the wave and its first MFMA.
+  struct BSet {
+    uint4 wb[BNB];
+    half2_t dd[BNB], o1024[BNB], o64[BNB];
+  };
+#define AWQ_G2_PREP(P, ST, R)                                                            \
+  {                                                                                     \
+    const unsigned char* p_ = ring_g + (ST) * KG * kG2Stage;                            \
+    const int grp_ = ((kt0 + KG * (P) + kgrp) * BK + 32 * bc) / G;                      \
+    _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) {                                \
+      R.wb[bn] = *reinterpret_cast<const uint4*>(p_ + b_off[bn]);                       \
+      const uint32_t sw_ = *reinterpret_cast<const uint32_t*>(p_ + s_off[bn]);          \
+      const uint32_t zw_ = *reinterpret_cast<const uint32_t*>(p_ + z_off[bn]);          \
+      const uint32_t s_ = (sw_ >> (16 * (grp_ & 1))) & 0xFFFFu;                         \
+      const uint32_t z_ = (zw_ >> (4 * (grp_ & 7))) & 0xFu;                             \
+      R.dd[bn] = __builtin_bit_cast(half2_t, s_ | (s_ << 16));                          \
+      R.o1024[bn] = __builtin_bit_cast(half2_t, (0xE400u + z_) * 0x10001u);             \
+      R.o64[bn] = __builtin_bit_cast(half2_t, (0xD400u + (z_ << 4)) * 0x10001u);        \
+    }                                                                                   \
+  }
+  // dequantized B fragments of sub-step S (word S of each block) from R
+#define AWQ_G2_DQ(R, S, OUT)                                                             \
+  {                                                                                     \
+    _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) {                                \
+      const uint32_t wsel = (S) == 0 ? R.wb[bn].x : (S) == 1 ? R.wb[bn].y : (S) == 2 ? R.wb[bn].z : R.wb[bn].w; \
+      uint32_t u[4];                                                                    \
+      unpack_word(wsel, u, uc);                                                         \
+      const half2_t q0 = (__builtin_bit_cast(half2_t, u[0]) + R.o1024[bn]) * R.dd[bn];    \
+      const half2_t q1 = (__builtin_bit_cast(half2_t, u[1]) + R.o64[bn]) * R.dd[bn];      \
+      const half2_t q2 = (__builtin_bit_cast(half2_t, u[2]) + R.o1024[bn]) * R.dd[bn];    \
+      const half2_t q3 = (__builtin_bit_cast(half2_t, u[3]) + R.o64[bn]) * R.dd[bn];      \
+      OUT[bn] = __builtin_bit_cast(                                                     \
+          half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1), \
+                              __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3))); \
+    }                                                                                   \
+  }
+  // Round P (stage ST, weights in R, the B fragments of its first sub-step in
+  // bq): meet (every wave has its copies of P), then four 16-channel
+  // sub-steps as in the 64-row kernel.  Each sub-step's MFMAs run while the
+  // B fragments of the next are dequantized; the copies of round P + 2 go
+  // into the stage round P - 1 used once the first sub-step's MFMAs are
+  // issued; the last sub-step waits for the wave's own copies of round P + 1,
+  // prepares its weights into RN and dequantizes its first B fragments.  With
+  // two K groups the second has no K-step in the last round when the slice's
+  // step count is odd: it only copies and prepares.
+#define AWQ_G2_STEP(P, ST, STN, STP, R, RN)                                              \
+  {                                                                                     \
+    /* the previous round's work (the first B fragments of this one          */       \
+    /* included) is issued before the barrier, not after it                  */       \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    g2_barrier();                                                                       \
+    if (KG == 1 || kt0 + KG * (P) + kgrp < kt1) {                                       \
+      const unsigned char* cur_ = ring_g + (ST) * KG * kG2Stage;                        \
+      half8_t af[BMB];                                                                  \
+      _Pragma("unroll") for (int bm = 0; bm < BMB; ++bm)                                \
+        af[bm] = *reinterpret_cast<const half8_t*>(cur_ + a_base[bm]);                  \
+      _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                   \
+        half8_t bqn[BNB];                                                               \
+        if (s < 3) {                                                                    \
+          AWQ_G2_DQ(R, s + 1, bqn)                                                      \
+        } else {                                                                        \
+          AWQ_G2_WAIT_VMCNT(kCopiesPerStep);                                            \
+          AWQ_G2_PREP((P) + 1, STP, RN)                                                 \
+          AWQ_G2_DQ(RN, 0, bqn)                                                         \
+        }                                                                               \
+        _Pragma("unroll") for (int bm = 0; bm < BMB; ++bm) {                            \
+          _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn)                            \
+            acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[bm], bq[bn], acc[bm][bn], 0, 0, 0); \
+          if (s + 1 < 4)                                                                \
+            af[bm] = *reinterpret_cast<const half8_t*>(cur_ + (a_base[bm] ^ (uint32_t)(16 * (s + 1)))); \
+        }                                                                               \
+        if (s == 0) AWQ_G2_LOAD((P) + 2, STN)                                           \
+        _Pragma("unroll") for (int bn = 0; bn < BNB; ++bn) bq[bn] = bqn[bn];            \
+      }                                                                                 \
+    } else {                                                                            \
+      AWQ_G2_LOAD((P) + 2, STN)                                                         \
+      AWQ_G2_WAIT_VMCNT(kCopiesPerStep);                                                \
+      AWQ_G2_PREP((P) + 1, STP, RN)                                                     \
+      AWQ_G2_DQ(RN, 0, bq)                                                              \
+    }                                                                                   \
+  }
+  BSet r0, r1;
+  half8_t bq[BNB];
+  AWQ_G2_LOAD(0, 0)
+  AWQ_G2_LOAD(1, 1)
+  AWQ_G2_WAIT_VMCNT(kCopiesPerStep);
+  AWQ_G2_PREP(0, 0, r0)
+  AWQ_G2_DQ(r0, 0, bq)
+  int rp = 0;
+  for (; rp + 3 <= nr; rp += 3) {
+    AWQ_G2_STEP(rp, 0, 2, 1, r0, r1)
+    AWQ_G2_STEP(rp + 1, 1, 0, 2, r1, r0)
+    AWQ_G2_STEP(rp + 2, 2, 1, 0, r0, r1)
+    r0 = r1;
+  }
+  if (rp < nr) {
+    AWQ_G2_STEP(rp, 0, 2, 1, r0, r1)
+    r0 = r1;
+  }
+  if (rp + 1 < nr) {
+    AWQ_G2_STEP(rp + 1, 1, 0, 2, r0, r1)
+  }
+  AWQ_G2_WAIT_VMCNT(0);               // the look-ahead copies have landed before the wave ends
+#undef AWQ_G2_STEP
+#undef AWQ_G2_DQ
+#undef AWQ_G2_PREP
+#undef AWQ_G2_LOAD
+
+  // ---- two K groups: the second hands its sums to the first through LDS
+  // (element-major, 16 bytes per lane: consecutive lanes, consecutive bytes)
+  if constexpr (KG == 2) {
+    g2_barrier();                     // every copy landed, every fragment read done
+    float* red = reinterpret_cast<float*>(ring) + wv * (BMB * BNB * 16 * 64);
+    if (kgrp == 1) {
+#pragma unroll
+      for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < BNB; ++bn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(red + (((bm * BNB + bn) * 4 + q) * 64 + lane) * 4) =
+                make_float4(acc[bm][bn][4 * q], acc[bm][bn][4 * q + 1], acc[bm][bn][4 * q + 2],
+                            acc[bm][bn][4 * q + 3]);
+    }
+    g2_barrier();
+    if (kgrp == 1) return;
+#pragma unroll
+    for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < BNB; ++bn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(red + (((bm * BNB + bn) * 4 + q) * 64 + lane) * 4);
+          acc[bm][bn][4 * q] += v.x;
+          acc[bm][bn][4 * q + 1] += v.y;
+          acc[bm][bn][4 * q + 2] += v.z;
+          acc[bm][bn][4 * q + 3] += v.w;
+        }
+  }
+
+  // ---- epilogue: value e of lane l in block (bm, bn) is row 8(e/4) + 4(l/32) + e%4, column l%32
+  if (ks == 1) {
+    if (n % 8 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+      // through LDS (free once every wave's copies have landed and its last
+      // fragments are read; with two K groups each wave reuses its own part
+      // of the hand-over area, already read): the wave's 128 x 64 outputs
+      // into rows of 72 halves (the two lane halves of a write land 16 banks
+      // apart), read back as 16-byte row chunks and stored 8 lanes per row
+      constexpr int ER = 72;
+      if constexpr (KG == 1) g2_barrier();
+      uint16_t* ep = reinterpret_cast<uint16_t*>(ring) + wv * (KG == 1 ? BM * ER : BMB * BNB * 16 * 64 * 2);
+#pragma unroll
+      for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < BNB; ++bn)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int row = bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+            ep[row * ER + bn * 32 + (lane & 31)] = f2act(acc[bm][bn][e], gp.bf != 0);
+          }
+#pragma unroll
+      for (int i = 0; i < BM / 8; ++i) {
+        const int row = 8 * i + (lane >> 3), c8 = (lane & 7) * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + row * ER + c8);
+        const int64_t t = m0 + row, cidx = n0 + wv * 64 + c8;
+        if (t < m && cidx < n) *reinterpret_cast<uint4*>(y + t * n + cidx) = v;
+      }
+    } else {
+#pragma unroll
+      for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < BNB; ++bn)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t t = m0 + bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+            const int64_t cidx = n0 + wv * 64 + bn * 32 + (lane & 31);
+            if (t < m && cidx < n) y[t * n + cidx] = f2act(acc[bm][bn][e], gp.bf != 0);
+          }
+    }
+    return;
+  }
+  // split along K: the fp32 partial tile (its valid rows) goes to slice sl
+  const int rows_t = m < BM ? (int)m : BM;
+  const int mrow = (m - m0) < rows_t ? (int)(m - m0) : rows_t;
+  float* __restrict__ part = L.part + ((size_t)tl * ks + sl) * rows_t * BN;
+#pragma unroll
+  for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < BNB; ++bn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = bm * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
+        const int col = wv * 64 + bn * 32 + (lane & 31);
+        const float v = acc[bm][bn][e];
+        if (row < mrow) part[row * BN + col] = v;
+      }
+}
+
 // Sums the K slices of the split linears of a GEMM launch (linear
 // blockIdx.y; a linear that was not split has no work here): every thread
 // takes 4 adjacent columns of one row of one tile and adds the slices in
 // slice order, all slice loads of a batch of 8 in flight together.
-template <int BM>
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void linear_gemm_reduce_kernel(const LinGroup gp, int64_t m,
                                                                  int tiles_m) {
   int li = 0;
@@ -1846,17 +2235,17 @@ __global__ __launch_bounds__(256) void linear_gemm_reduce_kernel(const LinGroup 
   const float* __restrict__ part = gp.part[li];
   uint16_t* __restrict__ y = gp.y[li];
   const int rows_t = m < BM ? (int)m : BM;
-  const int tiles = tiles_m * (int)((n + kGemmBN - 1) / kGemmBN);
-  const int64_t chunks = (int64_t)tiles * rows_t * (kGemmBN / 4);
-  const size_t slice_floats = (size_t)rows_t * kGemmBN;
+  const int tiles = tiles_m * (int)((n + BN - 1) / BN);
+  const int64_t chunks = (int64_t)tiles * rows_t * (BN / 4);
+  const size_t slice_floats = (size_t)rows_t * BN;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * 256) {
-    const int tl = (int)(c / ((int64_t)rows_t * (kGemmBN / 4)));
-    const int w = (int)(c - (int64_t)tl * rows_t * (kGemmBN / 4));
-    const int row = w / (kGemmBN / 4), c4 = (w - row * (kGemmBN / 4)) * 4;
+    const int tl = (int)(c / ((int64_t)rows_t * (BN / 4)));
+    const int w = (int)(c - (int64_t)tl * rows_t * (BN / 4));
+    const int row = w / (BN / 4), c4 = (w - row * (BN / 4)) * 4;
     const int tm = tl % tiles_m, tn = tl / tiles_m;
-    const int64_t t = (int64_t)tm * BM + row, col = (int64_t)tn * kGemmBN + c4;
+    const int64_t t = (int64_t)tm * BM + row, col = (int64_t)tn * BN + c4;
     if (t >= m) continue;
-    const float* src = part + (size_t)tl * ks * slice_floats + (size_t)row * kGemmBN + c4;
+    const float* src = part + (size_t)tl * ks * slice_floats + (size_t)row * BN + c4;
     float sum[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < ks; s0 += 8) {
       float4 v[8];
@@ -2048,7 +2437,7 @@ static bool skinny_wide(const LinItem& it, int64_t m, int64_t k) {
 template <int G>
 static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, int64_t k,
                                     Scratch& scr, hipStream_t stream) {
-  const int bm = gemm_bm(m);
+  const int bm = gemm_bm(m, k, G), bn = gemm_bn(bm);
   const int64_t chunk = gemm_row_chunk(k);
   const bool whole = m <= chunk;
   // slices of every linear (one when the call runs in row chunks), and the
@@ -2060,10 +2449,11 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
     const int gl = gemm_slice_groups(k, G, sks[l]);
     gmax = gmax > gl ? gmax : gl;
   }
-  const size_t lds = gemm_lds_bytes(gmax);
+  // dynamic LDS: the scales and zero words of the 64-row kernel (the 128-row
+  // kernel has only its static stages)
+  const size_t lds = bm == 64 ? gemm_lds_bytes(gmax) : 0;
   const size_t lds_static = gemm_static_lds(bm);
-  const void* fn = bm == 64 ? reinterpret_cast<const void*>(&linear_gemm_kernel<G, 64>)
-                            : reinterpret_cast<const void*>(&linear_gemm_kernel<G, kGemmBM>);
+  const void* fn = reinterpret_cast<const void*>(&linear_gemm_kernel<G>);
   if (lds + lds_static > 160 * 1024) return hipErrorInvalidValue;
   // scratch: one x_tilde slot per linear and the fp32 partial tiles of the
   // split linears (whole m in one launch), else slot 0 reused linear by linear
@@ -2074,7 +2464,7 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
       if (sks[l] > 1) scratch_bytes += gemm_part_bytes(m, items[l].n, k, G);
   char* const scratch = scr.at(0, scratch_bytes);
   if (scr.dry) return hipSuccess;
-  if (lds + lds_static > 65536) {
+  if (bm == 64 && lds + lds_static > 65536) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
@@ -2097,48 +2487,73 @@ static hipError_t launch_gemm_group(const LinItem* items, int count, int64_t m, 
     for (int64_t r0 = 0; r0 < m; r0 += chunk) {
       const int64_t mc = (m - r0) < chunk ? (m - r0) : chunk;
       const int tiles_m = (int)((mc + bm - 1) / bm);
-      LinGroup gg = {};
-      int total = 0;
-      bool split = false;
+      // the work-groups of every linear and, for the 128-row kernel, its
+      // K groups: two where the linear, not split along K, has at most one
+      // work-group per CU (a property of the linear, so that a group call
+      // gives the bits of the single calls; linears of both kinds take one
+      // launch per kind).  A split linear has work-groups enough for two per
+      // CU, and so has a group of them.
+      int wgs[kGroupMax], kgs[kGroupMax];
+      char* parts[kGroupMax];
       char* part = scratch + (size_t)cnt * slot_bytes;
       for (int l = 0; l < cnt; ++l) {
-        const int64_t n = its[l].n;
-        gg.x[l] = xg.y[l] + r0 * k;
-        gg.qw[l] = its[l].qw;
-        gg.sc[l] = its[l].sc;
-        gg.qz[l] = its[l].qz;
-        gg.y[l] = its[l].y + r0 * n;
-        gg.n[l] = n;
-        gg.wg0[l] = total;
         // split along K only where the whole m is one launch (mc == m)
         const int sk = whole ? sks[l] : 1;
-        gg.ks[l] = sk;
+        wgs[l] = tiles_m * (int)((its[l].n + bn - 1) / bn) * sk;
+        kgs[l] = (bm != 64 && sk == 1 && wgs[l] <= kGemvCUs) ? 2 : 1;
+        parts[l] = nullptr;
         if (sk > 1) {
-          gg.part[l] = reinterpret_cast<float*>(part);
-          part += gemm_part_bytes(m, n, k, G);
-          split = true;
+          parts[l] = part;
+          part += gemm_part_bytes(m, its[l].n, k, G);
         }
-        total += tiles_m * (int)((n + kGemmBN - 1) / kGemmBN) * sk;
       }
-      for (int l = cnt; l <= kGroupMax; ++l) gg.wg0[l] = total;
-      gg.count = cnt;
-      gg.bf = its[0].bf;
-      gg.gmax = gmax;
-      if (bm == 64)
-        hipLaunchKernelGGL((linear_gemm_kernel<G, 64>), dim3((unsigned)total), dim3(256), lds, stream,
-                           gg, mc, k, tiles_m);
-      else
-        hipLaunchKernelGGL((linear_gemm_kernel<G, kGemmBM>), dim3((unsigned)total), dim3(256), lds,
-                           stream, gg, mc, k, tiles_m);
-      if (split) {
-        // the slices of every split linear (a few MB of fp32 partials, still
-        // in the caches): a grid over the chip per linear
-        const dim3 rg(256u, (unsigned)cnt);
+      for (int kg = 1; kg <= 2; ++kg) {
+        LinGroup gg = {};
+        int total = 0, c = 0;
+        bool split = false;
+        for (int l = 0; l < cnt; ++l) {
+          if (kgs[l] != kg) continue;
+          const int64_t n = its[l].n;
+          gg.x[c] = xg.y[l] + r0 * k;
+          gg.qw[c] = its[l].qw;
+          gg.sc[c] = its[l].sc;
+          gg.qz[c] = its[l].qz;
+          gg.y[c] = its[l].y + r0 * n;
+          gg.n[c] = n;
+          gg.wg0[c] = total;
+          gg.ks[c] = whole ? sks[l] : 1;
+          if (parts[l]) {
+            gg.part[c] = reinterpret_cast<float*>(parts[l]);
+            split = true;
+          }
+          total += wgs[l];
+          ++c;
+        }
+        if (c == 0) continue;
+        for (int l = c; l <= kGroupMax; ++l) gg.wg0[l] = total;
+        gg.count = c;
+        gg.bf = its[0].bf;
+        gg.gmax = gmax;
         if (bm == 64)
-          hipLaunchKernelGGL((linear_gemm_reduce_kernel<64>), rg, dim3(256), 0, stream, gg, mc, tiles_m);
+          hipLaunchKernelGGL((linear_gemm_kernel<G>), dim3((unsigned)total), dim3(256), lds, stream,
+                             gg, mc, k, tiles_m);
+        else if (kg == 2)
+          hipLaunchKernelGGL((linear_gemm2_kernel<G, 2>), dim3((unsigned)total), dim3(512), 0, stream,
+                             gg, mc, k, tiles_m);
         else
-          hipLaunchKernelGGL((linear_gemm_reduce_kernel<kGemmBM>), rg, dim3(256), 0, stream, gg, mc,
-                             tiles_m);
+          hipLaunchKernelGGL((linear_gemm2_kernel<G, 1>), dim3((unsigned)total), dim3(256), 0, stream,
+                             gg, mc, k, tiles_m);
+        if (split) {
+          // the slices of every split linear (a few MB of fp32 partials, still
+          // in the caches): a grid over the chip per linear
+          const dim3 rg(256u, (unsigned)c);
+          if (bm == 64)
+            hipLaunchKernelGGL((linear_gemm_reduce_kernel<64, kGemmBN>), rg, dim3(256), 0, stream, gg, mc,
+                               tiles_m);
+          else
+            hipLaunchKernelGGL((linear_gemm_reduce_kernel<kG2BM, kG2BN>), rg, dim3(256), 0, stream, gg,
+                               mc, tiles_m);
+        }
       }
     }
   }
