@@ -190,13 +190,18 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   constexpr int KSTEPS = G / 16;      // MFMA k-steps per group (even)
   constexpr int TOK = 128 * NT;       // tokens per pass
   constexpr int WLD = EPT / 8;        // 16-byte weight loads per producer thread per group
-  constexpr int DWN = KSTEPS * kSearchRows * 16;   // halves per dW buffer
+  // LDS padding, so that the 8 lanes an LDS cycle serves hit distinct banks:
+  // a producer's 16-byte dW stores (lanes: 2 rows x 4 quarters) shift by 32
+  // bytes per quarter of the group; its scale reads (4 quarters, the rows
+  // broadcast) by 16 bytes per quarter, its reciprocal reads likewise
+  constexpr int CPQ = EPT / 8;                     // 8-channel chunks per quarter
+  constexpr int DWN = KSTEPS * kSearchRows * 16 + 3 * 16;   // halves per dW buffer
   __shared__ __attribute__((aligned(16))) uint16_t dh0[DWN];
   __shared__ __attribute__((aligned(16))) uint16_t dl0[DWN];
   __shared__ __attribute__((aligned(16))) uint16_t dh1[DWN];
   __shared__ __attribute__((aligned(16))) uint16_t dl1[DWN];
-  __shared__ __attribute__((aligned(16))) uint16_t s_l[2][G];     // candidate scales
-  __shared__ __attribute__((aligned(16))) float rc_l[2][G];       // c / s
+  __shared__ __attribute__((aligned(16))) uint16_t s_l[2][G + 3 * 8];     // candidate scales
+  __shared__ __attribute__((aligned(16))) float rc_l[2][G + 3 * 4];       // c / s
   __shared__ double red[4];
   // activation ring: [slot][wave][tile][lane][8 halves]
   constexpr int XSN = 4 * NT * 64 * 8;
@@ -238,9 +243,9 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   uint4 sn;                           // scales / reciprocals of the next group:
   float4 rn;                          // loaded at the top of an iteration, stored to LDS at its end
   auto store_sr = [&](int buf, const uint4& sv, const float4& rv) {
-    if (ptid < G / 8) *reinterpret_cast<uint4*>(&s_l[buf][8 * s_i]) = sv;
+    if (ptid < G / 8) *reinterpret_cast<uint4*>(&s_l[buf][8 * s_i + (8 * s_i / EPT) * 8]) = sv;
     if (ptid < G / 4)
-      *reinterpret_cast<float4*>(&rc_l[buf][4 * r_i]) =
+      *reinterpret_cast<float4*>(&rc_l[buf][4 * r_i + (4 * r_i / EPT) * 4]) =
           make_float4(rv.x * cscale, rv.y * cscale, rv.z * cscale, rv.w * cscale);
   };
 #define AWQ_LOAD_W(WV, J)                                                                   \
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     half2_t pmx = {(half_t)-__builtin_inff(), (half_t)-__builtin_inff()};                   \
     half2_t pmn = {(half_t)__builtin_inff(), (half_t)__builtin_inff()};                     \
     _Pragma("unroll") for (int q = 0; q < WLD; ++q) {                                       \
-      const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * EPT + 8 * q]);        \
+      const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * (EPT + 8) + 8 * q]); \
       const uint32_t wq4[4] = {WV[q].x, WV[q].y, WV[q].z, WV[q].w};                         \
       const uint32_t sq4[4] = {sv.x, sv.y, sv.z, sv.w};                                     \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
@@ -283,9 +288,9 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     const GroupQ gq = group_q(mx, mn, qmax);                                                \
     _Pragma("unroll") for (int q = 0; q < WLD; ++q) {                                       \
       __builtin_amdgcn_sched_barrier(0);                                                    \
-      const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * EPT + 8 * q]);        \
-      const float4 rc0 = *reinterpret_cast<const float4*>(&rc_l[SB][sub * EPT + 8 * q]);    \
-      const float4 rc1 = *reinterpret_cast<const float4*>(&rc_l[SB][sub * EPT + 8 * q + 4]); \
+      const uint4 sv = *reinterpret_cast<const uint4*>(&s_l[SB][sub * (EPT + 8) + 8 * q]); \
+      const float4 rc0 = *reinterpret_cast<const float4*>(&rc_l[SB][sub * (EPT + 4) + 8 * q]);     \
+      const float4 rc1 = *reinterpret_cast<const float4*>(&rc_l[SB][sub * (EPT + 4) + 8 * q + 4]); \
       const uint32_t wq4[4] = {WV[q].x, WV[q].y, WV[q].z, WV[q].w};                         \
       const uint32_t sq4[4] = {sv.x, sv.y, sv.z, sv.w};                                     \
       const float rcv[8] = {rc0.x, rc0.y, rc0.z, rc0.w, rc1.x, rc1.y, rc1.z, rc1.w};        \
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
         lw[i] = __builtin_bit_cast(uint32_t, lo);                                           \
       }                                                                                     \
       const int kloc = sub * EPT + 8 * q;                                                   \
-      const int off = ((kloc / 8) * kSearchRows + r) * 8;   /* [step][half][row][8] */     \
+      const int off = ((kloc / 8) * kSearchRows + r) * 8 + sub * 16;   /* [step][half][row][8] */ \
       *reinterpret_cast<uint4*>(&DH[off]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);         \
       *reinterpret_cast<uint4*>(&DL[off]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);         \
     }                                                                                       \
@@ -332,52 +337,65 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     _Pragma("unroll") for (int ti_ = 0; ti_ < NT; ++ti_)                                    \
       lds_copy16(xs_ + xoff[ti_], slot_ + (uint32_t)(ti_ * 64 * 16));                      \
   }
-  // stage 2 for group J from LDS buffers DH / DL; the last step loads the
-  // first fragments of group JN (KSTEPS is even: they land in buffer 0)
+  // stage 2 for group J from LDS buffers DH / DL.  Software-pipelined: the
+  // fragments of step s + 1 (dW from DH / DL, activations from the ring) are
+  // read while the MFMAs of step s run, so an MFMA waits on LDS only at the
+  // group's first step.  Ring slot (t + 3) % 4, filled at step t, held step
+  // t - 1, whose fragments were read at step t - 2.
 #define AWQ_CONSUME(J, DH, DL)                                                              \
   {                                                                                         \
+    half8_t fa_[4], fb_[NT];                                                                \
+    auto frags_ = [&](int s_, int t_, half8_t* a_, half8_t* b_) {                           \
+      const uint16_t* xsl_ = xring + (t_ % 4) * XSN;                                        \
+      const int ch_ = s_ * 2 + (lane >> 5);                                                 \
+      const int aoff0 = (ch_ * kSearchRows + (lane & 31)) * 8 + (ch_ / CPQ) * 16;           \
+      const int aoff1 = aoff0 + 32 * 8;                                                     \
+      a_[0] = *reinterpret_cast<const half8_t*>(&DH[aoff0]);                                \
+      a_[1] = *reinterpret_cast<const half8_t*>(&DH[aoff1]);                                \
+      a_[2] = *reinterpret_cast<const half8_t*>(&DL[aoff0]);                                \
+      a_[3] = *reinterpret_cast<const half8_t*>(&DL[aoff1]);                                \
+      _Pragma("unroll") for (int ti = 0; ti < NT; ++ti)                                     \
+        b_[ti] = *reinterpret_cast<const half8_t*>(xsl_ + ((wave * NT + ti) * 64 + lane) * 8); \
+    };                                                                                      \
+    /* copies of steps t .. t + 2 are in flight: wait for step t's */                      \
+    AWQ_WAIT_VMCNT(2 * NT);                                                                 \
+    frags_(0, (J) * KSTEPS, fa_, fb_);                                                      \
     _Pragma("unroll") for (int s = 0; s < KSTEPS; ++s) {                                    \
-      /* pass step t = J KSTEPS + s: copy step t + 3, then wait for step t's copies */      \
       const int t_ = (J) * KSTEPS + s;                                                      \
       AWQ_LOAD_X(t_ + 3)                                                                    \
-      AWQ_WAIT_VMCNT(3 * NT);                                                               \
-      const uint16_t* xsl_ = xring + (t_ % 4) * XSN;                                        \
-      const int aoff0 = ((s * 2 + (lane >> 5)) * kSearchRows + (lane & 31)) * 8;            \
-      const int aoff1 = aoff0 + 32 * 8;                                                     \
-      const half8_t ah0 = *reinterpret_cast<const half8_t*>(&DH[aoff0]);                    \
-      const half8_t al0 = *reinterpret_cast<const half8_t*>(&DL[aoff0]);                    \
-      const half8_t ah1 = *reinterpret_cast<const half8_t*>(&DH[aoff1]);                    \
-      const half8_t al1 = *reinterpret_cast<const half8_t*>(&DL[aoff1]);                    \
+      half8_t na_[4], nb_[NT];                                                              \
+      if (s + 1 < KSTEPS) {                                                                 \
+        AWQ_WAIT_VMCNT(2 * NT);       /* step t + 1's copies have landed */                 \
+        frags_(s + 1, t_ + 1, na_, nb_);                                                    \
+      }                                                                                     \
       _Pragma("unroll") for (int ti = 0; ti < NT; ++ti) {                                   \
-        const half8_t b = *reinterpret_cast<const half8_t*>(                                \
-            xsl_ + ((wave * NT + ti) * 64 + lane) * 8);                                     \
-        acc[0][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah0, b, acc[0][ti], 0, 0, 0);   \
-        acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah1, b, acc[1][ti], 0, 0, 0);   \
-        acc[0][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al0, b, acc[0][ti], 0, 0, 0);   \
-        acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al1, b, acc[1][ti], 0, 0, 0);   \
+        acc[0][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa_[0], fb_[ti], acc[0][ti], 0, 0, 0); \
+        acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa_[1], fb_[ti], acc[1][ti], 0, 0, 0); \
+        acc[0][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa_[2], fb_[ti], acc[0][ti], 0, 0, 0); \
+        acc[1][ti] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa_[3], fb_[ti], acc[1][ti], 0, 0, 0); \
+      }                                                                                     \
+      if (s + 1 < KSTEPS) {                                                                 \
+        _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) fa_[q_] = na_[q_];                 \
+        _Pragma("unroll") for (int ti = 0; ti < NT; ++ti) fb_[ti] = nb_[ti];                \
       }                                                                                     \
     }                                                                                       \
   }
 
-  // iteration I: producers quantize group I (weights CUR, scales buffer I%2,
+  // Iteration I: producers quantize group I (weights CUR, scales buffer I%2,
   // errors into dW buffer I%2) and load group I+1 into NXT; consumers multiply
-  // group I-1 from the other dW buffer.  PB is I%2, known statically.
-#define AWQ_STEP(I, PB, WCUR, WNXT, DHP, DLP, DHC, DLC)                                      \
+  // group I-1 from the other dW buffer.  PB is I%2, known statically.  The two
+  // roles run separate loops with the same barriers: in one shared loop the
+  // producers' weight loads, pending across the loop head, make the compiler
+  // wait for every outstanding load of the consumers too (their activation
+  // copies, three steps ahead) before it reuses a register.
+#define AWQ_PRODUCE_STEP(I, PB, WCUR, WNXT, DHP, DLP)                                        \
   {                                                                                         \
-    if (consumer) {                                                                         \
-      if ((I) >= 1) {                                                                       \
-        const int jc_ = (I) - 1;                                                            \
-        AWQ_CONSUME(jc_, DHC, DLC)                                                          \
-      }                                                                                     \
-    } else if ((I) < ng) {                                                                  \
-      const int jn_ = (I) + 1 < ng ? (I) + 1 : ng - 1;                                      \
-      AWQ_LOAD_SR(sn, rn, jn_)                                                              \
-      if constexpr (kWDouble) AWQ_LOAD_W(WNXT, jn_)                                         \
-      AWQ_PRODUCE(WCUR, PB, DHP, DLP)                                                       \
-      if constexpr (!kWDouble) AWQ_LOAD_W(WCUR, jn_)                                        \
-      store_sr((PB) ^ 1, sn, rn);                                                           \
-    }                                                                                       \
-    __syncthreads();                                                                        \
+    const int jn_ = (I) + 1 < ng ? (I) + 1 : ng - 1;                                        \
+    AWQ_LOAD_SR(sn, rn, jn_)                                                                \
+    if constexpr (kWDouble) AWQ_LOAD_W(WNXT, jn_)                                           \
+    AWQ_PRODUCE(WCUR, PB, DHP, DLP)                                                         \
+    if constexpr (!kWDouble) AWQ_LOAD_W(WCUR, jn_)                                          \
+    store_sr((PB) ^ 1, sn, rn);                                                             \
   }
 
   double loss = 0.0;
@@ -398,23 +416,16 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
       AWQ_LOAD_X(0)
       AWQ_LOAD_X(1)
       AWQ_LOAD_X(2)
-    } else {
-      AWQ_LOAD_W(wa, 0)
-      AWQ_LOAD_SR(sn, rn, 0)
-      store_sr(0, sn, rn);
-    }
-    __syncthreads();
-    for (int i = 0; i <= ng; i += 2) {
-      if constexpr (kWDouble) {
-        AWQ_STEP(i, 0, wa, wb, dh0, dl0, dh1, dl1)
-        if (i + 1 <= ng) AWQ_STEP(i + 1, 1, wb, wa, dh1, dl1, dh0, dl0)
-      } else {
-        AWQ_STEP(i, 0, wa, wa, dh0, dl0, dh1, dl1)
-        if (i + 1 <= ng) AWQ_STEP(i + 1, 1, wa, wa, dh1, dl1, dh0, dl0)
+      __syncthreads();
+      for (int i = 0; i <= ng; i += 2) {
+        if (i >= 1) AWQ_CONSUME(i - 1, dh1, dl1)
+        __syncthreads();
+        if (i + 1 <= ng) {
+          AWQ_CONSUME(i, dh0, dl0)
+          __syncthreads();
+        }
       }
-    }
-    // ---- square and reduce (float64, fixed order) over the valid tokens
-    if (consumer) {
+      // ---- square and reduce (float64, fixed order) over the valid tokens
       AWQ_WAIT_VMCNT(0);              // the ring's look-ahead copies have landed
       double sq = 0.0;
 #pragma unroll
@@ -433,12 +444,31 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sq += shfl_xor_d(sq, off);
       if (lane == 0) red[wave] = sq;
+    } else {
+      AWQ_LOAD_W(wa, 0)
+      AWQ_LOAD_SR(sn, rn, 0)
+      store_sr(0, sn, rn);
+      __syncthreads();
+      for (int i = 0; i <= ng; i += 2) {
+        if (i < ng) {
+          if constexpr (kWDouble) AWQ_PRODUCE_STEP(i, 0, wa, wb, dh0, dl0)
+          else AWQ_PRODUCE_STEP(i, 0, wa, wa, dh0, dl0)
+        }
+        __syncthreads();
+        if (i + 1 <= ng) {
+          if (i + 1 < ng) {
+            if constexpr (kWDouble) AWQ_PRODUCE_STEP(i + 1, 1, wb, wa, dh1, dl1)
+            else AWQ_PRODUCE_STEP(i + 1, 1, wa, wa, dh1, dl1)
+          }
+          __syncthreads();
+        }
+      }
     }
     __syncthreads();
     loss += ((red[0] + red[1]) + red[2]) + red[3];
     __syncthreads();
   }
-#undef AWQ_STEP
+#undef AWQ_PRODUCE_STEP
 #undef AWQ_CONSUME
 
 #undef AWQ_LOAD_X
