@@ -205,7 +205,9 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   __shared__ double red[4];
   // activation ring: [slot][wave][tile][lane][8 halves]
   constexpr int XSN = 4 * NT * 64 * 8;
-  __shared__ __attribute__((aligned(16))) uint16_t xring[4 * XSN];
+  // the global -> LDS copies write 64 lanes x 16 bytes from a base that
+  // must be aligned to that 1 KB (a 64-byte offset gave wrong data)
+  __shared__ __attribute__((aligned(1024))) uint16_t xring[4 * XSN];
 
   // XCD-aware order: consecutive logical ids (the alphas of one row block)
   // land on the same XCD, so they share W through that XCD's L2.
