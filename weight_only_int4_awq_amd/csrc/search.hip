@@ -147,6 +147,31 @@ __device__ __forceinline__ void lds_copy16(const void* gsrc, uint32_t lds_base) 
 // s_waitcnt on the vector memory counter only, as inline asm: the compiler
 // does not see the copies above and would drop a wait it thinks is idle.  The
 // memory clobber keeps the LDS reads that follow below it.
+// The producer's per-element arithmetic in the fewest instructions, each
+// result bit-identical to the plain float form:
+//  * the code of an fp16 w' takes w' straight into the quotient's fmas
+//    (v_fma_mix_f32 reads fp16 operands), as rne_quot and code_minus_zero do
+//    with a float w' (the two differ at most in the sign of a zero t1, which
+//    the following fmas turn into the same +0);
+//  * dw - hi for the fp16 hi half of a packed pair is one v_fma_mix_f32
+//    (-hi * 1 + dw, one rounding of the exact difference, as dw - (float)hi).
+__device__ __forceinline__ float code_minus_zero_h(half_t w, const GroupQ& gq) {
+  const float t1 = __builtin_fmaf((float)w, gq.rd, 0.0f);
+  const float r = __builtin_fmaf(-t1, gq.d, (float)w);
+  const float t = __builtin_rintf(__builtin_fmaf(r, gq.rd, t1));
+  return __builtin_fminf(__builtin_fmaxf(t, -gq.z), gq.qmax - gq.z);
+}
+__device__ __forceinline__ float sub_f16_lo(float dw, half2_t h) {
+  float o;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(o) : "v"(h), "v"(dw));
+  return o;
+}
+__device__ __forceinline__ float sub_f16_hi(float dw, half2_t h) {
+  float o;
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(o) : "v"(h), "v"(dw));
+  return o;
+}
+
 #define AWQ_WAIT_VMCNT(N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory")
 
 // Lane moves inside aligned groups of 4 lanes (DPP quad permutes).
@@ -157,12 +182,14 @@ __device__ __forceinline__ float dpp_mov(float v) {
 }
 
 // Work-group: 64 rows of W (two 32-row MFMA blocks) x one alpha x all tokens
-// in passes of 128 NT, as 8 waves in two roles that run concurrently on each
-// SIMD, one group of g channels apart:
-//  * producer waves 4..7 (stage 1): thread (row t/4, quarter t%4) fake-
-//    quantizes g/4 elements of group i: W' = fp16(W s) two at a time
-//    (v_pk_mul_f16), the group max/min two at a time and across the quad
-//    (DPP), then per element the exact code, deq = (q - z) D, the scaled error
+// in passes of 128 NT, as 4 + NP waves in two roles that run concurrently on
+// each SIMD, one group of g channels apart:
+//  * producer waves 4 .. 3 + NP (stage 1): thread (row t / NP, part t % NP)
+//    fake-quantizes g / NP elements of group i (eight producers where the
+//    tokens are few and quantizing a group would outlast its MFMAs): W' =
+//    fp16(W s) two at a time (v_pk_mul_f16), the group max/min two at a time
+//    and across the row's lanes (DPP), then per element the exact code,
+//    deq = (q - z) D, the scaled error
 //    dW c = (deq - W s)(c/s) and its fp16 split hi = rtz(dW c),
 //    lo = rtz(dW c - hi) (v_cvt_pkrtz, two at a time), stored in LDS buffer
 //    i % 2 in the MFMA A layout with 16-byte stores.  The next group's
@@ -180,31 +207,34 @@ __device__ __forceinline__ float dpp_mov(float v) {
 // (indices clamped), so the waits stay exact.  After the last group of a pass
 // the consumers square E in float64 over the valid tokens; fixed-order
 // reductions give one partial loss per (alpha, block).
-template <int G, int NT>
-__global__ __launch_bounds__(512, 1) void search_loss_kernel(
+template <int G, int NT, int NP>
+__global__ __launch_bounds__(64 * (4 + NP), 1) void search_loss_kernel(
     const uint16_t* __restrict__ w, const uint16_t* __restrict__ x, int64_t n, int64_t k,
     int64_t m, int32_t n_grid, int64_t n_blocks, const uint16_t* __restrict__ s16_all,
     const float* __restrict__ rs_all, const uint32_t* __restrict__ bmax, double* __restrict__ part,
     float qmax) {
-  constexpr int EPT = G / 4;          // elements of one row-group per producer thread
+  static_assert((NP == 4 || NP == 8) && G / NP >= 8, "four or eight producer waves");
+  constexpr int NC = 4;               // consumer waves
+  constexpr int EPT = G / NP;         // elements of one row-group per producer thread
   constexpr int KSTEPS = G / 16;      // MFMA k-steps per group (even)
-  constexpr int TOK = 128 * NT;       // tokens per pass
+  constexpr int TOK = 32 * NC * NT;   // tokens per pass
   constexpr int WLD = EPT / 8;        // 16-byte weight loads per producer thread per group
   // LDS padding, so that the 8 lanes an LDS cycle serves hit distinct banks:
   // a producer's 16-byte dW stores (lanes: 2 rows x 4 quarters) shift by 32
   // bytes per quarter of the group; its scale reads (4 quarters, the rows
   // broadcast) by 16 bytes per quarter, its reciprocal reads likewise
-  constexpr int CPQ = EPT / 8;                     // 8-channel chunks per quarter
-  constexpr int DWN = KSTEPS * kSearchRows * 16 + 3 * 16;   // halves per dW buffer
+  constexpr int CPQ = EPT / 8;                     // 8-channel chunks per part
+  constexpr int PADS = NP == 4 ? 16 : 8;           // dW pad (halves) per part of the group
+  constexpr int DWN = KSTEPS * kSearchRows * 16 + (NP - 1) * PADS;   // halves per dW buffer
   __shared__ __attribute__((aligned(16))) uint16_t dh0[DWN];
   __shared__ __attribute__((aligned(16))) uint16_t dl0[DWN];
   __shared__ __attribute__((aligned(16))) uint16_t dh1[DWN];
   __shared__ __attribute__((aligned(16))) uint16_t dl1[DWN];
-  __shared__ __attribute__((aligned(16))) uint16_t s_l[2][G + 3 * 8];     // candidate scales
-  __shared__ __attribute__((aligned(16))) float rc_l[2][G + 3 * 4];       // c / s
-  __shared__ double red[4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_l[2][G + (NP - 1) * 8];   // candidate scales
+  __shared__ __attribute__((aligned(16))) float rc_l[2][G + (NP - 1) * 4];     // c / s
+  __shared__ double red[NC];
   // activation ring: [slot][wave][tile][lane][8 halves]
-  constexpr int XSN = 4 * NT * 64 * 8;
+  constexpr int XSN = NC * NT * 64 * 8;
   // the global -> LDS copies write 64 lanes x 16 bytes from a base that
   // must be aligned to that 1 KB (a 64-byte offset gave wrong data)
   __shared__ __attribute__((aligned(1024))) uint16_t xring[4 * XSN];
@@ -225,17 +255,17 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool consumer = wave < 4;     // wave-uniform role
+  const bool consumer = wave < NC;    // wave-uniform role
   const float cscale = block_factor(bmax[rb]);
   const int ng = (int)(k / G);
 
   // ---- producer state
-  const int ptid = tid & 255;
-  const int r = ptid >> 2;            // row of the block this thread quantizes
-  const int sub = ptid & 3;           // which quarter of the group
+  const int ptid = tid - 64 * NC;     // producers are the last NP waves
+  const int r = ptid / NP;            // row of the block this thread quantizes
+  const int sub = ptid % NP;          // which part of the group
   const int64_t row = rb * kSearchRows + r;
   const bool row_ok = row < n;
-  const uint32_t row_mask = row_ok ? 0xFFFFFFFFu : 0u;    // rows past n contribute zero errors
+  // rows past n load row n - 1 and zero it: a zero row has zero errors
   const uint16_t* wrow = w + (row_ok ? row : n - 1) * k + sub * EPT;
   // scale / reciprocal staging: producer thread t loads halves 8 (t % (G/8))
   // of the scales and floats 4 (t % (G/4)) of the reciprocals (clamped: every
@@ -252,8 +282,10 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
   };
 #define AWQ_LOAD_W(WV, J)                                                                   \
   {                                                                                         \
-    _Pragma("unroll") for (int q_ = 0; q_ < WLD; ++q_)                                      \
-      WV[q_] = *reinterpret_cast<const uint4*>(wrow + (int64_t)(J) * G + 8 * q_);          \
+    _Pragma("unroll") for (int q_ = 0; q_ < WLD; ++q_) {                                    \
+      const uint4 v_ = *reinterpret_cast<const uint4*>(wrow + (int64_t)(J) * G + 8 * q_);  \
+      WV[q_] = row_ok ? v_ : make_uint4(0u, 0u, 0u, 0u);                                    \
+    }                                                                                       \
   }
 #define AWQ_LOAD_SR(SV, RV, J)                                                              \
   {                                                                                         \
@@ -287,6 +319,10 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     mn = __builtin_fminf(mn, dpp_mov<0xB1>(mn));                                            \
     mx = __builtin_fmaxf(mx, dpp_mov<0x4E>(mx));                                            \
     mn = __builtin_fminf(mn, dpp_mov<0x4E>(mn));                                            \
+    if constexpr (NP == 8) { /* the other quad of the row's 8 lanes (row_half_mirror) */    \
+      mx = __builtin_fmaxf(mx, dpp_mov<0x141>(mx));                                         \
+      mn = __builtin_fminf(mn, dpp_mov<0x141>(mn));                                         \
+    }                                                                                       \
     const GroupQ gq = group_q(mx, mn, qmax);                                                \
     _Pragma("unroll") for (int q = 0; q < WLD; ++q) {                                       \
       __builtin_amdgcn_sched_barrier(0);                                                    \
@@ -303,19 +339,18 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
         const half2_t wp = wv * sv2;                                                        \
         float dw[2];                                                                        \
         _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                     \
-          const float deq = code_minus_zero((float)wp[e], gq) * gq.d;                       \
-          const float wsx = __builtin_fmaf((float)wv[e], (float)sv2[e], 0.0f);              \
-          dw[e] = __builtin_bit_cast(                                                       \
-              float, __builtin_bit_cast(uint32_t, (deq - wsx) * rcv[2 * i + e]) & row_mask);   \
+          const float deq = code_minus_zero_h(wp[e], gq) * gq.d;                            \
+          /* deq - W s: the exact product, one rounding (v_fma_mix_f32) */                  \
+          dw[e] = __builtin_fmaf(-(float)wv[e], (float)sv2[e], deq) * rcv[2 * i + e];       \
         }                                                                                   \
         const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(dw[0], dw[1])); \
         const half2_t lo = __builtin_bit_cast(                                              \
-            half2_t, __builtin_amdgcn_cvt_pkrtz(dw[0] - (float)hi[0], dw[1] - (float)hi[1])); \
+            half2_t, __builtin_amdgcn_cvt_pkrtz(sub_f16_lo(dw[0], hi), sub_f16_hi(dw[1], hi))); \
         hw[i] = __builtin_bit_cast(uint32_t, hi);                                           \
         lw[i] = __builtin_bit_cast(uint32_t, lo);                                           \
       }                                                                                     \
       const int kloc = sub * EPT + 8 * q;                                                   \
-      const int off = ((kloc / 8) * kSearchRows + r) * 8 + sub * 16;   /* [step][half][row][8] */ \
+      const int off = ((kloc / 8) * kSearchRows + r) * 8 + sub * PADS; /* [step][half][row][8] */ \
       *reinterpret_cast<uint4*>(&DH[off]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);         \
       *reinterpret_cast<uint4*>(&DL[off]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);         \
     }                                                                                       \
@@ -350,7 +385,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
     auto frags_ = [&](int s_, int t_, half8_t* a_, half8_t* b_) {                           \
       const uint16_t* xsl_ = xring + (t_ % 4) * XSN;                                        \
       const int ch_ = s_ * 2 + (lane >> 5);                                                 \
-      const int aoff0 = (ch_ * kSearchRows + (lane & 31)) * 8 + (ch_ / CPQ) * 16;           \
+      const int aoff0 = (ch_ * kSearchRows + (lane & 31)) * 8 + (ch_ / CPQ) * PADS;         \
       const int aoff1 = aoff0 + 32 * 8;                                                     \
       a_[0] = *reinterpret_cast<const half8_t*>(&DH[aoff0]);                                \
       a_[1] = *reinterpret_cast<const half8_t*>(&DH[aoff1]);                                \
@@ -411,7 +446,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
       // past m are left out of the squares)
 #pragma unroll
       for (int ti = 0; ti < NT; ++ti) {
-        int64_t tok = t0 + (int64_t)(wave + 4 * ti) * 32 + (lane & 31);
+        int64_t tok = t0 + (int64_t)(wave + NC * ti) * 32 + (lane & 31);
         tok = tok < m ? tok : m - 1;
         xoff[ti] = (uint32_t)((tok * k + 8 * (lane >> 5)) * 2);
       }
@@ -432,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
       double sq = 0.0;
 #pragma unroll
       for (int ti = 0; ti < NT; ++ti) {
-        const int64_t tok = t0 + (int64_t)(wave + 4 * ti) * 32 + (lane & 31);
+        const int64_t tok = t0 + (int64_t)(wave + NC * ti) * 32 + (lane & 31);
         if (tok < m) {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
@@ -467,7 +502,10 @@ __global__ __launch_bounds__(512, 1) void search_loss_kernel(
       }
     }
     __syncthreads();
-    loss += ((red[0] + red[1]) + red[2]) + red[3];
+    double pass = red[0];
+#pragma unroll
+    for (int i = 1; i < NC; ++i) pass += red[i];
+    loss += pass;
     __syncthreads();
   }
 #undef AWQ_PRODUCE_STEP
@@ -545,20 +583,30 @@ hipError_t launch_search(const uint16_t* w, const uint16_t* x, const double* mea
                      dim3(256), 0, stream, w, n, k, bmax);
   const unsigned nwg = (unsigned)(L.n_blocks * n_grid);
   // token tiles per wave and pass: 128 NT tokens per pass
+  // token tiles per consumer wave and pass (128 NT tokens) and producer
+  // waves: up to 128 tokens, where quantizing a group takes longer than its
+  // MFMAs, eight producers (g >= 64), else four
   const int nt = m <= 128 ? 1 : (m <= 256 ? 2 : 4);
-#define AWQ_SEARCH_LAUNCH(GG, NTT)                                                              \
-  hipLaunchKernelGGL((search_loss_kernel<GG, NTT>), dim3(nwg), dim3(512), 0, stream, w, x, n, k, \
-                     m, n_grid, L.n_blocks, s16_all, rs_all, bmax, part, qmax)
-#define AWQ_SEARCH_NT(GG)                     \
-  switch (nt) {                               \
-    case 1: AWQ_SEARCH_LAUNCH(GG, 1); break;  \
-    case 2: AWQ_SEARCH_LAUNCH(GG, 2); break;  \
-    default: AWQ_SEARCH_LAUNCH(GG, 4); break; \
+  const bool np8 = m <= 128 && g >= 64;
+#define AWQ_SEARCH_LAUNCH(GG, NTT, NPP)                                                         \
+  hipLaunchKernelGGL((search_loss_kernel<GG, NTT, NPP>), dim3(nwg), dim3(64 * (4 + NPP)), 0,  \
+                     stream, w, x, n, k, m, n_grid, L.n_blocks, s16_all, rs_all, bmax, part, qmax)
+#define AWQ_SEARCH_NT(GG)                        \
+  switch (nt) {                                  \
+    case 1: AWQ_SEARCH_LAUNCH(GG, 1, 4); break;  \
+    case 2: AWQ_SEARCH_LAUNCH(GG, 2, 4); break;  \
+    default: AWQ_SEARCH_LAUNCH(GG, 4, 4); break; \
   }
   switch (g) {
     case 32: AWQ_SEARCH_NT(32); break;
-    case 64: AWQ_SEARCH_NT(64); break;
-    default: AWQ_SEARCH_NT(128); break;
+    case 64:
+      if (np8) AWQ_SEARCH_LAUNCH(64, 1, 8);
+      else AWQ_SEARCH_NT(64);
+      break;
+    default:
+      if (np8) AWQ_SEARCH_LAUNCH(128, 1, 8);
+      else AWQ_SEARCH_NT(128);
+      break;
   }
 #undef AWQ_SEARCH_NT
 #undef AWQ_SEARCH_LAUNCH
