@@ -346,6 +346,28 @@ def test_linear_decode_multiblock(P, n, k, g):
     _check_linear(P, w, x, s16, g)
 
 
+@pytest.mark.parametrize("n,k,g", [(8261, 256, 64), (12345, 2048, 32), (1024, 8192, 128), (20000, 4096, 64),
+                                   (3000, 4096, 128)])
+def test_linear_decode_rows_multiblock(P, n, k, g):
+    # the decode GEMV with token rows (2 <= m <= 8): several column blocks per
+    # work-group (up to four with two 8-wave work-groups per CU, up to eight
+    # with one 16-wave work-group: 20000 x 4096 at m = 8), a ragged last
+    # block, waves that own no group (k / g below the wave count), and at
+    # k = 8192 the activations alone filling most of LDS (one block per
+    # work-group)
+    w = S.weights(n, k, 0.02, 460 + n)
+    xc = S.activations(64, k, 463, S.outlier_channels(k, 0.01, 462), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.3)
+    inv = O.fp16_rn(1.0 / s16.astype(np.float64))
+    (qw, sc, qz), (hq, hs, hz) = oracle_pack(w, s16, g)
+    for m in (2, 5, 8):
+        x = S.activations(m, k, 461 + n + m, S.outlier_channels(k, 0.01, 462), 20.0)
+        y = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=g)
+        torch.cuda.synchronize()
+        ok, worst, raw = O.check_linear(host16(y), O.linear_ref(x, hq, hs, hz, inv, k, g))
+        assert ok, (m, worst, raw)
+
+
 def test_linear_packed_weights_at_4gib(P):
     # the largest packed weights a call takes (n k / 2 just below 4 GiB): the
     # decode kernels' 32-bit byte offsets, which run up to a block past the

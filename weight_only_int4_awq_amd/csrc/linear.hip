@@ -610,6 +610,280 @@ __global__ __launch_bounds__(W * 64, 2) void linear_gemv_kernel(const LinGroup g
   gemv_body<G, SZV, W>(L.x, L.inv, L.qw, L.sc, L.qz, L.n, k, L.y, L.bid, L.grid, gp.bf != 0);
 }
 
+// ---------------------------------------------------------------- decode GEMV, 2 <= m <= 8
+// The decode GEMV with the tokens as rows 0 .. m-1 of the MFMA A operand
+// (x_tilde = fp16_rn(x inv_s), one rounding, as in the skinny kernels; rows
+// m .. 15 read the zero block), staged once per work-group in LDS as
+// [group][lane group c][token][g/4 halves] with the offset sums T, U per
+// (group, token) in [group][16] float pairs.  Weights, scales and the
+// (block, group) walk of every wave are the decode GEMV's.  Lane (c, r) holds
+// rows 4c .. 4c + 3 of column r of the MFMA result, and per item adds
+// D (C_t - T_t - z U_t) for each of them (rows past m are never stored).  At
+// the end of a block a wave writes its partial rows to LDS as
+// [block][wave][column][8 tokens]; after the loop every thread sums one
+// output over the waves in wave order.
+constexpr int kRowsMaxBlk = 8;         // column blocks per work-group
+constexpr int kRowsMaxTok = 8;
+
+size_t gemv_rows_lds_bytes(int64_t k, int32_t g, int64_t m, int nb, int waves) {
+  const size_t ng = (size_t)(k / g);
+  return (size_t)k * (size_t)m * 2 + ng * 16 * 8 + (size_t)(g / 4) * 2 + (size_t)nb * ng * 16 * 4 +
+         (size_t)nb * waves * 16 * kRowsMaxTok * 4;
+}
+
+template <int G, bool SZV, int W>
+__device__ __forceinline__ void gemv_rows_body(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
+    const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, int64_t n, int64_t k, int64_t m_in,
+    uint16_t* __restrict__ y, int bid, int grid, bool bf) {
+  constexpr int WPL = G / 32, HPL = G / 4, LPG = G / 8;
+  constexpr int kThreads = W * 64;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int m = (int)m_in;                              // 2 .. 8
+  const int ng = (int)(k / G);
+  const int nblk = (int)((n + 15) / 16);
+  const int my_blocks = (nblk - bid + grid - 1) / grid;   // 1 .. kRowsMaxBlk
+  unsigned char* sp = smem;
+  uint16_t* xa = reinterpret_cast<uint16_t*>(sp);      sp += (size_t)k * m * 2;      // [ng][4][m][HPL]
+  float2* tu = reinterpret_cast<float2*>(sp);          sp += (size_t)ng * 16 * 8;    // [ng][16] (T, U)
+  uint16_t* zblk = reinterpret_cast<uint16_t*>(sp);    sp += HPL * 2;
+  uint32_t* szw = reinterpret_cast<uint32_t*>(sp);     sp += (size_t)my_blocks * ng * 16 * 4;
+  float* red = reinterpret_cast<float*>(sp);           // [nb][W][16][kRowsMaxTok]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane >> 4, r = lane & 15;
+  const int jb = ng * wave / W, je = ng * (wave + 1) / W;
+  const int cnt = je - jb;
+  const int total = my_blocks * cnt;
+  const int nzw = (ng + 7) / 8, kw_row = (int)(k / 8);
+
+  // ---- 1. scale and zero words of every block (lane-predicated, first)
+  const int n_oct = my_blocks * 16 * nzw;
+  uint4 sz_s[kGemvSzRounds];
+  uint32_t sz_z[kGemvSzRounds];
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    sz_s[i] = make_uint4(0, 0, 0, 0);
+    sz_z[i] = 0;
+    const int o = tid + i * kThreads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      int col = (bid + bs * grid) * 16 + row;
+      col = col < (int)n ? col : (int)n - 1;
+      const uint16_t* srow = scales + (int64_t)col * ng + oct * 8;
+      if constexpr (SZV) {
+        sz_s[i] = *reinterpret_cast<const uint4*>(srow);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (oct * 8 + e < ng) ? srow[e] : (uint16_t)0;
+        sz_s[i] = make_uint4(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                             h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16));
+      }
+      sz_z[i] = qzeros[(int64_t)col * nzw + oct];
+    }
+  }
+
+  // ---- 2. activations: item i of thread t is word (t + threads i) of the
+  // m rows, row-major (clamped: the loads are unconditional)
+  const int n_items = m * kw_row;
+  const bool has_inv = inv_s != nullptr;
+  const uint16_t* sbase = has_inv ? inv_s : x;
+  uint4 xv[kGemvXPre], sv[kGemvXPre];
+#pragma unroll
+  for (int i = 0; i < kGemvXPre; ++i) {
+    int it = tid + i * kThreads;
+    it = it < n_items ? it : n_items - 1;
+    const int t = it / kw_row, wi = it - t * kw_row;
+    xv[i] = *reinterpret_cast<const uint4*>(x + (int64_t)t * k + (int64_t)wi * 8);
+    sv[i] = *reinterpret_cast<const uint4*>(sbase + (int64_t)wi * 8);
+  }
+
+  // ---- 3. first weights (as in the decode GEMV)
+  uint32_t wq[2 * kGemvPF][WPL];
+  const char* qbase = reinterpret_cast<const char*>(qweight);
+  int i_blk = bid, i_j = jb, i_left = total;
+  auto issue = [&](int slot) {
+    int col = i_blk * 16 + r;
+    col = col < (int)n ? col : (int)n - 1;
+    uint32_t qoff = ((uint32_t)col * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
+    asm volatile("" : "+v"(qoff));
+    const int jj = i_j < ng ? i_j : ng - 1;
+    load_words<WPL>(reinterpret_cast<const uint32_t*>(qbase + (int64_t)jj * (LPG * 4) + qoff), wq[slot]);
+    if (i_left > 1) {
+      --i_left;
+      if (++i_j == je) { i_j = jb; i_blk += grid; }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < kGemvPF; ++p) issue(p);
+
+  // ---- 4. stage x_tilde and the offset sums
+  if (tid < HPL / 2) reinterpret_cast<uint32_t*>(zblk)[tid] = 0u;
+  const uint4 ones = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  auto stage = [&](int it, const uint4& xraw, const uint4& sq) {
+    const int t = it / kw_row, wi = it - t * kw_row;
+    const uint4 sv_ = has_inv ? sq : ones;
+    const uint4 xq = act8_h(xraw, bf);
+    const uint32_t xw[4] = {xq.x, xq.y, xq.z, xq.w};
+    const uint32_t sw[4] = {sv_.x, sv_.y, sv_.z, sv_.w};
+    const half2_t one2 = {(half_t)1.0f, (half_t)1.0f};
+    const half2_t off2 = {(half_t)1024.0f, (half_t)64.0f};
+    uint32_t hw[4];
+    float th = 0.f, uh = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2_t h = __builtin_bit_cast(half2_t, xw[i]) * __builtin_bit_cast(half2_t, sw[i]);
+      hw[i] = __builtin_bit_cast(uint32_t, h);
+      uh = dot2_f16(h, one2, uh);
+      th = dot2_f16(h, off2, th);
+    }
+    const int j = wi / LPG;
+    const int wg = wi % LPG;
+    const int cc = wg / WPL, i = wg % WPL;
+    uint4 vh;
+    vh.x = __builtin_amdgcn_perm(hw[2], hw[0], 0x05040100u);
+    vh.y = __builtin_amdgcn_perm(hw[2], hw[0], 0x07060302u);
+    vh.z = __builtin_amdgcn_perm(hw[3], hw[1], 0x05040100u);
+    vh.w = __builtin_amdgcn_perm(hw[3], hw[1], 0x07060302u);
+    *reinterpret_cast<uint4*>(xa + ((size_t)(j * 4 + cc) * m + t) * HPL + i * 8) = vh;
+    // the LPG words of a group are LPG consecutive, aligned lanes of one row
+    th = row_group_sum<LPG>(th);
+    uh = row_group_sum<LPG>(uh);
+    if (wg == 0) tu[j * 16 + t] = make_float2(th, uh);
+  };
+#pragma unroll
+  for (int i = 0; i < kGemvXPre; ++i) {
+    const int it = tid + i * kThreads;
+    if (it < n_items) stage(it, xv[i], sv[i]);
+  }
+  for (int it = tid + kGemvXPre * kThreads; it < n_items; it += kThreads) {
+    const int t = it / kw_row, wi = it - t * kw_row;
+    const uint4 xq = *reinterpret_cast<const uint4*>(x + (int64_t)t * k + (int64_t)wi * 8);
+    const uint4 sq = *reinterpret_cast<const uint4*>(sbase + (int64_t)wi * 8);
+    stage(it, xq, sq);
+  }
+
+  // ---- 5. scale|zero words into LDS
+#pragma unroll
+  for (int i = 0; i < kGemvSzRounds; ++i) {
+    const int o = tid + i * kThreads;
+    if (o < n_oct) {
+      const int row_all = o / nzw, oct = o - row_all * nzw;
+      const int bs = row_all >> 4, row = row_all & 15;
+      const uint32_t sw[4] = {sz_s[i].x, sz_s[i].y, sz_s[i].z, sz_s[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = oct * 8 + e;
+        if (j < ng)
+          szw[((size_t)bs * ng + j) * 16 + row] =
+              ((sw[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu) | (((sz_z[i] >> (4 * e)) & 0xFu) << 16);
+      }
+    }
+  }
+  __syncthreads();
+
+  const bool arow = r < m;
+  const uint32_t a_lane = arow ? (uint32_t)((c * m + r) * HPL * 2) : 0u;
+  const char* a_base = arow ? reinterpret_cast<const char*>(xa) : reinterpret_cast<const char*>(zblk);
+  const uint32_t a_step = arow ? (uint32_t)(4 * m * HPL * 2) : 0u;      // bytes per group
+  const char* tu_lane = reinterpret_cast<const char*>(tu) + c * 32;
+  const UnpackConsts uc = unpack_consts();
+  float yacc[4] = {0.f, 0.f, 0.f, 0.f};
+  int blocks_done = 0;
+  auto finish_block = [&]() {
+    if (c < 2)
+      *reinterpret_cast<float4*>(red + (((size_t)blocks_done * W + wave) * 16 + r) * kRowsMaxTok + 4 * c) =
+          make_float4(yacc[0], yacc[1], yacc[2], yacc[3]);
+    yacc[0] = yacc[1] = yacc[2] = yacc[3] = 0.f;
+    ++blocks_done;
+  };
+  int c_j = jb, c_left = total;
+  auto consume = [&](int p, bool guarded) {
+    if (!guarded || c_left > 0) {
+      const int j = c_j;
+      const char* asrc = a_base + a_lane + (uint32_t)j * a_step;
+      half8_t aop[WPL];
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) aop[i] = *reinterpret_cast<const half8_t*>(asrc + 16 * i);
+      const float4 t01 = *reinterpret_cast<const float4*>(tu_lane + (uint32_t)j * 128);
+      const float4 t23 = *reinterpret_cast<const float4*>(tu_lane + (uint32_t)j * 128 + 16);
+      const uint32_t szv = szw[((size_t)blocks_done * ng + j) * 16 + r];
+      floatx4_t cacc = floatx4_t{};
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        uint32_t u[4];
+        unpack_word(wq[p][i], u, uc);
+        const half8_t bop = __builtin_bit_cast(half8_t, make_uint4(u[0], u[1], u[2], u[3]));
+        cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[i], bop, cacc, 0, 0, 0);
+      }
+      const float d = h2f((uint16_t)szv), zf = (float)(szv >> 16);
+      const float c0 = cacc[0], c1 = cacc[1], c2 = cacc[2], c3 = cacc[3];
+      yacc[0] = __builtin_fmaf(d, __builtin_fmaf(-zf, t01.y, c0 - t01.x), yacc[0]);
+      yacc[1] = __builtin_fmaf(d, __builtin_fmaf(-zf, t01.w, c1 - t01.z), yacc[1]);
+      yacc[2] = __builtin_fmaf(d, __builtin_fmaf(-zf, t23.y, c2 - t23.x), yacc[2]);
+      yacc[3] = __builtin_fmaf(d, __builtin_fmaf(-zf, t23.w, c3 - t23.z), yacc[3]);
+      --c_left;
+      if (++c_j == je) {
+        finish_block();
+        c_j = jb;
+      }
+    }
+  };
+  if (cnt > 0) {
+    int left = total;
+    while (true) {
+      if (left > kGemvPF) {
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) issue(kGemvPF + p);
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) consume(p, false);
+        left -= kGemvPF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) consume(p, true);
+        break;
+      }
+      if (left > kGemvPF) {
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) issue(p);
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p, false);
+        left -= kGemvPF;
+      } else {
+#pragma unroll
+        for (int p = 0; p < kGemvPF; ++p) consume(kGemvPF + p, true);
+        break;
+      }
+    }
+  } else {
+    for (int bi = 0; bi < my_blocks; ++bi) finish_block();
+  }
+
+  // ---- outputs: every thread sums outputs (block, token, column) over the
+  // waves in wave order
+  __syncthreads();
+  const int n_out = my_blocks * m * 16;
+  for (int o = tid; o < n_out; o += kThreads) {
+    const int bs = o / (m * 16), rem = o - bs * (m * 16);
+    const int t = rem >> 4, cl = rem & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < W; ++wv) sum += red[(((size_t)bs * W + wv) * 16 + cl) * kRowsMaxTok + t];
+    const int64_t col = ((int64_t)bid + (int64_t)bs * grid) * 16 + cl;
+    if (col < n) y[(int64_t)t * n + col] = f2act(sum, bf);
+  }
+}
+
+template <int G, bool SZV, int W>
+__global__ __launch_bounds__(W * 64, W == 16 ? 1 : 2) void linear_gemv_rows_kernel(const LinGroup gp, int64_t m, int64_t k) {
+  const LinPick L = pick_linear(gp);
+  gemv_rows_body<G, SZV, W>(L.x, L.inv, L.qw, L.sc, L.qz, L.n, k, m, L.y, L.bid, L.grid, gp.bf != 0);
+}
+
 // ---------------------------------------------------------------- skinny, 2 <= m <= 32
 // linear_prep16 writes x_tilde = fp16_rn(x * inv_s) once per call as the MFMA
 // A operand, 16 tokens per chunk (one chunk for m <= 16, two for m <= 32):
@@ -2621,6 +2895,69 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
           hipLaunchKernelGGL((linear_gemv_kernel<G, false, 8>), gd, bd, lds, stream, gp, k);
       }
       return hipGetLastError();
+    }
+  }
+  // 2 <= m <= 8: the decode GEMV with token rows for every linear whose
+  // activations fit its LDS plan with all its column blocks in one round of
+  // work-groups (a property of the linear, so a group call gives the bits of
+  // the single calls; a group with linears of both kinds runs them one by one)
+#ifndef AWQ_GEMV_ROWS
+#define AWQ_GEMV_ROWS 1
+#endif
+  if (AWQ_GEMV_ROWS && m >= 2 && m <= kRowsMaxTok && off32) {
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
+    auto plan = [&](int waves, int cap, int& nb_cap, int64_t& per_cu) {
+      nb_cap = cap;
+      while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * waves * 64 ||
+                            gemv_rows_lds_bytes(k, G, m, nb_cap, waves) > 160 * 1024))
+        --nb_cap;
+      per_cu = nb_cap > 0 ? (int64_t)(160 * 1024) / (int64_t)gemv_rows_lds_bytes(k, G, m, nb_cap, waves) : 0;
+      const int64_t wg_cap = 16 / waves;
+      per_cu = per_cu < wg_cap ? per_cu : wg_cap;
+    };
+    int nb_cap = 0, waves = 8;
+    int64_t per_cu = 0;
+    plan(8, kGemvMaxBlk, nb_cap, per_cu);
+    if (nb_cap > 0 && per_cu < 2) {
+      int nb16 = 0;
+      int64_t pc16 = 0;
+      plan(16, kRowsMaxBlk, nb16, pc16);
+      if (nb16 > 0 && pc16 >= 1) { waves = 16; nb_cap = nb16; per_cu = pc16; }
+    }
+    int fits = 0;
+    if (nb_cap > 0 && per_cu >= 1)
+      for (int l = 0; l < count; ++l)
+        if ((items[l].n + 15) / 16 <= (int64_t)kGemvCUs * per_cu * nb_cap) ++fits;
+    if (fits == count) {
+      LinGroup gp = {};
+      const int nb = split_group_grid(items, count, (int64_t)kGemvCUs * per_cu, nb_cap, gp);
+      const size_t lds = gemv_rows_lds_bytes(k, G, m, nb, waves);
+      const bool szv = scales_octets(items, count, ng_all);
+      if (scr.dry) return hipSuccess;               // no scratch
+      const dim3 gd((unsigned)gp.wg0[count]), bd((unsigned)(waves * 64));
+#define AWQ_GR(SZ, WW)                                                                         \
+  {                                                                                            \
+    const void* fn_ = reinterpret_cast<const void*>(&linear_gemv_rows_kernel<G, SZ, WW>);      \
+    if (lds > 65536) {                                                                         \
+      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((linear_gemv_rows_kernel<G, SZ, WW>), gd, bd, lds, stream, gp, m, k);   \
+  }
+      if (waves == 16) {
+        if (szv) AWQ_GR(true, 16) else AWQ_GR(false, 16)
+      } else {
+        if (szv) AWQ_GR(true, 8) else AWQ_GR(false, 8)
+      }
+#undef AWQ_GR
+      return hipGetLastError();
+    }
+    if (fits > 0) {
+      for (int l = 0; l < count; ++l) {
+        hipError_t e = launch_linear_group_g<G>(items + l, 1, m, k, scr, stream);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
   }
   // skinny 2 <= m <= 32: one fused kernel when its LDS plan fits (16-token
