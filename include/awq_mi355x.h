@@ -369,10 +369,11 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight,
  *   Every y holds exactly the bits awq_linear_w4a16 writes for that linear
  *   alone (the arithmetic of a column block does not depend on the launch).
  *   m = 1 and 2 <= m <= 16 run the whole group in one launch of the decode
- *   GEMV or of the fused skinny kernel when their shared-memory plans fit
- *   the k; m > 32 one activation-prep launch and one GEMM launch over the
- *   tiles of every linear; otherwise the linears run one after another on
- *   the stream, reusing the workspace in stream order.
+ *   GEMV (with the tokens as MFMA rows for m <= 8) or of the fused skinny
+ *   kernel when their shared-memory plans fit the k and every linear of the
+ *   group plans alike; m > 32 one activation-prep launch and one GEMM launch
+ *   over the tiles of every linear; otherwise the linears run one after
+ *   another on the stream, reusing the workspace in stream order.
  *   workspace: awq_linear_group_workspace_size(n, count, m, k, g) bytes for
  *            the outputs' widths n[0..count-1], 256-byte aligned (NULL if
  *            that is 0).
