@@ -65,8 +65,9 @@ def test_noalloc_group_matches_workspace_call(lib):
     assert lib.awq_linear_noalloc_scratch_bytes() == 64 << 20
     # 600 tokens (GEMM: x_tilde slots, three row tiles), then 256 (split-K
     # GEMM: slots and partial tiles), 40 (64-row split-K tiles), 24 (fused
-    # two-chunk kernel, no scratch) and 1; every plan fits the static scratch
-    for m in (600, 256, 40, 24, 1):
+    # two-chunk kernel, no scratch), 8 (token-row decode GEMV, no scratch)
+    # and 1; every plan fits the static scratch
+    for m in (600, 256, 40, 24, 8, 1):
         x_h = S.activations(m, k, 1910 + m, ch, 20.0)
         x = dev(x_h)
         need = lib.awq_linear_group_workspace_size(ns, 3, m, k, g)
