@@ -220,9 +220,10 @@ __global__ __launch_bounds__(64 * (4 + NP), 1) void search_loss_kernel(
   constexpr int TOK = 32 * NC * NT;   // tokens per pass
   constexpr int WLD = EPT / 8;        // 16-byte weight loads per producer thread per group
   // LDS padding, so that the 8 lanes an LDS cycle serves hit distinct banks:
-  // a producer's 16-byte dW stores (lanes: 2 rows x 4 quarters) shift by 32
-  // bytes per quarter of the group; its scale reads (4 quarters, the rows
-  // broadcast) by 16 bytes per quarter, its reciprocal reads likewise
+  // a producer's 16-byte dW stores (lanes: 2 rows x 4 quarters, or 1 row x 8
+  // eighths) shift by 32 (16) bytes per part of the group; its scale reads
+  // (the parts, the rows broadcast) by 16 bytes per part, its reciprocal
+  // reads likewise
   constexpr int CPQ = EPT / 8;                     // 8-channel chunks per part
   constexpr int PADS = NP == 4 ? 16 : 8;           // dW pad (halves) per part of the group
   constexpr int DWN = KSTEPS * kSearchRows * 16 + (NP - 1) * PADS;   // halves per dW buffer
