@@ -332,9 +332,10 @@ awq_status awq_linear_wbit(const uint16_t* x, const uint32_t* qweight,
  *            bytes, 256-byte aligned, owned by the caller (NULL when the
  *            size is 0); contents on entry are ignored.
  *   m = 1 runs the decode GEMV and 2 <= m <= 16 one fused skinny kernel,
- *   both without scratch; 17 <= m <= 32 a fused kernel with two token
- *   chunks, or for linears above 16 MiB of packed weights the tiled GEMM
- *   (GEMV mode); m > 32 the prefill GEMM (x * inv_s16 staged in the
+ *   both without scratch; 17 <= m <= 32 a group-major kernel with two
+ *   token chunks, or for linears above 16 MiB of packed weights with more
+ *   than 512 column blocks or k > 8192 the tiled GEMM (GEMV mode); m > 32
+ *   the prefill GEMM (x * inv_s16 staged in the
  *   workspace, and fp32 partial tiles there where the linear is split along
  *   K).  Shapes whose activations or scale rows do not fit LDS for these take
  *   a staged two-kernel decode path (activations staged in the workspace).

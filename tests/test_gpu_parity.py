@@ -275,7 +275,7 @@ def test_linear_decode_full_size(P, name, n, k, g):
     # every output of the Llama-3-8B-shaped linears at the decode sizes, with
     # group sizes 128 and 64 (the stack's two variants): m = 1 the decode GEMV,
     # 8 the fused skinny kernel (group-major where blocks are shared), 24 and 32
-    # the fused two-chunk kernel for q, k, v and o and the grouped GEMM (64-row
+    # the two-chunk group-major kernel for q, k, v and o and the grouped GEMM (64-row
     # tiles, split along K) for gate, up and down
     w, x_cal, _, _ = S.config_layer(2, name, n, k, 128, 0, 0.02, 0.01, 20.0)
     s16 = O.scale_candidate(O.calib_stats(x_cal), 0.4)
@@ -517,8 +517,8 @@ def _check_group(P, items, meta, k, g, cols_per=None):
 @pytest.mark.parametrize("m", [1, 8, 24, 40, 300])
 @pytest.mark.parametrize("g", [128, 64])
 def test_linear_group_matches_single_and_oracle(P, m, g):
-    # m = 1, 8 and 24: one grouped decode launch (at 24 the fused kernel with
-    # two token chunks);
+    # m = 1, 8 and 24: one grouped decode launch (at 24 the group-major kernel
+    # with two token chunks);
     # m = 40 and 300 (two row tiles, the second ragged): one activation-prep
     # launch and one GEMM launch over the tiles of every linear
     specs = [(1000, 0.5, 460), (256, 0.3, 470), (264, None, 480), (16, 0.4, 490)]
@@ -541,8 +541,9 @@ def test_linear_group_llama3_8b_full_size_sampled(P, m):
 def test_linear_group_mixed_plan(P, m):
     # m = 8: the group takes two column blocks per work-group (group-major
     # kernel), the small linears alone take one (block-major kernel); above 16
-    # tokens the linear of more than 16 MiB of packed weights runs the grouped
-    # GEMM and the small linears each take their own (fused) plan
+    # tokens the linear of more than 16 MiB of packed weights in 896 column
+    # blocks runs the grouped GEMM and the small linears share one launch of
+    # the two-chunk group-major kernel
     specs = [(14336, 0.5, 570), (1024, 0.4, 580), (264, None, 590)]
     items, meta = _group_case(P, m, 4096, 128, specs, 600 + m)
     _check_group(P, items, meta, 4096, 128, cols_per=128)

@@ -72,10 +72,12 @@ def _check_rows(y_host, x, host, inv, k, g, w_bit=4):
 
 
 # (n, k, m, g): m = 1 decode GEMV with a ragged last block; 8 fused skinny;
-# 24 fused two-chunk; 24 on a linear above 16 MiB of packed weights (grouped
-# GEMM with 64-row tiles split along K); 33 and 64 split-K GEMM; 300 GEMM with
-# a ragged second row tile; k = 65536 the staged two-kernel decode path
-CASES = [(1000, 2048, 1, 128), (1000, 2048, 8, 64), (257, 4096, 24, 128), (8200, 4096, 24, 128),
+# 24 two-chunk group-major kernel (also on 16.4 MiB of packed weights in 257
+# blocks, the last ragged); 24 on a linear above 16 MiB in more than 512 blocks
+# (grouped GEMM with 64-row tiles split along K); 33 and 64 split-K GEMM; 300
+# GEMM with a ragged second row tile; k = 65536 the staged two-kernel decode path
+CASES = [(1000, 2048, 1, 128), (1000, 2048, 8, 64), (257, 4096, 24, 128), (4100, 8192, 24, 128),
+         (8200, 4096, 24, 128),
          (1000, 2048, 33, 128), (1000, 4096, 64, 32), (260, 2048, 300, 128), (40, 65536, 8, 128)]
 
 

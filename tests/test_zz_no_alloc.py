@@ -64,8 +64,8 @@ def test_noalloc_group_matches_workspace_call(lib):
     ns = (C.c_int64 * 3)(*[lin[4] for lin in linears])
     assert lib.awq_linear_noalloc_scratch_bytes() == 64 << 20
     # 600 tokens (GEMM: x_tilde slots, three row tiles), then 256 (split-K
-    # GEMM: slots and partial tiles), 40 (64-row split-K tiles), 24 (fused
-    # two-chunk kernel, no scratch), 8 (token-row decode GEMV, no scratch)
+    # GEMM: slots and partial tiles), 40 (64-row split-K tiles), 24 (two-chunk
+    # group-major kernel, no scratch), 8 (token-row decode GEMV, no scratch)
     # and 1; every plan fits the static scratch
     for m in (600, 256, 40, 24, 8, 1):
         x_h = S.activations(m, k, 1910 + m, ch, 20.0)

@@ -1454,8 +1454,10 @@ __device__ __forceinline__ void skinny_fused_body(
 // wave's K range, so the main loop has no barrier; after it the waves meet
 // once per block to sum their partial rows, and the reducing wave stores the
 // outputs.  Block slots past the linear's last block point one block past its
-// end: their weight loads read zeros, and they are not stored.
-template <int G, bool SZV, int NB, int PF>
+// end: their weight loads read zeros, and they are not stored.  TC = 2 (17 to
+// 32 tokens) gives every dequantized weight fragment two A fragments, tokens
+// 0-15 and 16-31, so the weights are read and dequantized once for both.
+template <int G, bool SZV, int NB, int PF, int TC>
 __device__ __forceinline__ void skinny_gm_body(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
     const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scales,
@@ -1527,7 +1529,7 @@ __device__ __forceinline__ void skinny_gm_body(
   // past the last block and tokens past m read zeros; the row or token is in
   // the VGPR offset, the group along K in the scalar one)
   uint32_t wq[2 * PF][NB][WPL];
-  uint4 xq[2 * PF][WPL];
+  uint4 xq[2 * PF][TC][WPL];
   const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(qweight, (uint32_t)((uint64_t)n * (uint64_t)k / 2));
   const __amdgpu_buffer_rsrc_t rs_x = buf_rsrc(x, (uint32_t)((uint64_t)m * (uint64_t)k * 2));
   uint32_t w_voff[NB];
@@ -1538,6 +1540,7 @@ __device__ __forceinline__ void skinny_gm_body(
     w_voff[bb] = ((uint32_t)(blk * 16 + r) * (uint32_t)kw_row + (uint32_t)(WPL * c)) * 4u;
   }
   const uint32_t x_voff = ((uint32_t)r * (uint32_t)k + (uint32_t)(8 * WPL * c)) * 2u;
+  const uint32_t x_chunk = (uint32_t)k * 32u;     // 16 token rows
   int i_j = jb, i_left = cnt;
   auto issue = [&](int slot) {
     const int jj = i_j < ng ? i_j : ng - 1;
@@ -1545,9 +1548,12 @@ __device__ __forceinline__ void skinny_gm_body(
     for (int bb = 0; bb < NB; ++bb)
       buf_words<WPL>(rs_w, w_voff[bb], (uint32_t)(jj * LPG) * 4u, wq[slot][bb]);
 #pragma unroll
-    for (int i = 0; i < WPL; ++i)
-      xq[slot][i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, x_voff + 16u * i, (uint32_t)(jj * G) * 2u, 0));
+    for (int t = 0; t < TC; ++t)
+#pragma unroll
+      for (int i = 0; i < WPL; ++i)
+        xq[slot][t][i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, x_voff + x_chunk * t + 16u * i,
+                                                         (uint32_t)(jj * G) * 2u, 0));
     if (i_left > 1) {
       --i_left;
       ++i_j;
@@ -1577,29 +1583,34 @@ __device__ __forceinline__ void skinny_gm_body(
   __syncthreads();
 
   const UnpackConsts uc = unpack_consts();
-  floatx4_t acc[NB];
+  floatx4_t acc[TC][NB];
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) acc[bb] = floatx4_t{};
+  for (int t = 0; t < TC; ++t)
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) acc[t][bb] = floatx4_t{};
   int c_j = jb, c_left = cnt;
   auto consume = [&](int p, bool guarded) {   // guarded only in the tail
     if (!guarded || c_left > 0) {
       const int j = c_j;
-      // A: x_tilde = fp16_rn(x inv_s) of the 16 token rows, channels permuted
-      // into the unpack order (k0, k4, k1, k5, k2, k6, k3, k7)
-      half8_t av[WPL];
+      // A: x_tilde = fp16_rn(x inv_s) of the 16 token rows of each chunk,
+      // channels permuted into the unpack order (k0, k4, k1, k5, k2, k6, k3, k7)
+      half8_t av[TC][WPL];
 #pragma unroll
       for (int i = 0; i < WPL; ++i) {
         const uint4 sv = has_inv ? *reinterpret_cast<const uint4*>(inv_l + j * G + 8 * (WPL * c + i))
                                  : make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-        const uint4 xv = act8_h(xq[p][i], bf);
-        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, sv.x));
-        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
-        const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
-        const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.w) * __builtin_bit_cast(half2_t, sv.w));
-        av[i] = __builtin_bit_cast(half8_t, make_uint4(__builtin_amdgcn_perm(p2, p0, 0x05040100u),
-                                                       __builtin_amdgcn_perm(p2, p0, 0x07060302u),
-                                                       __builtin_amdgcn_perm(p3, p1, 0x05040100u),
-                                                       __builtin_amdgcn_perm(p3, p1, 0x07060302u)));
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+          const uint4 xv = act8_h(xq[p][t][i], bf);
+          const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.x) * __builtin_bit_cast(half2_t, sv.x));
+          const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.y) * __builtin_bit_cast(half2_t, sv.y));
+          const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.z) * __builtin_bit_cast(half2_t, sv.z));
+          const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, xv.w) * __builtin_bit_cast(half2_t, sv.w));
+          av[t][i] = __builtin_bit_cast(half8_t, make_uint4(__builtin_amdgcn_perm(p2, p0, 0x05040100u),
+                                                            __builtin_amdgcn_perm(p2, p0, 0x07060302u),
+                                                            __builtin_amdgcn_perm(p3, p1, 0x05040100u),
+                                                            __builtin_amdgcn_perm(p3, p1, 0x07060302u)));
+        }
       }
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
@@ -1620,7 +1631,9 @@ __device__ __forceinline__ void skinny_gm_body(
           const half8_t bop = __builtin_bit_cast(
               half8_t, make_uint4(__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
                                   __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)));
-          acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], bop, acc[bb], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < TC; ++t)
+            acc[t][bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t][i], bop, acc[t][bb], 0, 0, 0);
         }
       }
       --c_left;
@@ -1655,25 +1668,29 @@ __device__ __forceinline__ void skinny_gm_body(
     }
   }
 
-  // ---- 5. per block: the W partial rows summed in wave order by the last
-  // wave, which stores the block (lane (c, r) holds tokens 4c + e of column r)
+  // ---- 5. per block and chunk: the W partial rows summed in wave order by
+  // the last wave, which stores them (lane (c, r) holds tokens 16 tc + 4c + e
+  // of column r); the two reduction buffers alternate
   const int reducer = W - 1;
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
     if (bb < my_blocks) {
-      floatx4_t* rb = red + (size_t)(bb & 1) * W * 64;
-      rb[wave * 64 + lane] = acc[bb];
-      __syncthreads();
-      if (wave == reducer) {
-        floatx4_t sacc = rb[lane];
 #pragma unroll
-        for (int wv = 1; wv < W; ++wv) sacc += rb[wv * 64 + lane];
-        const int64_t col = ((int64_t)bid + (int64_t)bb * grid) * 16 + r;
+      for (int tc = 0; tc < TC; ++tc) {
+        floatx4_t* rb = red + (size_t)((bb * TC + tc) & 1) * W * 64;
+        rb[wave * 64 + lane] = acc[tc][bb];
+        __syncthreads();
+        if (wave == reducer) {
+          floatx4_t sacc = rb[lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = sacc[e];
-          const int64_t t = 4 * c + e;
-          if (t < m && col < n) y[t * n + col] = f2act(v, bf);
+          for (int wv = 1; wv < W; ++wv) sacc += rb[wv * 64 + lane];
+          const int64_t col = ((int64_t)bid + (int64_t)bb * grid) * 16 + r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = sacc[e];
+            const int64_t t = 16 * tc + 4 * c + e;
+            if (t < m && col < n) y[t * n + col] = f2act(v, bf);
+          }
         }
       }
     }
@@ -1687,8 +1704,17 @@ template <int G, bool SZV, int NB, int PF>
 __global__ __launch_bounds__(kSk16Threads, AWQ_SKINNY_GM_MINW) void linear_skinny_gm_kernel(const LinGroup gp,
                                                                            int64_t m, int64_t k) {
   const LinPick L = pick_linear(gp);
-  skinny_gm_body<G, SZV, NB, PF>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid,
-                                 gp.bf != 0);
+  skinny_gm_body<G, SZV, NB, PF, 1>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid,
+                                    gp.bf != 0);
+}
+// 17 to 32 tokens: two A chunks per weight fragment; one work-group per CU
+// (the second chunk's activations and accumulators double those registers)
+template <int G, bool SZV, int NB, int PF>
+__global__ __launch_bounds__(kSk16Threads, 1) void linear_skinny_gm2_kernel(const LinGroup gp,
+                                                                             int64_t m, int64_t k) {
+  const LinPick L = pick_linear(gp);
+  skinny_gm_body<G, SZV, NB, PF, 2>(L.x, L.inv, L.qw, L.sc, L.qz, m, L.n, k, L.y, L.bid, L.grid,
+                                    gp.bf != 0);
 }
 
 // LDS of the group-major skinny kernel: inv_s (whole 1 KiB copies), scale|zero
@@ -2699,8 +2725,17 @@ static hipError_t launch_linear_one(const LinItem& it, int64_t m, int64_t k, Scr
 // 17 <= m <= 32: a linear that a call of it alone would not run fused (more
 // than 16 MiB of packed weights) and that is wide (at least 12288 columns)
 // takes the GEMM.  A property of the linear alone, as every plan choice.
+// 17 to 32 tokens: the linears that run the grouped GEMM (64-row tiles, split
+// along K) rather than the two-chunk group-major kernel: more than 16 MiB of
+// packed weights with either more column blocks than one round of one
+// work-group per CU takes at two blocks each, or k > 8192.  Measured at 20 and
+// 32 tokens: the kernel is faster for q/k/v (12 MiB) and o (8 MiB) of
+// Llama-3-8B and the 70B-shaped 8192 x 8192 (32 MiB, 512 blocks), the GEMM for
+// gate/up (28 MiB each, 896 blocks each) and down (28 MiB at k = 14336).
 static bool skinny_wide(const LinItem& it, int64_t m, int64_t k) {
-  return m > 16 && m <= 32 && it.n * k / 2 > ((int64_t)16 << 20);
+  const int64_t blocks = (it.n + 15) / 16;
+  return m > 16 && m <= 32 && it.n * k / 2 > ((int64_t)16 << 20) &&
+         (blocks > 2 * (int64_t)kGemvCUs || k > 8192);
 }
 
 // The prefill GEMM of a group (m > 32): x_tilde of every linear into a
@@ -2958,6 +2993,66 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
         if (e != hipSuccess) return e;
       }
       return hipSuccess;
+    }
+  }
+  // 17 <= m <= 32: the wide linears as one grouped GEMM launch, the others
+  // as one launch of the group-major kernel with two token chunks (one
+  // work-group per CU), when its LDS plan fits
+#ifndef AWQ_SKINNY_GM2
+#define AWQ_SKINNY_GM2 1
+#endif
+#ifndef AWQ_SKINNY_GM2_PF
+#define AWQ_SKINNY_GM2_PF 1
+#endif
+  if (AWQ_SKINNY_GM2 && off32 && m > 16 && m <= 32) {
+    const int64_t ng_all = k / G, nzw_all = (ng_all + 7) / 8;
+    // at g = 128 three or more blocks spill registers
+    int nb_cap = G == 128 ? 2 : kGemvMaxBlk;
+    while (nb_cap > 0 && ((int64_t)nb_cap * 16 * nzw_all > (int64_t)kGemvSzRounds * kSk16Threads ||
+                          skinny_gm_lds_bytes(k, G, nb_cap) > 160 * 1024))
+      --nb_cap;
+    if (nb_cap > 0) {
+      LinItem wide[kGroupMax], rest[kGroupMax];
+      int nw = 0, nr = 0;
+      for (int l = 0; l < count; ++l) {
+        if (skinny_wide(items[l], m, k)) wide[nw++] = items[l];
+        else rest[nr++] = items[l];
+      }
+      if (nw > 0) {
+        hipError_t e = launch_gemm_group<G>(wide, nw, m, k, scr, stream);
+        if (e != hipSuccess || nr == 0) return e;
+      }
+      LinGroup gp = {};
+      const int nb = split_group_grid(rest, nr, (int64_t)kGemvCUs, nb_cap, gp);
+      const size_t lds = skinny_gm_lds_bytes(k, G, nb);
+      const bool szv = scales_octets(rest, nr, ng_all);
+      if (scr.dry) return hipSuccess;               // no scratch of its own
+      const dim3 gd((unsigned)gp.wg0[nr]), bd(kSk16Threads);
+#define AWQ_SKG2(SZ, NBB)                                                                      \
+  {                                                                                            \
+    const void* fn_ = reinterpret_cast<const void*>(&linear_skinny_gm2_kernel<G, SZ, NBB, AWQ_SKINNY_GM2_PF>); \
+    if (lds > 65536) {                                                                         \
+      hipError_t e_ = hipFuncSetAttribute(fn_, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e_ != hipSuccess) return e_;                                                         \
+    }                                                                                          \
+    hipLaunchKernelGGL((linear_skinny_gm2_kernel<G, SZ, NBB, AWQ_SKINNY_GM2_PF>), gd, bd, lds, stream, gp, \
+                       m, k);                                                                  \
+  }
+      if (nb == 1) {
+        if (szv) AWQ_SKG2(true, 1) else AWQ_SKG2(false, 1)
+      } else if (G == 128 || nb == 2) {
+        if (szv) AWQ_SKG2(true, 2) else AWQ_SKG2(false, 2)
+      } else {
+        if constexpr (G != 128) {
+          if (nb == 3) {
+            if (szv) AWQ_SKG2(true, 3) else AWQ_SKG2(false, 3)
+          } else {
+            if (szv) AWQ_SKG2(true, 4) else AWQ_SKG2(false, 4)
+          }
+        }
+      }
+#undef AWQ_SKG2
+      return hipGetLastError();
     }
   }
   // skinny 2 <= m <= 32: one fused kernel when its LDS plan fits (16-token
