@@ -368,6 +368,27 @@ def test_linear_decode_rows_multiblock(P, n, k, g):
         assert ok, (m, worst, raw)
 
 
+@pytest.mark.parametrize("n,k,g", [(12008, 2048, 64), (16008, 2048, 32), (8008, 4096, 128), (700, 8192, 64)])
+def test_linear_skinny_two_chunk_multiblock(P, n, k, g):
+    # 17 to 32 tokens on linears of at most 16 MiB of packed weights: the
+    # group-major kernel with two token chunks, one work-group per CU, so more
+    # than 256 column blocks give several per work-group (three at 12008 x 2048,
+    # four at 16008 x 2048, two at g = 128, where more would spill), ragged last
+    # blocks, tokens of the second chunk partly past m; at k = 8192 one block per
+    # work-group
+    w = S.weights(n, k, 0.02, 470 + n)
+    xc = S.activations(64, k, 473, S.outlier_channels(k, 0.01, 472), 20.0)
+    s16 = O.scale_candidate(O.calib_stats(xc), 0.3)
+    inv = O.fp16_rn(1.0 / s16.astype(np.float64))
+    (qw, sc, qz), (hq, hs, hz) = oracle_pack(w, s16, g)
+    for m in (17, 24, 32):
+        x = S.activations(m, k, 471 + n + m, S.outlier_channels(k, 0.01, 472), 20.0)
+        y = P.awq_linear_w4a16(dev(x), qw, sc, qz, dev(inv), g=g)
+        torch.cuda.synchronize()
+        ok, worst, raw = O.check_linear(host16(y), O.linear_ref(x, hq, hs, hz, inv, k, g))
+        assert ok, (m, worst, raw)
+
+
 def test_linear_packed_weights_at_4gib(P):
     # the largest packed weights a call takes (n k / 2 just below 4 GiB): the
     # decode kernels' 32-bit byte offsets, which run up to a block past the
