@@ -372,9 +372,12 @@ awq_status awq_linear_w4a16(const uint16_t* x, const uint32_t* qweight,
  *   m = 1 and 2 <= m <= 16 run the whole group in one launch of the decode
  *   GEMV (with the tokens as MFMA rows for m <= 8) or of the fused skinny
  *   kernel when their shared-memory plans fit the k and every linear of the
- *   group plans alike; m > 32 one activation-prep launch and one GEMM launch
- *   over the tiles of every linear; otherwise the linears run one after
- *   another on the stream, reusing the workspace in stream order.
+ *   group plans alike; 17 <= m <= 32 one tiled-GEMM launch for the linears
+ *   above 16 MiB of packed weights with more than 512 column blocks or
+ *   k > 8192 and one launch of the two-chunk group-major kernel for the
+ *   others; m > 32 one activation-prep launch and one GEMM launch over the
+ *   tiles of every linear; otherwise the linears run one after another on
+ *   the stream, reusing the workspace in stream order.
  *   workspace: awq_linear_group_workspace_size(n, count, m, k, g) bytes for
  *            the outputs' widths n[0..count-1], 256-byte aligned (NULL if
  *            that is 0).
