@@ -40,7 +40,7 @@ graph replays (128 decode-GEMV launches per stack), measured with HIP events on 
 on.  The stack is 3.6 GB, far beyond the 256 MB Infinity Cache, so every
 weight byte comes from HBM.
 
-    python bench.py [--steps K] [--warmup W] [--layers 32] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--layers 32] [--no-cpu] [--no-sclk]
     python bench.py --copy-calibration      (counter calibration only)
 """
 from __future__ import annotations
@@ -78,6 +78,77 @@ def wbit_bytes(m, n, k, g, w_bit):
             + 2 * m * n)
 
 
+# Child process that samples the shader (GFX) clock of the GPU whose PCI bus
+# id it is given, through amdsmi's gpu_metrics, every ~2 ms for argv[2]
+# seconds after printing "ready"; it prints one JSON line with two series in
+# MHz: the current clock (mean over the XCDs that report one) and the
+# firmware's activity-averaged clock.
+_SCLK_SAMPLER = r"""
+import json, sys, time
+import amdsmi
+want, dur = sys.argv[1].lower(), float(sys.argv[2])
+amdsmi.amdsmi_init()
+handle = None
+for h in amdsmi.amdsmi_get_processor_handles():
+    bdf = str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower()
+    if bdf.endswith(want) or want.endswith(bdf):
+        handle = h
+print("ready" if handle is not None else "nomatch", flush=True)
+out = {"current_gfxclks": [], "average_gfxclk_frequency": []}
+t_end = time.time() + dur
+while handle is not None and time.time() < t_end:
+    m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+    for key in out:
+        v = m.get(key)
+        vals = [float(x) for x in (v if isinstance(v, (list, tuple)) else [v])
+                if isinstance(x, (int, float)) and 0 < x < 10000]
+        if vals:
+            out[key].append(sum(vals) / len(vals))
+    time.sleep(0.002)
+amdsmi.amdsmi_shut_down()
+print(json.dumps(out), flush=True)
+"""
+
+
+def sample_sclk(work, seconds=0.6):
+    """Mean shader clock (MHz) while `work()` runs back to back on the GPU for
+    about `seconds`, sampled by a child process; None where the clock cannot
+    be read (no amdsmi, the device not found, a timeout)."""
+    import select
+    import subprocess
+    import torch
+    try:
+        props = torch.cuda.get_device_properties(0)
+        bdf = "%02x:%02x.0" % (int(props.pci_bus_id), int(props.pci_device_id))
+    except Exception:
+        return None
+    try:
+        child = subprocess.Popen([sys.executable, "-c", _SCLK_SAMPLER, bdf, str(seconds)],
+                                 stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except Exception:
+        return None
+    try:
+        ready, _, _ = select.select([child.stdout], [], [], 30.0)
+        if not ready or child.stdout.readline().strip() != "ready":
+            child.kill()
+            child.wait(timeout=10)
+            return None
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            work()
+            torch.cuda.synchronize()
+        out, _ = child.communicate(timeout=30)
+        series = json.loads(out.strip().splitlines()[-1])
+    except Exception:
+        child.kill()
+        child.wait(timeout=10)
+        return None
+    res = {key: {"mean": round(sum(v) / len(v), 1), "min": round(min(v), 1), "max": round(max(v), 1),
+                 "samples": len(v)}
+           for key, v in series.items() if v}
+    return res or None
+
+
 def measured_traffic(root):
     """HBM bytes per decode-GEMV launch from the committed counter summary, if it
     was taken on the current kernel source (else None)."""
@@ -106,6 +177,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the shader-clock sampling")
     ap.add_argument("--cpu-seconds", type=float, default=30.0,
                     help="time of the M=1 oracle leg (one thread plus all cores); the other legs are fixed samples")
     ap.add_argument("--cpu-only", action="store_true", help="only the CPU oracle baseline")
@@ -544,6 +616,16 @@ def main():
             acc[p] += ev[pi].elapsed_time(ev[pi + 1]) * 1e-3     # seconds
     log(f"timed {args.steps} steps in {t_total:.3f}s")
 
+    # shader clock under the two headline loads, after the timed region
+    sclk = None
+    if not args.no_sclk:
+        sclk = {"prefill_m2048": sample_sclk(lambda: prefill(0)),
+                "decode_g128_m1": sample_sclk(lambda: graphs[(128, 1)].replay()),
+                "source": "amdsmi gpu_metrics, sampled every ~2 ms while the load runs back to back "
+                          "after the timed region: current_gfxclks (mean over XCDs), and "
+                          "average_gfxclk_frequency where the firmware reports it"}
+        log(f"shader clock: {sclk['prefill_m2048']} (prefill), {sclk['decode_g128_m1']} (decode)")
+
     K = args.steps
     nlin = L * len(shapes)
     bytes_by = {}
@@ -659,6 +741,8 @@ def main():
                           "frac": round(rows["prefill_m2048"]["frac_mfma_peak"], 4)},
         "rows": rows,
     }
+    if sclk is not None:
+        out["sclk_mhz"] = sclk
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
