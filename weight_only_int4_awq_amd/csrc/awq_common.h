@@ -132,6 +132,28 @@ __device__ __forceinline__ float code_minus_zero(float w, const GroupQ& gq) {
   return __builtin_fminf(__builtin_fmaxf(t, -gq.z), gq.qmax - gq.z);
 }
 
+// Tile t of a linear's tiles_m x tiles_n output tiles in banded order: bands
+// of GM row tiles, each band column by column with its row tiles fastest.  A
+// contiguous run of the order (the work-groups resident on one XCD at a time)
+// then covers a few row tiles and a few column tiles rather than every row
+// tile of a few columns, so both operands' tiles are shared in that XCD's L2.
+// A bijection of [0, tiles_m * tiles_n); with at most GM row tiles it is the
+// plain rows-fastest order.
+template <int GM>
+__device__ __forceinline__ void banded_tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if (tiles_m <= GM) {
+    tm = t % tiles_m;
+    tn = t / tiles_m;
+    return;
+  }
+  const int span = GM * tiles_n;
+  const int band = t / span, first = band * GM;
+  const int rows = tiles_m - first < GM ? tiles_m - first : GM;
+  const int r = t - band * span;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }

@@ -2200,29 +2200,11 @@ __device__ __forceinline__ void g2_barrier() {
 #ifndef AWQ_G2_GROUP_M
 #define AWQ_G2_GROUP_M 4
 #endif
-// Order of the 128-row kernel's tiles within a linear: bands of
-// AWQ_G2_GROUP_M row tiles, each band column by column with its rows
-// fastest, so that the work-groups resident on an XCD at one time (a
-// contiguous run of the order, about 64 at two per CU) cover a few row tiles
-// of activations and a few column tiles of weights instead of every row tile
-// of four columns (m = 2048: 4 x 16 tiles instead of 16 x 4; the prefill
-// layer 926 -> 938 TFLOP/s with bands of 4, 935 with bands of 8).  A
-// bijection of [0, tiles_m * tiles_n); with at most one band it is the plain
-// rows-fastest order.
-__device__ __forceinline__ void g2_tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GM = AWQ_G2_GROUP_M;
-  if (tiles_m <= GM) {
-    tm = t % tiles_m;
-    tn = t / tiles_m;
-    return;
-  }
-  const int span = GM * tiles_n;
-  const int band = t / span, first = band * GM;
-  const int rows = tiles_m - first < GM ? tiles_m - first : GM;
-  const int r = t - band * span;
-  tm = first + r % rows;
-  tn = r / rows;
-}
+// The 128-row kernel walks each linear's tiles in bands of AWQ_G2_GROUP_M row
+// tiles (banded_tile_coords): at m = 2048 the ~64 work-groups resident on an
+// XCD share 4 row tiles of activations and 16 column tiles of weights instead
+// of 16 row tiles of 4 columns (the prefill layer 926 -> 938 TFLOP/s with
+// bands of 4, 935 with bands of 8).
 
 template <int G, int KG>
 __global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void linear_gemm2_kernel(const LinGroup gp, int64_t m,
@@ -2241,7 +2223,7 @@ __global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void linear_gemm2_kernel
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kgrp = wave >> 2, wv = wave & 3;          // K group, wave within the group
   // XCD-aware order: each XCD takes a contiguous run of the tile order
-  // (g2_tile_coords within each linear)
+  // (banded within each linear)
   const int total = gp.wg0[gp.count];
   const int bid = blockIdx.x;
   const int per = total / 8, rem = total % 8;
@@ -2253,7 +2235,7 @@ __global__ __launch_bounds__(256 * KG, KG == 1 ? 2 : 1) void linear_gemm2_kernel
   const int ks = L.ks;
   const int t_ord = L.bid / ks, sl = L.bid - t_ord * ks;
   int tm, tn;
-  g2_tile_coords(t_ord, tiles_m, (int)((n + BN - 1) / BN), tm, tn);
+  banded_tile_coords<AWQ_G2_GROUP_M>(t_ord, tiles_m, (int)((n + BN - 1) / BN), tm, tn);
   const int tl = tm + tn * tiles_m;                   // the tile's slot among the partial tiles
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t kw_row = k / 8;

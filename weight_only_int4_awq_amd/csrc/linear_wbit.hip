@@ -165,6 +165,10 @@ struct WbLane {
 // exactly, and the product with D rounds once.  Activations become
 // fp16_rn(x inv_s).  The waves' fp32 partial tiles are summed in wave order
 // through LDS.
+#ifndef AWQ_WB_GROUP_M
+#define AWQ_WB_GROUP_M 4
+#endif
+
 template <int G, int BITS, int W>
 __global__ __launch_bounds__(W * 64) void linear_wbit_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ inv_s,
@@ -599,15 +603,19 @@ __global__ __launch_bounds__(256, 2) void linear_wbit_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  // XCD-aware tile order: each XCD gets a contiguous range of tiles, M fastest
+  // XCD-aware tile order: each XCD gets a contiguous run of the tiles in
+  // banded order (bands of AWQ_WB_GROUP_M row tiles)
   const int bid = blockIdx.x;
   const int per = tiles_total / 8, rem = tiles_total % 8;
   const int xcd = bid % 8, slot = bid / 8;
   const int wgi = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  // work-group wgi: tile wgi / ks, slice wgi % ks of its K range; slices
-  // start on group boundaries (units of max(1, G / 64) K-steps)
-  const int tl = wgi / ks, sl = wgi - tl * ks;
-  const int tm = tl % tiles_m, tn = tl / tiles_m;
+  // work-group wgi: tile wgi / ks of the order, slice wgi % ks of its K range;
+  // slices start on group boundaries (units of max(1, G / 64) K-steps); tl is
+  // the tile's slot among the partial tiles (rows fastest)
+  const int t_ord = wgi / ks, sl = wgi - t_ord * ks;
+  int tm, tn;
+  banded_tile_coords<AWQ_WB_GROUP_M>(t_ord, tiles_m, tiles_total / ks / tiles_m, tm, tn);
+  const int tl = tm + tn * tiles_m;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * kWbBN;
   const int ng = (int)(k / G), nzw = (ng + ZPW - 1) / ZPW;
   constexpr int UNIT = G / kWbBK > 1 ? G / kWbBK : 1;
