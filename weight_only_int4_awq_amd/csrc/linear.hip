@@ -2907,8 +2907,14 @@ static hipError_t launch_linear_group_g(const LinItem* items, int count, int64_t
     plan(8, nb_cap, per_cu);
     int waves = 8;
     // LDS leaves room for one 8-wave work-group per CU: 16 waves put twice
-    // the weight bytes in flight
-    if (nb_cap > 0 && per_cu < 2) {
+    // the weight bytes in flight.  Also 16 waves for long K (>= 8192) and at
+    // most two blocks per CU: half the work-groups, each staging its K once
+    // for up to two blocks, with as many waves per CU (Llama-3-70B-shaped
+    // 8192<-8192 11.9 -> 11.5 us, 1024<-8192 7.0 -> 6.8 us; at K = 4096 the
+    // stack's q/k/v and o were 3 % slower so)
+    int64_t blocks_all = 0;
+    for (int l = 0; l < count; ++l) blocks_all += (items[l].n + 15) / 16;
+    if (nb_cap > 0 && (per_cu < 2 || (k >= 8192 && blocks_all <= 2 * kGemvCUs))) {
       int nb16 = 0;
       int64_t pc16 = 0;
       plan(16, nb16, pc16);
